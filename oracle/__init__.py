@@ -1,0 +1,173 @@
+"""CPU oracle for the DSA token indexer and PIVOT Reuse/Refine (fp64, one thread).
+
+TEST INFRASTRUCTURE ONLY: the test-suite, the smoke check and the benchmark's
+CPU-baseline leg are the only users. The GPU library never imports or links this
+package, and this package imports nothing from the library.
+
+The arithmetic lives in ``oracle.c`` (plain C, compiled with gcc into
+``liboracle.so`` next to it); this module only marshals numpy arrays through
+ctypes. bf16 tensors travel as their raw ``uint16`` bit patterns so that the
+oracle widens exactly the values the GPU reads.
+
+Paper: "PIVOT: Efficient Query-Group Indexing for Token-Level Sparse Attention"
+(arXiv 2607.24593); see ``oracle.c`` for which section each step follows.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+
+# Plain build: no fast-math, no FMA contraction, so every double operation is
+# the IEEE operation written in the source.
+CFLAGS = ["-O2", "-std=c99", "-fPIC", "-shared", "-fno-fast-math", "-ffp-contract=off"]
+
+
+def build(src: str = _SRC, out: str = _LIB) -> str:
+    """Compile the oracle with gcc. Returns the path of the shared library."""
+    cmd = ["gcc", *CFLAGS, src, "-o", out + ".tmp", "-lm"]
+    subprocess.run(cmd, check=True)
+    os.replace(out + ".tmp", out)
+    return out
+
+
+_lib = None
+
+
+def load(path: str | None = None):
+    """Load (building first if absent) the oracle shared library."""
+    global _lib
+    if path is not None:
+        return _bind(ctypes.CDLL(path))
+    if _lib is None:
+        if not os.path.exists(_LIB):
+            build()
+        _lib = _bind(ctypes.CDLL(_LIB))
+    return _lib
+
+
+def _bind(lib):
+    P = ctypes.c_void_p
+    i64 = ctypes.c_int64
+    i32 = ctypes.c_int
+    lib.orc_scores.argtypes = [P, P, P, i32, i32, i64, P, P]
+    lib.orc_select.argtypes = [P, P, i64, i64, P, P]
+    lib.orc_dense_rows.argtypes = [P, P, P, i64, i64, i32, i32, i64, P, i64, P, P]
+    lib.orc_proxy.argtypes = [P, P, i64, i32, i32, i64, i64, P, P]
+    lib.orc_pivot_groups.argtypes = [P, P, P, i64, i64, i32, i32, i64, i64, i64,
+                                     P, i64, P, P, P, P, P, P, P]
+    for f in (lib.orc_scores, lib.orc_select, lib.orc_dense_rows, lib.orc_proxy,
+              lib.orc_pivot_groups):
+        f.restype = ctypes.c_int
+    return lib
+
+
+def _p(a):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _u16(a):
+    a = np.ascontiguousarray(a)
+    if a.dtype != np.uint16:
+        raise TypeError("bf16 arrays are passed as uint16 bit patterns")
+    return a
+
+
+def _f32(a):
+    return np.ascontiguousarray(a, dtype=np.float32)
+
+
+def _check(rc, what):
+    if rc != 0:
+        raise ValueError(f"oracle {what}: invalid arguments (rc={rc})")
+
+
+def scores(q, w, K, n=None, lib=None):
+    """Index scores of one query row against keys 0..n-1.
+
+    q: uint16 [H, d]; w: float32 [H]; K: uint16 [>=n, d].
+    Returns (score, mass), float64 [n] each; mass bounds every partial sum.
+    """
+    lib = lib or load()
+    q, K, w = _u16(q), _u16(K), _f32(w)
+    H, d = q.shape
+    n = K.shape[0] if n is None else int(n)
+    sc = np.empty(n, np.float64)
+    ms = np.empty(n, np.float64)
+    _check(lib.orc_scores(_p(q), _p(w), _p(K), H, d, n, _p(sc), _p(ms)), "scores")
+    return sc, ms
+
+
+def select(score, k, idx=None, lib=None):
+    """Top-k under (score desc, index asc). Returns (idx int64 [k], score [k])."""
+    lib = lib or load()
+    score = np.ascontiguousarray(score, dtype=np.float64)
+    n = score.shape[0]
+    ix = None if idx is None else np.ascontiguousarray(idx, dtype=np.int64)
+    oi = np.empty(k, np.int64)
+    os_ = np.empty(k, np.float64)
+    _check(lib.orc_select(_p(score), _p(ix), n, k, _p(oi), _p(os_)), "select")
+    return oi, os_
+
+
+def proxy(Q, W, g, m, lib=None):
+    """Proxy (bf16 bits [H, d], fp32 [H]) of query group m of Q [q_len, H, d]."""
+    lib = lib or load()
+    Q, W = _u16(Q), _f32(W)
+    q_len, H, d = Q.shape
+    qb = np.empty((H, d), np.uint16)
+    wb = np.empty(H, np.float32)
+    _check(lib.orc_proxy(_p(Q), _p(W), q_len, H, d, g, m, _p(qb), _p(wb)), "proxy")
+    return qb, wb
+
+
+def dense_rows(Q, W, K, k, rows, lib=None):
+    """Dense top-k for query rows ``rows`` of one sequence.
+
+    Q: uint16 [q_len, H, d] (the last q_len positions of the sequence);
+    W: float32 [q_len, H]; K: uint16 [L, d]. Returns (idx [nrows, k], score).
+    """
+    lib = lib or load()
+    Q, K, W = _u16(Q), _u16(K), _f32(W)
+    q_len, H, d = Q.shape
+    L = K.shape[0]
+    rows = np.ascontiguousarray(rows, dtype=np.int64)
+    oi = np.empty((rows.size, k), np.int64)
+    os_ = np.empty((rows.size, k), np.float64)
+    _check(lib.orc_dense_rows(_p(Q), _p(W), _p(K), L, q_len, H, d, k, _p(rows),
+                              rows.size, _p(oi), _p(os_)), "dense_rows")
+    return oi, os_
+
+
+def pivot_groups(Q, W, K, g, c, k, groups, cand_in=None, lib=None):
+    """PIVOT proxy scan, candidates, Reuse and Refine for groups ``groups``.
+
+    Returns a dict with cand/cand_score [ng, c], reuse/reuse_score [ng, k] and
+    refine/refine_score [ng, g, k]. ``cand_in`` ([ng, c], -1 padded) replaces the
+    candidate list Refine uses.
+    """
+    lib = lib or load()
+    Q, K, W = _u16(Q), _u16(K), _f32(W)
+    q_len, H, d = Q.shape
+    L = K.shape[0]
+    groups = np.ascontiguousarray(groups, dtype=np.int64)
+    ng = groups.size
+    ci = None if cand_in is None else np.ascontiguousarray(cand_in, dtype=np.int64)
+    out = dict(
+        cand=np.empty((ng, c), np.int64), cand_score=np.empty((ng, c), np.float64),
+        reuse=np.empty((ng, k), np.int64), reuse_score=np.empty((ng, k), np.float64),
+        refine=np.empty((ng, g, k), np.int64),
+        refine_score=np.empty((ng, g, k), np.float64),
+    )
+    _check(lib.orc_pivot_groups(
+        _p(Q), _p(W), _p(K), L, q_len, H, d, g, c, k, _p(groups), ng, _p(ci),
+        _p(out["cand"]), _p(out["cand_score"]), _p(out["reuse"]),
+        _p(out["reuse_score"]), _p(out["refine"]), _p(out["refine_score"])),
+        "pivot_groups")
+    return out

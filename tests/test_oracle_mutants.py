@@ -1,0 +1,81 @@
+"""The pins must be strong enough to catch plausible mistakes in the oracle.
+
+Each case copies oracle.c, plants one mistake (a dropped ReLU, a wrong index, an
+off-by-one causal limit, a reversed tie rule, a missing division, truncation
+instead of rounding, ...), compiles the copy with gcc into a temporary
+directory and runs the pin battery against it: at least one pin must fail.
+All of this runs on the CPU; the real oracle is never modified.
+"""
+import os
+import shutil
+import subprocess
+import tempfile
+
+import pytest
+
+import oracle
+from pins import ALL_PINS
+
+SRC = os.path.join(os.path.dirname(oracle.__file__), "oracle.c")
+
+MUTANTS = {
+    "relu_dropped": ("double relu = dot > 0.0 ? dot : 0.0;", "double relu = dot;"),
+    "relu_is_abs": ("double relu = dot > 0.0 ? dot : 0.0;", "double relu = fabs(dot);"),
+    "weight_of_head0": ("total += (double)w[j] * relu;", "total += (double)w[0] * relu;"),
+    "weight_dropped": ("total += (double)w[j] * relu;", "total += relu;"),
+    "query_of_head0": ("double p = qd[(int64_t)j * d + e] * kd[e];", "double p = qd[e] * kd[e];"),
+    "key_element0": ("kd[e] = bf16_to_double(K[s * d + e]);", "kd[e] = bf16_to_double(K[s * d]);"),
+    "causal_strict": ("int64_t n = L - q_len + r + 1;", "int64_t n = L - q_len + r;"),
+    "position_ignores_qlen": ("int64_t n = L - q_len + r + 1;", "int64_t n = r + 1;"),
+    "ties_to_higher_index": ("if (a->idx < b->idx)\n        return -1;\n    if (a->idx > b->idx)\n        return 1;",
+                             "if (a->idx > b->idx)\n        return -1;\n    if (a->idx < b->idx)\n        return 1;"),
+    "ascending_scores": ("if (a->score > b->score)\n        return -1;\n    if (a->score < b->score)\n        return 1;",
+                         "if (a->score < b->score)\n        return -1;\n    if (a->score > b->score)\n        return 1;"),
+    "proxy_not_divided": ("qbar[x] = float_to_bf16_rne(acc / cnt);", "qbar[x] = float_to_bf16_rne(acc);"),
+    "proxy_truncates": ("u += 0x7FFFu + lsb;", "u += 0u * lsb;"),
+    "proxy_rounds_half_up": ("u += 0x7FFFu + lsb;", "u += 0x8000u + 0u * lsb;"),
+    "proxy_count_is_g": ("float cnt = (float)(r1 - r0);", "float cnt = (float)g;"),
+    "proxy_weight_first_member": ("wbar[j] = acc / cnt;", "wbar[j] = W[r0 * H + j];"),
+    "refine_not_causal": ("if (cand[x] >= 0 && cand[x] <= pos)", "if (cand[x] >= 0 && cand[x] <= t_last)"),
+    "scan_stops_early": ("int64_t t_last = L - q_len + r1 - 1;", "int64_t t_last = L - q_len + r1 - 2;"),
+    "scan_starts_group": ("int64_t t_last = L - q_len + r1 - 1;", "int64_t t_last = L - q_len + r0;"),
+}
+
+
+@pytest.fixture(scope="module")
+def workdir():
+    d = tempfile.mkdtemp(prefix="oracle_mutants_")
+    yield d
+    shutil.rmtree(d, ignore_errors=True)
+
+
+def test_unmutated_copy_passes(workdir):
+    src = open(SRC).read()
+    path = os.path.join(workdir, "orig.c")
+    with open(path, "w") as f:
+        f.write(src)
+    lib = oracle.load(oracle.build(path, os.path.join(workdir, "orig.so")))
+    for pin in ALL_PINS:
+        pin(lib)
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutant_is_caught(name, workdir):
+    old, new = MUTANTS[name]
+    src = open(SRC).read()
+    assert src.count(old) == 1, f"mutation site for {name} not found exactly once"
+    path = os.path.join(workdir, f"{name}.c")
+    with open(path, "w") as f:
+        f.write(src.replace(old, new))
+    so = os.path.join(workdir, f"{name}.so")
+    try:
+        lib = oracle.load(oracle.build(path, so))
+    except subprocess.CalledProcessError:
+        pytest.fail(f"mutant {name} does not compile")
+    caught = []
+    for pin in ALL_PINS:
+        try:
+            pin(lib)
+        except (AssertionError, ValueError):
+            caught.append(pin.__name__)
+    assert caught, f"no pin catches the mutant {name}"
