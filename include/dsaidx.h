@@ -1,0 +1,142 @@
+/*
+ * dsaidx.h - C ABI of the DSA token indexer and of PIVOT query-group indexing
+ * on AMD Instinct MI355X (gfx950).
+ *
+ * What is computed. For a query row t and a key s, the index score of the
+ * DeepSeek-Sparse-Attention indexer is
+ *
+ *     I(t,s) = sum_{j < H_I} w[t][j] * max(0, q[t][j] . k[s])
+ *
+ * ("PIVOT: Efficient Query-Group Indexing for Token-Level Sparse Attention",
+ * arXiv 2607.24593: Eq. (1), whose form the paper describes in its paragraph on
+ * observation O3: a per-head ReLU of q_{t,j} . k_s summed over the indexer
+ * heads; one key vector per token, shared by every head). Each query keeps
+ * the k keys of its causal prefix with the highest scores (motivation
+ * paragraph: every query is scored against the entire prefix).
+ *
+ * PIVOT (same paper, Method and abstract) splits the query rows into groups of
+ * g consecutive rows (the last group may be shorter), averages each group into
+ * one proxy query and proxy weights per head, scans the causal prefix once
+ * with the proxy (up to the group's last position) and keeps c candidates.
+ *   - Reuse: every member of the group receives the proxy's top-k.
+ *   - Refine: every member re-scores the candidates that are causal for it
+ *     with its own query and weights and keeps its own top-k.
+ *
+ * Conventions shared by every entry point.
+ *   Shapes (row-major, contiguous, device memory):
+ *     Q        [B][q_len][H_I][d_I]  bf16 (raw 16-bit patterns)
+ *     W        [B][q_len][H_I]       fp32
+ *     K        [B][L][d_I]           bf16
+ *     out_idx  [B][q_len][k]         int32
+ *     out_score[B][q_len][k]         fp32, may be NULL
+ *     out_cand [B][G][c]             int32, may be NULL, G = ceil(q_len / g)
+ *   The q_len query rows of a sequence are its last q_len positions: row r sits
+ *   at position L - q_len + r and may select keys 0 .. L - q_len + r (its own
+ *   key included). Prefill passes q_len = L; a decode step passes the few new
+ *   rows whose keys are already in K.
+ *   Ranking: a key outranks another when its score is higher, or when the
+ *   scores are equal and its index is lower. A selection of size n is the
+ *   first n keys under this ranking.
+ *   Output rows hold the selected key indices in ascending index order, with
+ *   their scores alongside; a row whose eligible keys number fewer than its
+ *   selection size is completed with index -1 and score -inf.
+ *   Scores are computed from the bf16 inputs with fp32 accumulation.
+ *   Supported (H_I, d_I): (4, 32) and (64, 128). Other pairs return
+ *   DSAIDX_EUNSUPPORTED.
+ *
+ * Memory ownership. Every pointer is caller-owned device memory (16-byte
+ * aligned for Q, K and ws). The library allocates and frees nothing, never
+ * synchronises the stream, and keeps no state between calls except the last
+ * error message of the calling thread. Work is enqueued on `stream`; results
+ * are valid once the stream reaches that point. `ws` is scratch space of at
+ * least indexer_workspace_bytes(...) bytes whose content on entry is
+ * irrelevant; calls sharing one ws must not overlap in time.
+ *
+ * Errors. Every entry point returns a dsaidx_status and never throws.
+ * Arguments are validated before anything is enqueued; on DSAIDX_EHIP a
+ * launch failed and part of the work may have been enqueued. The message of
+ * the last non-OK return on the calling thread is in indexer_last_error().
+ */
+#ifndef DSAIDX_H
+#define DSAIDX_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    DSAIDX_OK = 0,
+    DSAIDX_EINVAL = 1,       /* null pointer, size out of range, misalignment */
+    DSAIDX_EUNSUPPORTED = 2, /* (H_I, d_I) without a kernel instantiation     */
+    DSAIDX_EWORKSPACE = 3,   /* ws_bytes below indexer_workspace_bytes(...)   */
+    DSAIDX_EHIP = 4          /* a HIP runtime call or kernel launch failed    */
+} dsaidx_status;
+
+typedef enum {
+    DSAIDX_DENSE = 0,
+    DSAIDX_REUSE = 1,
+    DSAIDX_REFINE = 2
+} dsaidx_mode;
+
+/*
+ * Workspace size in bytes that `mode` needs for these sizes on the current
+ * HIP device (it depends on the device's compute-unit count). For
+ * DSAIDX_DENSE, g and c are ignored. Returns 0 when the arguments are invalid
+ * (the matching entry point would return DSAIDX_EINVAL or
+ * DSAIDX_EUNSUPPORTED).
+ */
+size_t indexer_workspace_bytes(int mode, int B, int64_t L, int64_t q_len,
+                               int H_I, int d_I, int g, int c, int k);
+
+/*
+ * Dense DSA indexer (PIVOT paper, motivation paragraph and Eq. (1)): for each
+ * query row, the top-k keys of its causal prefix.
+ * Requires B >= 1, 1 <= q_len <= L, 1 <= k, L < 2^31.
+ */
+int indexer_dense(const void *Q, const float *W, const void *K,
+                  int B, int64_t L, int64_t q_len, int H_I, int d_I, int k,
+                  int32_t *out_idx, float *out_score,
+                  void *ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * PIVOT-Reuse (PIVOT paper, abstract and Method): every member row of a group
+ * receives the top-k of the group's proxy scan (so the rows of one group are
+ * identical, and early members may hold keys beyond their own position, which
+ * the downstream attention masks). c is used only to fill out_cand with the
+ * proxy's top-c when out_cand is not NULL; otherwise it is ignored.
+ * Requires g >= 1 and, when out_cand is not NULL, c >= 1.
+ */
+int indexer_pivot_reuse(const void *Q, const float *W, const void *K,
+                        int B, int64_t L, int64_t q_len, int H_I, int d_I,
+                        int g, int c, int k,
+                        int32_t *out_idx, float *out_score, int32_t *out_cand,
+                        void *ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * PIVOT-Refine (PIVOT paper, abstract and Method): each member row re-scores
+ * the group's top-c candidates that lie at or before its own position, with
+ * its own query and weights, and keeps its top-k. out_cand, when not NULL,
+ * receives the candidates. Requires g >= 1 and c >= k.
+ */
+int indexer_pivot_refine(const void *Q, const float *W, const void *K,
+                         int B, int64_t L, int64_t q_len, int H_I, int d_I,
+                         int g, int c, int k,
+                         int32_t *out_idx, float *out_score, int32_t *out_cand,
+                         void *ws, size_t ws_bytes, hipStream_t stream);
+
+/* Message of the last non-OK return on the calling thread ("" if none). */
+const char *indexer_last_error(void);
+
+/* Library version string, e.g. "dsaidx 0.1.0 gfx950". */
+const char *indexer_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DSAIDX_H */

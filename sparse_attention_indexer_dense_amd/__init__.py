@@ -1,0 +1,174 @@
+"""Python binding of the dsaidx C ABI (include/dsaidx.h): the DSA token indexer
+and PIVOT Reuse/Refine on AMD MI355X (gfx950).
+
+This module only marshals arguments: the functions named like the C entry
+points (``indexer_dense``, ``indexer_pivot_reuse``, ``indexer_pivot_refine``,
+``indexer_workspace_bytes``, ``indexer_last_error``, ``indexer_version``) take
+raw device pointers and sizes, exactly as the C functions do. ``dense``,
+``pivot_reuse`` and ``pivot_refine`` take torch tensors on the GPU, allocate
+the outputs and the workspace with torch (device memory and the current stream
+are the only things torch provides) and call the same entry points. Every step
+of the computation runs in the library's HIP kernels; there is no other path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libdsaidx.so")
+
+DENSE, REUSE, REFINE = 0, 1, 2
+STATUS = {0: "OK", 1: "EINVAL", 2: "EUNSUPPORTED", 3: "EWORKSPACE", 4: "EHIP"}
+EXPORTS = ("indexer_workspace_bytes", "indexer_dense", "indexer_pivot_reuse",
+           "indexer_pivot_refine", "indexer_last_error", "indexer_version")
+
+
+class IndexerError(RuntimeError):
+    def __init__(self, status, message):
+        super().__init__(f"{STATUS.get(status, status)}: {message}")
+        self.status = status
+
+
+_lib = None
+
+
+def load(path: str = LIB_PATH):
+    """Load libdsaidx.so; raise if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(
+            f"{path} is missing: build it with `python -c 'import __graft_entry__ as g; g.build()'`")
+    lib = ctypes.CDLL(path)
+    P, i64, i32, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_size_t
+    lib.indexer_workspace_bytes.argtypes = [i32, i32, i64, i64, i32, i32, i32, i32, i32]
+    lib.indexer_workspace_bytes.restype = sz
+    lib.indexer_dense.argtypes = [P, P, P, i32, i64, i64, i32, i32, i32, P, P, P, sz, P]
+    lib.indexer_dense.restype = i32
+    for f in (lib.indexer_pivot_reuse, lib.indexer_pivot_refine):
+        f.argtypes = [P, P, P, i32, i64, i64, i32, i32, i32, i32, i32, P, P, P, P, sz, P]
+        f.restype = i32
+    lib.indexer_last_error.argtypes = []
+    lib.indexer_last_error.restype = ctypes.c_char_p
+    lib.indexer_version.argtypes = []
+    lib.indexer_version.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+# ---------------------------------------------------------------- raw C ABI
+def indexer_workspace_bytes(mode, B, L, q_len, H_I, d_I, g, c, k):
+    return load().indexer_workspace_bytes(mode, B, L, q_len, H_I, d_I, g, c, k)
+
+
+def indexer_dense(Q, W, K, B, L, q_len, H_I, d_I, k, out_idx, out_score, ws, ws_bytes, stream):
+    return load().indexer_dense(Q, W, K, B, L, q_len, H_I, d_I, k, out_idx, out_score, ws,
+                                ws_bytes, stream)
+
+
+def indexer_pivot_reuse(Q, W, K, B, L, q_len, H_I, d_I, g, c, k, out_idx, out_score, out_cand,
+                        ws, ws_bytes, stream):
+    return load().indexer_pivot_reuse(Q, W, K, B, L, q_len, H_I, d_I, g, c, k, out_idx, out_score,
+                                      out_cand, ws, ws_bytes, stream)
+
+
+def indexer_pivot_refine(Q, W, K, B, L, q_len, H_I, d_I, g, c, k, out_idx, out_score, out_cand,
+                         ws, ws_bytes, stream):
+    return load().indexer_pivot_refine(Q, W, K, B, L, q_len, H_I, d_I, g, c, k, out_idx, out_score,
+                                       out_cand, ws, ws_bytes, stream)
+
+
+def indexer_last_error():
+    return load().indexer_last_error().decode()
+
+
+def indexer_version():
+    return load().indexer_version().decode()
+
+
+# ------------------------------------------------------------ torch helpers
+def _shapes(Q, W, K):
+    import torch
+    if Q.dtype != torch.bfloat16 or K.dtype != torch.bfloat16 or W.dtype != torch.float32:
+        raise TypeError("Q and K must be bf16, W fp32")
+    if not (Q.is_cuda and W.is_cuda and K.is_cuda):
+        raise ValueError("Q, W and K must be GPU tensors")
+    if Q.dim() != 4 or W.dim() != 3 or K.dim() != 3:
+        raise ValueError("expected Q [B,q_len,H,d], W [B,q_len,H], K [B,L,d]")
+    B, q_len, H, d = Q.shape
+    if tuple(W.shape) != (B, q_len, H) or K.shape[0] != B or K.shape[2] != d:
+        raise ValueError("inconsistent Q/W/K shapes")
+    for t in (Q, W, K):
+        if not t.is_contiguous():
+            raise ValueError("Q, W and K must be contiguous")
+    return B, K.shape[1], q_len, H, d
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _check(rc):
+    if rc != 0:
+        raise IndexerError(rc, indexer_last_error())
+
+
+class Workspace:
+    """Reusable device workspace (grown on demand)."""
+
+    def __init__(self):
+        self.buf = None
+
+    def get(self, nbytes, device):
+        import torch
+        nbytes = max(int(nbytes), 256)
+        if self.buf is None or self.buf.numel() < nbytes or self.buf.device != device:
+            self.buf = torch.empty(nbytes, dtype=torch.uint8, device=device)
+        return self.buf
+
+
+_default_ws = Workspace()
+
+
+def _run(mode, Q, W, K, k, g=1, c=0, scores=True, cand=False, ws=None, out=None):
+    import torch
+    B, L, q_len, H, d = _shapes(Q, W, K)
+    dev = Q.device
+    # an invalid call sizes to 0 bytes; the entry point then reports the error
+    need = indexer_workspace_bytes(mode, B, L, q_len, H, d, g, c, k)
+    wsb = (ws or _default_ws).get(need, dev)
+    if out is None:
+        out_idx = torch.empty((B, q_len, k), dtype=torch.int32, device=dev)
+        out_score = torch.empty((B, q_len, k), dtype=torch.float32, device=dev) if scores else None
+        G = (q_len + g - 1) // g
+        out_cand = torch.empty((B, G, c), dtype=torch.int32, device=dev) if cand else None
+    else:
+        out_idx, out_score, out_cand = out
+    stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+    if mode == DENSE:
+        rc = indexer_dense(_ptr(Q), _ptr(W), _ptr(K), B, L, q_len, H, d, k, _ptr(out_idx),
+                           _ptr(out_score), _ptr(wsb), wsb.numel(), stream)
+    else:
+        f = indexer_pivot_reuse if mode == REUSE else indexer_pivot_refine
+        rc = f(_ptr(Q), _ptr(W), _ptr(K), B, L, q_len, H, d, g, c, k, _ptr(out_idx),
+               _ptr(out_score), _ptr(out_cand), _ptr(wsb), wsb.numel(), stream)
+    _check(rc)
+    return out_idx, out_score, out_cand
+
+
+def dense(Q, W, K, k, scores=True, ws=None, out=None):
+    """Dense DSA indexer: (idx [B,q_len,k] int32, score fp32 or None)."""
+    i, s, _ = _run(DENSE, Q, W, K, k, scores=scores, ws=ws, out=out)
+    return i, s
+
+
+def pivot_reuse(Q, W, K, g, k, c=0, scores=True, cand=False, ws=None, out=None):
+    """PIVOT-Reuse: (idx, score or None, cand [B,G,c] or None)."""
+    return _run(REUSE, Q, W, K, k, g=g, c=c, scores=scores, cand=cand, ws=ws, out=out)
+
+
+def pivot_refine(Q, W, K, g, c, k, scores=True, cand=False, ws=None, out=None):
+    """PIVOT-Refine: (idx, score or None, cand [B,G,c] or None)."""
+    return _run(REFINE, Q, W, K, k, g=g, c=c, scores=scores, cand=cand, ws=ws, out=out)

@@ -1,0 +1,149 @@
+// device.h - gfx950 building blocks shared by the indexer kernels: MFMA
+// operand types, order-preserving score keys, wave-level ballots/prefix counts
+// and the exact three-level radix cut used by every top-k / top-c.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dsaidx {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kWave = 64;
+
+// Register/LDS geometry of one query row (H heads of D dims) on the
+// v_mfma_f32_32x32x16_bf16 tile: heads are MFMA rows, keys MFMA columns.
+template <int H, int D>
+struct Shape {
+    static constexpr int MB = (H + 31) / 32;  // 32-head blocks (MFMA M)
+    static constexpr int KS = D / 16;         // 16-deep MFMA K-steps
+    static constexpr int ROWB = 2 * D;        // bytes of one bf16 key row
+    static constexpr int ROWS = ROWB + 16;    // padded LDS row stride (bank spread)
+    static constexpr int CHUNKS = ROWB / 16;  // 16-byte chunks per key row
+};
+
+// ---------------------------------------------------------------- score keys
+// A selection ranks keys by (score descending, index ascending). A score is
+// turned into an unsigned "key" that orders like the float (every finite
+// value, -0 folded into +0 before the conversion); equal keys are broken by
+// index, which the kernels get for free because they visit keys in
+// ascending index order.
+__device__ __forceinline__ uint32_t score_key(float f)
+{
+    uint32_t u = __float_as_uint(f);
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+__device__ __forceinline__ float key_score(uint32_t k)
+{
+    uint32_t u = (k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k;
+    return __uint_as_float(u);
+}
+
+// Level-1 bins are the top 11 bits of the key (sign, exponent, two mantissa
+// bits); level 2 the next 11 bits, level 3 the last 10.
+constexpr int kBins1 = 2048;
+constexpr int kBins2 = 2048;
+constexpr int kBins3 = 1024;
+
+__device__ __forceinline__ uint32_t bin1(uint32_t key) { return key >> 21; }
+
+// Smallest score of level-1 bin b (bins below 4 hold -inf and NaN patterns).
+__device__ __forceinline__ float bin1_floor(int b)
+{
+    return b < 4 ? -__builtin_inff() : key_score((uint32_t)b << 21);
+}
+
+// ---------------------------------------------------------------- wave tools
+__device__ __forceinline__ int lane_id() { return __lane_id(); }
+
+// number of set bits of m below the calling lane
+__device__ __forceinline__ int prefix_count(uint64_t m)
+{
+    return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
+                                     __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+}
+
+__device__ __forceinline__ uint64_t ballot(bool p) { return __ballot(p); }
+
+__device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
+
+// Sum of the two half-waves: lane l and lane l^32 both get v[l%32] + v[l%32+32]
+// (added in that order in every lane, so both halves hold the same bits).
+__device__ __forceinline__ float half_wave_sum(float v)
+{
+    // With both operands equal, the swap returns (v[l%32], v[l%32+32]) in
+    // every lane l.
+    auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float(p[0]) + __uint_as_float(p[1]);
+}
+
+// Wave-wide sum of an int (all lanes get it).
+__device__ __forceinline__ int wave_sum(int v)
+{
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1)
+        v += __shfl_xor(v, o, kWave);
+    return v;
+}
+
+// ---------------------------------------------------------------- radix cut
+// A cut describes the selected set of a scored list: an entry is in when its
+// key is above kgt, or equal to keq and among the first req such entries in
+// index order.
+struct Cut {
+    int64_t kgt;
+    uint32_t keq;
+    int req;
+};
+
+// Largest bin x with sum_{y >= x} h[y] >= target (the caller guarantees the
+// total reaches target); above = sum_{y > x} h[y]. NB is a multiple of 64.
+// One wave; h is this wave's LDS histogram; result is wave-uniform.
+template <int NB>
+__device__ __forceinline__ void find_bin(const uint32_t *h, int target, int &x, int &above)
+{
+    constexpr int P = NB / kWave;
+    const int l = lane_id();
+    int s = 0;
+#pragma unroll
+    for (int p = 0; p < P; ++p)
+        s += (int)h[l * P + p];
+    // suffix sum over lanes: t_l = sum_{l' >= l} s_l'
+    int t = s;
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) {
+        int u = __shfl_down(t, o, kWave);
+        if (l + o < kWave)
+            t += u;
+    }
+    uint64_t m = ballot(t >= target);
+    int lc = 63 - __builtin_clzll(m);  // highest lane whose suffix reaches target
+    int run = __shfl(t, lc, kWave) - __shfl(s, lc, kWave);
+    int bx = lc * P;
+    int ab = run;
+    for (int p = P - 1; p >= 0; --p) {
+        int v = (int)h[lc * P + p];
+        if (run + v >= target) {
+            bx = lc * P + p;
+            ab = run;
+            break;
+        }
+        run += v;
+    }
+    x = uniform(bx);
+    above = uniform(ab);
+}
+
+template <int NB>
+__device__ __forceinline__ void clear_hist(uint32_t *h)
+{
+#pragma unroll
+    for (int p = 0; p < NB / kWave; ++p)
+        h[p * kWave + lane_id()] = 0u;
+}
+
+}  // namespace dsaidx

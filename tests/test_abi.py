@@ -1,0 +1,103 @@
+"""The C-ABI library loads, exports every function include/dsaidx.h declares,
+and rejects invalid arguments before touching the GPU (no kernel runs here)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import sparse_attention_indexer_dense_amd as dsa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "dsaidx.h")
+OK, EINVAL, EUNSUPPORTED, EWORKSPACE = 0, 1, 2, 3
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(indexer_\w+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return dsa.load()
+
+
+def test_exports_every_declared_function(lib):
+    names = declared_functions()
+    assert set(names) == set(dsa.EXPORTS)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_version(lib):
+    assert dsa.indexer_version().startswith("dsaidx")
+
+
+def ws(mode, B=1, L=4096, q_len=4096, H=64, d=128, g=4, c=512, k=256):
+    return dsa.indexer_workspace_bytes(mode, B, L, q_len, H, d, g, c, k)
+
+
+def test_workspace_sizes():
+    assert ws(dsa.DENSE) > 0
+    assert ws(dsa.REUSE) > 0 and ws(dsa.REFINE) > 0
+    assert ws(dsa.DENSE, k=2048) > ws(dsa.DENSE, k=256)
+    # decode shape: per-row score vectors
+    assert ws(dsa.DENSE, B=32, L=65536, q_len=2, k=2048) >= 32 * 2 * 65536 * 4
+    assert ws(dsa.DENSE, B=0) == 0
+    assert ws(dsa.DENSE, H=8, d=64) == 0
+    assert ws(dsa.REFINE, c=100, k=200) == 0
+    assert ws(99) == 0
+
+
+P = ctypes.c_void_p
+
+
+def fake(addr=0x100000):
+    return P(addr)
+
+
+def call_dense(B=1, L=1024, q_len=1024, H=64, d=128, k=64, Q=None, W=None, K=None,
+               out=None, ws_ptr=None, ws_bytes=1 << 40):
+    Q = fake() if Q is None else Q
+    W = fake() if W is None else W
+    K = fake() if K is None else K
+    out = fake() if out is None else out
+    ws_ptr = fake() if ws_ptr is None else ws_ptr
+    return dsa.indexer_dense(Q, W, K, B, L, q_len, H, d, k, out, None, ws_ptr, ws_bytes, None)
+
+
+def test_dense_rejects_bad_sizes():
+    assert call_dense(B=0) == EINVAL
+    assert call_dense(q_len=2000) == EINVAL
+    assert call_dense(q_len=0) == EINVAL
+    assert call_dense(k=0) == EINVAL
+    assert call_dense(H=8, d=64) == EUNSUPPORTED
+    assert "no kernel" in dsa.indexer_last_error()
+
+
+def test_dense_rejects_bad_pointers():
+    assert call_dense(Q=P(0)) == EINVAL
+    assert call_dense(out=P(0)) == EINVAL
+    assert call_dense(Q=fake(0x100008)) == EINVAL  # not 16-byte aligned
+    assert "aligned" in dsa.indexer_last_error()
+    assert call_dense(ws_bytes=16) == EWORKSPACE
+    assert "workspace" in dsa.indexer_last_error()
+
+
+def call_pivot(fn, g=4, c=512, k=256, cand=None, ws_bytes=1 << 40, L=1024):
+    return fn(fake(), fake(), fake(), 1, L, L, 64, 128, g, c, k, fake(), None, cand,
+              fake(), ws_bytes, None)
+
+
+@pytest.mark.parametrize("fn", [dsa.indexer_pivot_reuse, dsa.indexer_pivot_refine])
+def test_pivot_rejects_bad_arguments(fn):
+    assert call_pivot(fn, g=0) == EINVAL
+    assert call_pivot(fn, c=100, k=256, cand=fake()) == EINVAL  # c < k with candidates
+    assert call_pivot(fn, ws_bytes=1) == EWORKSPACE
+
+
+def test_refine_requires_c_ge_k():
+    assert call_pivot(dsa.indexer_pivot_refine, c=100, k=256) == EINVAL
+    assert "c=" in dsa.indexer_last_error()
