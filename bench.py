@@ -1,0 +1,338 @@
+"""Benchmark of the DSA indexer and PIVOT Reuse/Refine on one MI355X.
+
+A step is one pass of the whole prefill hot path over one synthetic sequence of
+L = 131072 tokens (H_I = 64, d_I = 128, bf16; g = 4, c = 4096, k = 2048):
+the dense indexer, PIVOT-Reuse and PIVOT-Refine (pooling, proxy scan, top-c,
+re-score, top-k). Inputs are resident in HBM before timing starts. The line
+printed at the end reports scored (query, key) pairs per second for the whole
+step, top-k rows per second, the dense kernel against the bf16 MFMA roofline,
+recall of Reuse/Refine against dense, a decode step (32 requests x 65536
+cached keys, 2 new rows each, Refine) against the HBM roofline, and the CPU
+oracle timed on a bounded sample of the same workload.
+
+usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+KERNEL_SOURCES = ["sparse_attention_indexer_dense_amd/csrc/scan.hip",
+                  "sparse_attention_indexer_dense_amd/csrc/device.h",
+                  "sparse_attention_indexer_dense_amd/csrc/kernels.h"]
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_dense_scan_pivot128k.json")
+
+
+def kernel_hash():
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def dense_pairs(L, q_len):
+    off = L - q_len
+    return sum_range(off + 1, L)  # row r scores pos(r) + 1 keys
+
+
+def sum_range(a, b):
+    """a + (a+1) + ... + b."""
+    return (a + b) * (b - a + 1) // 2
+
+
+def proxy_pairs(L, q_len, g):
+    G = (q_len + g - 1) // g
+    off = L - q_len
+    return sum(off + min((m + 1) * g, q_len) for m in range(G))
+
+
+def refine_pairs(cand, L, q_len, g):
+    """Member-candidate pairs Refine scores: candidates at or before the member."""
+    import torch
+    B, G, c = cand.shape
+    off = L - q_len
+    total = 0
+    for i in range(g):
+        r = torch.arange(G, device=cand.device) * g + i
+        valid = r < q_len
+        pos = (off + r).view(1, G, 1)
+        n = ((cand >= 0) & (cand <= pos)).sum(dim=2)
+        total += int((n * valid.view(1, G)).sum())
+    return total
+
+
+def recall(test_idx, ref_idx, chunk=4096):
+    """Mean over rows of |T cap D| / |D| (rows hold ascending indices, -1 padded)."""
+    import torch
+    t = test_idx.reshape(-1, test_idx.shape[-1])
+    d = ref_idx.reshape(-1, ref_idx.shape[-1])
+    big = torch.iinfo(torch.int32).max
+    acc = 0.0
+    for s in range(0, t.shape[0], chunk):
+        tt = t[s:s + chunk]
+        dd = d[s:s + chunk]
+        ds = torch.where(dd < 0, torch.full_like(dd, big), dd).contiguous()
+        pos = torch.searchsorted(ds, tt.contiguous()).clamp(max=ds.shape[1] - 1)
+        hit = (torch.gather(ds, 1, pos) == tt) & (tt >= 0)
+        nd = (dd >= 0).sum(dim=1).clamp(min=1)
+        acc += float((hit.sum(dim=1).double() / nd.double()).sum())
+    return acc / t.shape[0]
+
+
+# ------------------------------------------------------------- CPU baseline
+_KEYS = None
+
+
+def _attach_keys(name, shape):
+    global _KEYS
+    import numpy as np
+    from multiprocessing import shared_memory
+    shm = shared_memory.SharedMemory(name=name)
+    _KEYS = (shm, np.ndarray(shape, dtype=np.uint16, buffer=shm.buf))
+
+
+def _oracle_row(args):
+    import oracle
+    q, w, n, k = args
+    sc, _ = oracle.scores(q, w, _KEYS[1], n=n)
+    oracle.select(sc, k)
+    return n
+
+
+def cpu_baseline(Q, W, K, k, L, q_len, budget_rows, seed=0):
+    """The fp64 oracle (dense rows) on a bounded random sample of rows, timed on
+    the host cores with one single-threaded oracle per worker process."""
+    import multiprocessing as mp
+    from concurrent.futures import ProcessPoolExecutor
+    from multiprocessing import shared_memory
+
+    import numpy as np
+
+    import oracle
+    import synth
+    oracle.load()
+    rng = np.random.default_rng(seed)
+    rows = np.sort(rng.choice(q_len, size=budget_rows, replace=False))
+    Kh = synth.to_u16(K[0])
+    Qh = synth.to_u16(Q[0, rows])
+    Wh = W[0, rows].cpu().numpy()
+    off = L - q_len
+    work = [(Qh[i], Wh[i], off + int(r) + 1, k) for i, r in enumerate(rows)]
+    workers = max(1, min(16, os.cpu_count() or 1, len(work)))
+    shm = shared_memory.SharedMemory(create=True, size=Kh.nbytes)
+    try:
+        np.ndarray(Kh.shape, dtype=np.uint16, buffer=shm.buf)[:] = Kh
+        ctx = mp.get_context("spawn")
+        with ProcessPoolExecutor(max_workers=workers, mp_context=ctx, initializer=_attach_keys,
+                                 initargs=(shm.name, Kh.shape)) as ex:
+            list(ex.map(_oracle_row, [(Qh[0], Wh[0], 1, k)] * workers))  # start the workers
+            t0 = time.perf_counter()
+            pairs = sum(ex.map(_oracle_row, work))
+            dt = time.perf_counter() - t0
+    finally:
+        shm.close()
+        shm.unlink()
+    return {"value": pairs / dt, "unit": "pairs/s", "cores": workers, "kind": "oracle",
+            "sample": f"dense rows of the same L={L} sequence: {len(rows)} rows drawn uniformly "
+                      f"(seed {seed}), {pairs:.3e} scored pairs, fp64 single-threaded oracle per "
+                      f"worker process, {dt:.1f} s wall",
+            "seconds": dt}
+
+
+# ------------------------------------------------------------------- decode
+def bench_decode(dsa, synth, torch, iters=20, warmup=3):
+    w = synth.WORKLOADS["decode64k"]
+    Q, W, K = synth.make(w, device="cuda")
+    ws = dsa.Workspace()
+    B, g, c, k, L = w.batch, w.g, w.c, w.k, w.L
+    out = (torch.empty((B, g, k), dtype=torch.int32, device="cuda"),
+           torch.empty((B, g, k), dtype=torch.float32, device="cuda"),
+           torch.empty((B, 1, c), dtype=torch.int32, device="cuda"))
+    for _ in range(warmup):
+        dsa.pivot_refine(Q, W, K, g, c, k, ws=ws, out=out)
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(iters):
+        dsa.pivot_refine(Q, W, K, g, c, k, ws=ws, out=out)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / iters
+    # algorithmic bytes: every cached key once, the candidate rows once, queries,
+    # weights and the outputs
+    H, d = w.H, w.d
+    nbytes = (B * L * d * 2 + B * c * d * 2 + B * g * H * d * 2 + B * g * H * 4
+              + B * g * k * 8 + B * c * 4)
+    d_idx, _ = dsa.dense(Q, W, K, k, ws=ws)
+    rec = recall(out[0], d_idx)
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    return {"workload": "decode64k", "B": B, "L": L, "g": g, "c": c, "k": k,
+            "variant": "refine", "ms_per_step": ms, "rows_per_s": B * g / (ms * 1e-3),
+            "algorithmic_bytes": nbytes, "achieved_GBps": gbs,
+            "hbm_frac": gbs / PEAK_HBM_GBS, "recall_vs_dense": rec}
+
+
+# --------------------------------------------------------------------- main
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--workload", default="pivot128k")
+    ap.add_argument("--cpu-rows", type=int, default=48,
+                    help="rows of the oracle CPU baseline (0 disables it)")
+    ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="also run one 1 GiB device copy (counter calibration)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the indexer is not "
+              "sharded across GPUs in this build.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import sparse_attention_indexer_dense_amd as dsa
+    import synth
+
+    dsa.load()
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    w = synth.WORKLOADS[args.workload]
+    print(f"[bench] generating {w.name} inputs", file=sys.stderr, flush=True)
+    Q, W, K = synth.make(w, device=dev)
+    B, L, q_len, H, d = dsa._shapes(Q, W, K)
+    k, g, c = w.k, w.g, w.c
+    variants = list(w.variants)
+
+    def alloc(cand_c=None):
+        G = (q_len + g - 1) // g
+        return (torch.empty((B, q_len, k), dtype=torch.int32, device=dev),
+                torch.empty((B, q_len, k), dtype=torch.float32, device=dev),
+                torch.empty((B, G, cand_c), dtype=torch.int32, device=dev) if cand_c else None)
+
+    outs = {"dense": alloc(), "reuse": alloc(), "refine": alloc(c)}
+    wss = {v: dsa.Workspace() for v in variants}
+
+    def run(v):
+        if v == "dense":
+            dsa.dense(Q, W, K, k, ws=wss[v], out=outs[v][:2])
+        elif v == "reuse":
+            dsa.pivot_reuse(Q, W, K, g, k, ws=wss[v], out=outs[v])
+        else:
+            dsa.pivot_refine(Q, W, K, g, c, k, ws=wss[v], out=outs[v])
+
+    print("[bench] warmup", file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        for v in variants:
+            run(v)
+    torch.cuda.synchronize()
+
+    print("[bench] timed steps", file=sys.stderr, flush=True)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(variants) + 1)]
+          for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    torch.cuda.synchronize()
+    for s in range(args.steps):
+        ev[s][0].record()
+        for i, v in enumerate(variants):
+            run(v)
+            ev[s][i + 1].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per_variant = {v: 0.0 for v in variants}
+    step_ms = 0.0
+    for s in range(args.steps):
+        for i, v in enumerate(variants):
+            per_variant[v] += ev[s][i].elapsed_time(ev[s][i + 1]) / args.steps
+        step_ms += ev[s][0].elapsed_time(ev[s][-1]) / args.steps
+
+    # work accounting (outside the timed region)
+    pd = dense_pairs(L, q_len) * B
+    pp = proxy_pairs(L, q_len, g) * B if g > 0 else 0
+    pairs = {"dense": pd}
+    if "reuse" in variants:
+        pairs["reuse"] = pp
+    if "refine" in variants:
+        pairs["refine"] = pp + refine_pairs(outs["refine"][2], L, q_len, g)
+    total_pairs = sum(pairs[v] for v in variants)
+    flop_per_pair = 2 * H * d
+    detail = {}
+    for v in variants:
+        ms = per_variant[v]
+        detail[v] = {"ms": ms, "scored_pairs": pairs[v],
+                     "pairs_per_s": pairs[v] / (ms * 1e-3),
+                     "dense_equiv_pairs_per_s": pd / (ms * 1e-3),
+                     "queries_per_s": B * q_len / (ms * 1e-3),
+                     "mfma_frac": pairs[v] * flop_per_pair / (ms * 1e-3) / (PEAK_BF16_TFLOPS * 1e12)}
+        if v != "dense":
+            detail[v]["speedup_vs_dense"] = per_variant["dense"] / ms
+            detail[v]["recall_vs_dense"] = recall(outs[v][0], outs["dense"][0])
+
+    dense_ms = per_variant["dense"]
+    achieved = pd * flop_per_pair / (dense_ms * 1e-3) / 1e12
+    traffic = None
+    if os.path.exists(TRAFFIC_FILE):
+        with open(TRAFFIC_FILE) as f:
+            tr = json.load(f)
+        if tr.get("kernel_hash") == kernel_hash() and tr.get("workload") == w.name:
+            traffic = tr.get("hbm_bytes_per_launch")
+    roofline = {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS, "traffic": traffic,
+                "kernel": "scan_select_kernel<64,128,8,dense>",
+                "flop_per_launch": pd * flop_per_pair}
+
+    if args.calibrate_copy:
+        a = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        b = torch.empty_like(a)
+        b.copy_(a)
+        torch.cuda.synchronize()
+        del a, b
+
+    decode = None
+    if not args.no_decode:
+        print("[bench] decode step", file=sys.stderr, flush=True)
+        decode = bench_decode(dsa, synth, torch)
+
+    cpu = None
+    if args.cpu_rows > 0:
+        print("[bench] cpu baseline", file=sys.stderr, flush=True)
+        cpu = cpu_baseline(Q, W, K, k, L, q_len, args.cpu_rows)
+        cpu["gpu_over_cpu"] = (total_pairs / (step_ms * 1e-3)) / cpu["value"]
+
+    value = total_pairs / (step_ms * 1e-3)
+    line = {
+        "metric": "indexer (query,key) pairs/s + top-k queries/s at L=128K; % MFMA / HBM peak",
+        "value": value, "unit": "pairs/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": step_ms, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": w.name, "batch": B, "L": L, "q_len": q_len, "H_I": H, "d_I": d,
+                   "k": k, "g": g, "c": c, "variants": variants},
+        "queries_per_s": B * q_len * len(variants) / (step_ms * 1e-3),
+        "variants": detail,
+        "roofline": roofline,
+        "decode": decode,
+        "cpu_baseline": cpu,
+        "wall_s_timed": wall,
+        "kernel_hash": kernel_hash(),
+    }
+    print(json.dumps(line))
+
+
+if __name__ == "__main__":
+    main()

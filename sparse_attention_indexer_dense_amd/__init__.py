@@ -145,7 +145,7 @@ def _run(mode, Q, W, K, k, g=1, c=0, scores=True, cand=False, ws=None, out=None)
         G = (q_len + g - 1) // g
         out_cand = torch.empty((B, G, c), dtype=torch.int32, device=dev) if cand else None
     else:
-        out_idx, out_score, out_cand = out
+        out_idx, out_score, out_cand = (tuple(out) + (None, None))[:3]
     stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
     if mode == DENSE:
         rc = indexer_dense(_ptr(Q), _ptr(W), _ptr(K), B, L, q_len, H, d, k, _ptr(out_idx),
