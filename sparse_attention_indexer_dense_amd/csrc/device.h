@@ -57,6 +57,14 @@ __device__ __forceinline__ float bin1_floor(int b)
     return b < 4 ? -__builtin_inff() : key_score((uint32_t)b << 21);
 }
 
+// max(0, x) as one v_max_i32 on the bit pattern: a finite float with the sign
+// bit set is a negative int and becomes +0; any other float keeps its bits.
+// (An fmaxf would first canonicalise x for IEEE NaN semantics: two VALU ops.)
+__device__ __forceinline__ float relu(float x)
+{
+    return __int_as_float(max(__float_as_int(x), 0));
+}
+
 // ---------------------------------------------------------------- wave tools
 __device__ __forceinline__ int lane_id() { return __lane_id(); }
 

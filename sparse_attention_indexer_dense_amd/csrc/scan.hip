@@ -31,7 +31,12 @@
 
 namespace dsaidx {
 
-constexpr int kStage = 64;  // keys per LDS stage (two 32-key MFMA N-tiles)
+// Keys per LDS stage: 128 (four 32-key MFMA N-tiles) for 8-wave workgroups,
+// 64 for 4-wave ones (two workgroups then share a CU).
+template <int NW>
+struct ScanStage {
+    static constexpr int KEYS = NW >= 8 ? 128 : 64;
+};
 
 // ----------------------------------------------------------- per-row select
 struct RowState {
@@ -48,7 +53,7 @@ struct Level1 {
 };
 
 // Level-1 part of the cut for the top-`sel` of the live entries.
-__device__ __forceinline__ Level1 level1(const uint32_t *h, const RowState &st, int sel)
+__device__ __forceinline__ Level1 level1(const uint32_t *h, RowState st, int sel)
 {
     Level1 a;
     if (st.count_ge <= sel) {
@@ -68,7 +73,7 @@ __device__ __forceinline__ Level1 level1(const uint32_t *h, const RowState &st, 
 }
 
 // Finish a cut with levels 2 and 3 (passes over the buffer); h is scratch.
-__device__ Cut finish_cut(const Entry *buf, int nbuf, uint32_t *h, const Level1 &a)
+__device__ Cut finish_cut(const Entry *buf, int nbuf, uint32_t *h, Level1 a)
 {
     Cut c;
     const int lane = lane_id();
@@ -112,7 +117,7 @@ __device__ Cut finish_cut(const Entry *buf, int nbuf, uint32_t *h, const Level1 
 
 // Write the entries of the cut, in buffer (= ascending index) order, to
 // `fan` output rows spaced `fstride` apart; pad each row to `sel` with -1/-inf.
-__device__ void emit(const Entry *buf, int nbuf, const Cut &c, int sel,
+__device__ void emit(const Entry *buf, int nbuf, Cut c, int sel,
                      int32_t *oidx, float *osc, int fan, int64_t fstride)
 {
     const int lane = lane_id();
@@ -152,8 +157,9 @@ __device__ void emit(const Entry *buf, int nbuf, const Cut &c, int sel,
 }
 
 // Keep only the top-`sel` entries of the buffer (stable, in place) and rebuild
-// the level-1 histogram from them. Used when a buffer is about to overflow.
-__device__ void compact(Entry *buf, uint32_t *h, RowState &st, int sel)
+// the level-1 histogram from them; returns the new state. Used when a buffer
+// is about to overflow. (State travels by value so it stays in registers.)
+__device__ __noinline__ RowState compact(Entry *buf, uint32_t *h, RowState st, int sel)
 {
     const int lane = lane_id();
     __threadfence_block();
@@ -192,6 +198,7 @@ __device__ void compact(Entry *buf, uint32_t *h, RowState &st, int sel)
     else
         st.theta_exact = (c.kgt + 1 < (4ll << 21)) ? -__builtin_inff() : key_score((uint32_t)(c.kgt + 1));
     st.theta = fmaxf(st.theta_exact, bin1_floor(st.b));
+    return st;
 }
 
 // ------------------------------------------------------------- block plans
@@ -199,7 +206,7 @@ struct WaveRow {
     bool valid;
     const uint16_t *q;
     const float *w;
-    int64_t lim;  // last eligible key index
+    int lim;      // last eligible key index (< 2^31)
     int32_t *o1;
     float *s1;
     int fan1;
@@ -211,7 +218,7 @@ struct WaveRow {
 struct BlockKeys {
     const uint16_t *Kb;   // keys of this batch item
     const int32_t *list;  // candidate list (kRefine) or nullptr (prefix)
-    int64_t nkeys;        // list length, or number of prefix keys
+    int nkeys;            // list length, or number of prefix keys (< 2^31)
 };
 
 template <int H, int D, int NW, int MODE>
@@ -232,13 +239,13 @@ __device__ __forceinline__ void plan_block(const ScanParams &p, int64_t j, int w
         const int64_t row = (int64_t)bi * p.q_len + r;
         wr.q = p.Q + row * H * D;
         wr.w = p.W + row * H;
-        wr.lim = off + r;
+        wr.lim = (int)(off + r);
         wr.o1 = p.o1_idx + row * p.sel;
         wr.s1 = p.o1_score ? p.o1_score + row * p.sel : nullptr;
         wr.fan1 = 1;
         bk.Kb = p.K + (int64_t)bi * p.L * D;
         bk.list = nullptr;
-        bk.nkeys = off + rlast + 1;
+        bk.nkeys = (int)(off + rlast + 1);
     } else if (MODE == kProxy) {
         const int64_t rb = p.nblk_per_batch - 1 - jj;
         const int64_t m = rb * NW + wave;
@@ -249,9 +256,9 @@ __device__ __forceinline__ void plan_block(const ScanParams &p, int64_t j, int w
         const int64_t r1 = (r0 + p.g < p.q_len) ? r0 + p.g : p.q_len;
         wr.q = p.Q + grow * H * D;
         wr.w = p.W + grow * H;
-        wr.lim = off + r1 - 1;
+        wr.lim = (int)(off + r1 - 1);
         const int64_t r1last = ((mlast + 1) * p.g < p.q_len) ? (mlast + 1) * p.g : p.q_len;
-        bk.nkeys = off + r1last;
+        bk.nkeys = (int)(off + r1last);
         // output 1: candidate rows [B][G][sel] or the member rows
         if (p.o1_members) {
             const int64_t row = (int64_t)bi * p.q_len + r0;
@@ -281,31 +288,95 @@ __device__ __forceinline__ void plan_block(const ScanParams &p, int64_t j, int w
         const int64_t row = (int64_t)bi * p.q_len + r;
         wr.q = p.Q + row * H * D;
         wr.w = p.W + row * H;
-        wr.lim = off + r;
+        wr.lim = (int)(off + r);
         wr.o1 = p.o1_idx + row * p.sel;
         wr.s1 = p.o1_score ? p.o1_score + row * p.sel : nullptr;
         wr.fan1 = 1;
         const int64_t t_last = off + r1 - 1;
         bk.Kb = p.K + (int64_t)bi * p.L * D;
         bk.list = p.cand + ((int64_t)bi * p.G + m) * p.c;
-        bk.nkeys = (p.c < t_last + 1) ? p.c : t_last + 1;
+        bk.nkeys = (int)((p.c < t_last + 1) ? p.c : t_last + 1);
     }
 }
 
 // ------------------------------------------------------------------ kernel
+// Keys of one stage live in LDS as rows of 2*D bytes whose 16-byte chunks are
+// XOR-swizzled by the row index (chunk c of row n sits at slot c ^ (n % CHUNKS)),
+// so that the 32 rows one MFMA B-fragment read touches spread over all banks.
+// Stages are filled by global->LDS DMA (global_load_lds_dwordx4): lane l of a
+// DMA instruction writes the l-th 16 bytes of a 1 KiB span, so it fetches the
+// global chunk that belongs in that slot. A candidate list (Refine) travels the
+// same way, one int per lane, into a per-stage LDS array.
+template <int D, int NW, int STAGE>
+struct StageDma {
+    static constexpr int ROWB = 2 * D;
+    static constexpr int CHUNKS = ROWB / 16;
+    static constexpr int RPI = kWave / CHUNKS;                  // key rows per DMA instruction
+    static constexpr int PER_STAGE = STAGE * ROWB / 1024;       // DMA instructions per stage
+    static constexpr int PER_WAVE = (PER_STAGE + NW - 1) / NW;  // per wave
+};
+
+// Key index of the row this lane fetches for its DMA slot j of stage t (-1: none).
+template <int D, int NW, int STAGE>
+__device__ __forceinline__ int stage_key(const BlockKeys &bk, int t, int wave, int lane, int j)
+{
+    using SD = StageDma<D, NW, STAGE>;
+    const int i = wave + NW * j;
+    if (i >= SD::PER_STAGE)
+        return -1;
+    const int pp = t * STAGE + i * SD::RPI + lane / SD::CHUNKS;
+    if (pp >= bk.nkeys)
+        return -1;
+    return bk.list ? bk.list[pp] : pp;
+}
+
+template <int D, int NW, int STAGE>
+__device__ __forceinline__ void stage_issue(unsigned char *kbuf, int32_t *lbuf, const BlockKeys &bk, int L,
+                                            int t, const int (&keys)[StageDma<D, NW, STAGE>::PER_WAVE],
+                                            int wave, int lane)
+{
+    using SD = StageDma<D, NW, STAGE>;
+#pragma unroll
+    for (int j = 0; j < SD::PER_WAVE; ++j) {
+        const int i = wave + NW * j;
+        if (i < SD::PER_STAGE) {
+            const int n = i * SD::RPI + lane / SD::CHUNKS;
+            const int c = (lane % SD::CHUNKS) ^ (n & (SD::CHUNKS - 1));
+            const int key = keys[j];
+            if (key >= 0 && key < L) {
+                __builtin_amdgcn_global_load_lds(
+                    (const __attribute__((address_space(1))) void *)(bk.Kb + (int64_t)key * D + c * 8),
+                    (__attribute__((address_space(3))) void *)(kbuf + i * 1024), 16, 0, 0);
+            }
+        }
+    }
+    if (bk.list && wave == NW - 1) {
+#pragma unroll
+        for (int h0 = 0; h0 < STAGE; h0 += kWave) {
+            const int pp = t * STAGE + h0 + lane;
+            if (pp < bk.nkeys)
+                __builtin_amdgcn_global_load_lds(
+                    (const __attribute__((address_space(1))) void *)(bk.list + pp),
+                    (__attribute__((address_space(3))) void *)(lbuf + h0), 4, 0, 0);
+        }
+    }
+}
+
 template <int H, int D, int NW, int MODE>
 __global__ __launch_bounds__(NW * kWave) void scan_select_kernel(ScanParams p)
 {
     using S = Shape<H, D>;
-    constexpr int MB = S::MB, KS = S::KS, ROWS = S::ROWS, CHUNKS = S::CHUNKS;
-    constexpr int NT = NW * kWave;
-    constexpr int STAGE_CHUNKS = kStage * CHUNKS;
-    constexpr int LPT = (STAGE_CHUNKS + NT - 1) / NT;  // 16-byte loads per thread per stage
-    constexpr int STAGE_BYTES = kStage * ROWS;
+    constexpr int STAGE = ScanStage<NW>::KEYS;
+    using SD = StageDma<D, NW, STAGE>;
+    constexpr int MB = S::MB, KS = S::KS, ROWB = S::ROWB, CHUNKS = S::CHUNKS;
+    constexpr int STAGE_BYTES = STAGE * ROWB;
+    constexpr int TILES = STAGE / 32;
 
-    extern __shared__ __align__(16) unsigned char smem[];
-    unsigned char *kst = smem;
-    uint32_t *hist_all = reinterpret_cast<uint32_t *>(smem + 2 * STAGE_BYTES);
+    __shared__ __align__(1024) unsigned char kA[STAGE_BYTES];
+    __shared__ __align__(1024) unsigned char kB[STAGE_BYTES];
+    __shared__ __align__(16) int32_t lA[MODE == kRefine ? STAGE : 1];
+    __shared__ __align__(16) int32_t lB[MODE == kRefine ? STAGE : 1];
+    __shared__ uint32_t hist_all[NW * kBins1];
 
     const int tid = threadIdx.x;
     const int wave = tid / kWave;
@@ -314,6 +385,12 @@ __global__ __launch_bounds__(NW * kWave) void scan_select_kernel(ScanParams p)
     const int col = lane & 31;
     uint32_t *h = hist_all + wave * kBins1;
     Entry *buf = p.slots + ((int64_t)blockIdx.x * NW + wave) * p.cap;
+
+    // lane-constant LDS byte offsets of this lane's B-fragment chunks in a stage
+    uint32_t koff[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+        koff[ks] = (uint32_t)(col * ROWB + (((half * KS + ks) ^ (col & (CHUNKS - 1))) * 16));
 
     for (int64_t it = 0;; ++it) {
         const int64_t j = it * gridDim.x + ((it & 1) ? (gridDim.x - 1 - blockIdx.x) : blockIdx.x);
@@ -349,122 +426,137 @@ __global__ __launch_bounds__(NW * kWave) void scan_select_kernel(ScanParams p)
         st.b = 0;
         st.count_ge = 0;
         st.nbuf = 0;
+        int hb = 0;  // h[st.b], kept in step with the histogram
         if (wr.valid)
             clear_hist<kBins1>(h);
 
-        const int64_t nkeys = bk.nkeys;
-        const int64_t ntiles = (nkeys + kStage - 1) / kStage;
-        u32x4 regs[LPT];
+        const int nkeys = bk.nkeys;
+        const int lim = wr.valid ? wr.lim : -1;
+        // prefix keys: positions above `last` are never eligible for this row
+        const int last = (nkeys - 1 < lim) ? nkeys - 1 : lim;
+        const int ntiles = (nkeys + STAGE - 1) / STAGE;
 
-        auto load_stage = [&](int64_t t) {
+        // one 32-key tile of stage t held in (kb, lb)
+        auto tile = [&](const unsigned char *kb, const int32_t *lb, int t, int nt) {
+            const int p0 = t * STAGE + nt * 32;
+            if (MODE == kRefine ? (p0 >= nkeys || lim < 0) : (p0 > last))
+                return;
+            f32x16 acc[MB];
 #pragma unroll
-            for (int i = 0; i < LPT; ++i) {
-                const int c = tid + i * NT;
-                u32x4 v = {0u, 0u, 0u, 0u};
-                if (c < STAGE_CHUNKS) {
-                    const int kk = c / CHUNKS, part = c % CHUNKS;
-                    const int64_t pp = t * kStage + kk;
-                    if (pp < nkeys) {
-                        const int64_t key = bk.list ? (int64_t)bk.list[pp] : pp;
-                        if (key >= 0 && key < p.L)
-                            v = *reinterpret_cast<const u32x4 *>(bk.Kb + key * D + part * 8);
-                    }
+            for (int mb = 0; mb < MB; ++mb)
+                acc[mb] = f32x16{};
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                u32x4 kv = *reinterpret_cast<const u32x4 *>(kb + koff[ks] + nt * 32 * ROWB);
+                bf16x8 kf = __builtin_bit_cast(bf16x8, kv);
+#pragma unroll
+                for (int mb = 0; mb < MB; ++mb)
+                    acc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[mb][ks], kf, acc[mb], 0, 0, 0);
+            }
+            // epilogue: ReLU, head weights, head sum
+            float part = 0.f;
+#pragma unroll
+            for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+                for (int r = 0; r < 16; ++r)
+                    part = fmaf(wv[mb][r], relu(acc[mb][r]), part);
+            const float total = half_wave_sum(part) + 0.0f;
+
+            // causal mask and threshold filter (lanes 0..31 own the 32 keys)
+            int key;
+            bool ok;
+            if (MODE == kRefine) {
+                key = lb[nt * 32 + col];
+                ok = lane < 32 && col < nkeys - p0 && key <= lim;
+            } else {
+                key = p0 + col;
+                ok = lane < 32 && col <= last - p0;
+            }
+            const bool adm = ok && total > st.theta;
+            const uint64_t m = ballot(adm);
+            if (m) {
+                const uint32_t sk = score_key(total);
+                const int bin = (int)(sk >> 21);
+                if (adm) {
+                    Entry e;
+                    e.score = total;
+                    e.idx = key;
+                    buf[st.nbuf + prefix_count(m)] = e;
+                    atomicAdd(&h[bin], 1u);
                 }
-                regs[i] = v;
+                const int cnt = __popcll(m);
+                st.nbuf += cnt;
+                st.count_ge += cnt;
+                hb += __popcll(ballot(adm && bin == st.b));
             }
         };
-        auto store_stage = [&](int s) {
-#pragma unroll
-            for (int i = 0; i < LPT; ++i) {
-                const int c = tid + i * NT;
-                if (c < STAGE_CHUNKS) {
-                    const int kk = c / CHUNKS, part = c % CHUNKS;
-                    *reinterpret_cast<u32x4 *>(kst + s * STAGE_BYTES + kk * ROWS + part * 16) = regs[i];
+
+        // after a stage: raise the threshold bin, compact a nearly full buffer
+        auto stage_end = [&]() {
+            if (!wr.valid)
+                return;
+            if (st.count_ge - hb >= p.sel) {
+                int bb = st.b, cg = st.count_ge, hv = hb;
+                // a step or two: walk; otherwise search all bins at once
+                for (int step = 0; step < 2 && cg - hv >= p.sel && bb < kBins1 - 1; ++step) {
+                    cg -= hv;
+                    ++bb;
+                    hv = uniform((int)h[bb]);
                 }
+                if (cg - hv >= p.sel) {
+                    int x, above;
+                    find_bin<kBins1>(h, p.sel, x, above);
+                    bb = x;
+                    hv = uniform((int)h[x]);
+                    cg = above + hv;
+                }
+                st.b = bb;
+                st.count_ge = cg;
+                hb = hv;
+                st.theta = fmaxf(st.theta_exact, bin1_floor(st.b));
+            }
+            if (st.nbuf > p.cap - STAGE) {
+                st = compact(buf, h, st, p.sel);
+                hb = uniform((int)h[st.b]);
             }
         };
 
-        if (ntiles > 0) {
-            load_stage(0);
-            store_stage(0);
-        }
+        auto compute = [&](const unsigned char *kb, const int32_t *lb, int t) {
+            if (!wr.valid)
+                return;
+#pragma unroll
+            for (int nt = 0; nt < TILES; ++nt)
+                tile(kb, lb, t, nt);
+            stage_end();
+        };
+
+        // key indices of this wave's DMA slots, one stage ahead
+        int keys[SD::PER_WAVE];
+        auto fetch_keys = [&](int t) {
+#pragma unroll
+            for (int jj = 0; jj < SD::PER_WAVE; ++jj)
+                keys[jj] = (t < ntiles) ? stage_key<D, NW, STAGE>(bk, t, wave, lane, jj) : -1;
+        };
+
+        fetch_keys(0);
+        if (ntiles > 0)
+            stage_issue<D, NW, STAGE>(kA, lA, bk, (int)p.L, 0, keys, wave, lane);
+        fetch_keys(1);
         __syncthreads();
-
-        for (int64_t t = 0; t < ntiles; ++t) {
-            const int s = (int)(t & 1);
+        // two stages per trip so that each LDS buffer is a distinct object at
+        // every access (the DMA into one overlaps the MFMA reads of the other)
+        for (int t = 0; t < ntiles; t += 2) {
             if (t + 1 < ntiles)
-                load_stage(t + 1);
-            if (wr.valid) {
-#pragma unroll
-                for (int nt = 0; nt < kStage / 32; ++nt) {
-                    const int64_t p0 = t * kStage + nt * 32;
-                    if (p0 >= nkeys)
-                        break;
-                    const int64_t first = bk.list ? (int64_t)bk.list[p0] : p0;
-                    if (first > wr.lim)
-                        break;
-                    f32x16 acc[MB];
-#pragma unroll
-                    for (int mb = 0; mb < MB; ++mb)
-                        acc[mb] = f32x16{};
-                    const unsigned char *kb_base = kst + s * STAGE_BYTES + (nt * 32 + col) * ROWS;
-#pragma unroll
-                    for (int ks = 0; ks < KS; ++ks) {
-                        u32x4 kv = *reinterpret_cast<const u32x4 *>(kb_base + (half * KS + ks) * 16);
-                        bf16x8 kb = __builtin_bit_cast(bf16x8, kv);
-#pragma unroll
-                        for (int mb = 0; mb < MB; ++mb)
-                            acc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[mb][ks], kb, acc[mb], 0, 0, 0);
-                    }
-                    // epilogue: ReLU, head weights, head sum (Eq. (1))
-                    float part = 0.f;
-#pragma unroll
-                    for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-                        for (int r = 0; r < 16; ++r)
-                            part = fmaf(wv[mb][r], fmaxf(acc[mb][r], 0.f), part);
-                    const float total = half_wave_sum(part) + 0.0f;
-
-                    // causal mask and threshold filter (lanes 0..31 own the 32 keys)
-                    const int64_t pidx = p0 + col;
-                    bool ok = false;
-                    int64_t key = -1;
-                    if (lane < 32 && pidx < nkeys) {
-                        key = bk.list ? (int64_t)bk.list[pidx] : pidx;
-                        ok = key <= wr.lim;
-                    }
-                    const bool adm = ok && total > st.theta;
-                    const uint64_t m = ballot(adm);
-                    if (m) {
-                        const int cnt = __popcll(m);
-                        if (adm) {
-                            const int pos = st.nbuf + prefix_count(m);
-                            Entry e;
-                            e.score = total;
-                            e.idx = (int32_t)key;
-                            buf[pos] = e;
-                            atomicAdd(&h[bin1(score_key(total))], 1u);
-                        }
-                        st.nbuf += cnt;
-                        st.count_ge += cnt;
-                        int bb = st.b, cg = st.count_ge;
-                        while (bb < kBins1 - 1) {
-                            const int hb = (int)h[bb];
-                            if (cg - hb < p.sel)
-                                break;
-                            cg -= hb;
-                            ++bb;
-                        }
-                        st.b = uniform(bb);
-                        st.count_ge = uniform(cg);
-                        st.theta = fmaxf(st.theta_exact, bin1_floor(st.b));
-                        if (st.nbuf > p.cap - kWave)
-                            compact(buf, h, st, p.sel);
-                    }
-                }
-            }
-            if (t + 1 < ntiles)
-                store_stage(s ^ 1);
+                stage_issue<D, NW, STAGE>(kB, lB, bk, (int)p.L, t + 1, keys, wave, lane);
+            fetch_keys(t + 2);
+            compute(kA, lA, t);
+            __syncthreads();
+            if (t + 1 >= ntiles)
+                break;
+            if (t + 2 < ntiles)
+                stage_issue<D, NW, STAGE>(kA, lA, bk, (int)p.L, t + 2, keys, wave, lane);
+            fetch_keys(t + 3);
+            compute(kB, lB, t + 1);
             __syncthreads();
         }
 
@@ -481,6 +573,7 @@ __global__ __launch_bounds__(NW * kWave) void scan_select_kernel(ScanParams p)
                 emit(buf, st.nbuf, c2, p.sel2, wr.o2, wr.s2, wr.fan2, p.sel2);
             }
         }
+        __syncthreads();
     }
 }
 
@@ -530,16 +623,7 @@ __global__ __launch_bounds__(256) void pool_kernel(PoolParams p)
 template <int H, int D, int NW, int MODE>
 static hipError_t launch_scan(const ScanParams &prm, int grid, hipStream_t stream)
 {
-    constexpr size_t lds = 2 * kStage * Shape<H, D>::ROWS + (size_t)NW * kBins1 * 4;
-    static bool attr = false;
-    if (!attr) {
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&scan_select_kernel<H, D, NW, MODE>),
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-        if (e != hipSuccess)
-            return e;
-        attr = true;
-    }
-    hipLaunchKernelGGL((scan_select_kernel<H, D, NW, MODE>), dim3(grid), dim3(NW * kWave), lds, stream, prm);
+    hipLaunchKernelGGL((scan_select_kernel<H, D, NW, MODE>), dim3(grid), dim3(NW * kWave), 0, stream, prm);
     return hipGetLastError();
 }
 
@@ -552,9 +636,9 @@ static hipError_t launch_pool_t(const PoolParams &prm, hipStream_t stream)
 
 size_t scan_lds_bytes(int H, int D, int NW)
 {
-    int rows = 2 * D + 16;
     (void)H;
-    return 2 * (size_t)kStage * rows + (size_t)NW * kBins1 * 4;
+    const int stage = NW >= 8 ? ScanStage<8>::KEYS : ScanStage<4>::KEYS;
+    return 2 * (size_t)stage * 2 * D + (size_t)NW * kBins1 * 4;
 }
 
 hipError_t launch_scan_select(int H, int D, int NW, int mode, const ScanParams &prm, int grid,

@@ -153,7 +153,7 @@ __global__ __launch_bounds__(kSplitWaves * kWave) void split_score_kernel(SplitS
         for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
             for (int rr = 0; rr < 16; ++rr)
-                part = fmaf(wv[mb][rr], fmaxf(acc[mb][rr], 0.f), part);
+                part = fmaf(wv[mb][rr], relu(acc[mb][rr]), part);
         const float total = half_wave_sum(part) + 0.0f;
         const int64_t pos = pt + col;
         if (lane < 32 && pos < p1) {
