@@ -45,9 +45,11 @@ int hip_fail(hipError_t e, const char *what)
 
 // Rows per batch item at or below which a stage uses the split-key kernels.
 constexpr int64_t kSplitRowsMax = 64;
-// Persistent workgroups of the scan kernels are capped at this many; the
-// workspace holds one set of candidate buffers per slot.
-constexpr int64_t kGridSlots = 512;
+// Persistent workgroups of the scan kernels: at most as many as fit at once
+// on the 256 CUs of an MI355X (LDS decides: one 8-wave or two 4-wave
+// workgroups per CU); the workspace holds one set of row buffers per slot.
+constexpr int64_t kCus = 256;
+constexpr size_t kLdsPerCu = 160 * 1024;
 constexpr int64_t kMaxSel = 1 << 20;
 constexpr size_t kAlign = 256;
 
@@ -57,12 +59,49 @@ int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 bool supported(int H, int D) { return (H == 64 && D == 128) || (H == 4 && D == 32); }
 
+// Entries per row buffer. A row admits about sel * (1 + ln(n / sel)) keys
+// while its threshold rises (plus the width of a histogram bin), so a buffer
+// of 16 sel entries is compacted only on adversarial inputs; it never needs
+// more than the row's keys plus one stage.
 int scan_cap(int64_t sel, int64_t L)
 {
-    int64_t cap = std::max<int64_t>(2 * sel, sel + 2048);
+    int64_t cap = std::max<int64_t>(16 * sel, sel + 4096);
     cap = std::min<int64_t>(cap, L + 128);
     cap = std::max<int64_t>(cap, sel + 128);
     return (int)ceil_div(cap, 64) * 64;
+}
+
+int num_cus()
+{
+    static thread_local int cached_dev = -1;
+    static thread_local int cached_cus = 0;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess)
+        return 0;
+    if (dev != cached_dev) {
+        int cus = 0;
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+            return 0;
+        cached_dev = dev;
+        cached_cus = cus;
+    }
+    return cached_cus;
+}
+
+int64_t scan_slots(int H, int D, int NW)
+{
+    const size_t lds = scan_lds_bytes(H, D, NW);
+    return kCus * std::max<int64_t>(1, (int64_t)(kLdsPerCu / lds));
+}
+
+int scan_grid(int H, int D, int NW, int64_t nblocks)
+{
+    const size_t lds = scan_lds_bytes(H, D, NW);
+    const int per_cu = std::max<int>(1, (int)(kLdsPerCu / lds));
+    int64_t grid = (int64_t)std::max(1, num_cus()) * per_cu;
+    grid = std::min<int64_t>(grid, scan_slots(H, D, NW));
+    grid = std::min<int64_t>(grid, nblocks);
+    return (int)std::max<int64_t>(grid, 1);
 }
 
 // Workspace layout of one call.
@@ -104,7 +143,7 @@ int make_plan(int mode, int B, int64_t L, int64_t q_len, int H, int D, int64_t g
             off += align_up((size_t)B * q_len * L * sizeof(float));
         } else {
             pl.off_slots = off;
-            off += align_up((size_t)kGridSlots * pl.nw_scan * pl.cap_scan * sizeof(Entry));
+            off += align_up((size_t)scan_slots(H, D, pl.nw_scan) * pl.nw_scan * pl.cap_scan * sizeof(Entry));
         }
         pl.total = off;
         return DSAIDX_OK;
@@ -136,7 +175,7 @@ int make_plan(int mode, int B, int64_t L, int64_t q_len, int H, int D, int64_t g
     // scan stage
     size_t scan_bytes = pl.split_scan
         ? (size_t)B * pl.G * L * sizeof(float)
-        : (size_t)kGridSlots * pl.nw_scan * pl.cap_scan * sizeof(Entry);
+        : (size_t)scan_slots(H, D, pl.nw_scan) * pl.nw_scan * pl.cap_scan * sizeof(Entry);
     size_t refine_bytes = 0;
     if (mode == DSAIDX_REFINE) {
         pl.split_refine = q_len <= kSplitRowsMax;
@@ -144,7 +183,7 @@ int make_plan(int mode, int B, int64_t L, int64_t q_len, int H, int D, int64_t g
         pl.cap_refine = (int)ceil_div(c + 128, 64) * 64;
         refine_bytes = pl.split_refine
             ? (size_t)B * q_len * c * sizeof(float)
-            : (size_t)kGridSlots * pl.nw_refine * pl.cap_refine * sizeof(Entry);
+            : (size_t)scan_slots(H, D, pl.nw_refine) * pl.nw_refine * pl.cap_refine * sizeof(Entry);
     }
     // the scan's buffers/scores and Refine's are used one after the other
     pl.off_slots = off;
@@ -152,33 +191,6 @@ int make_plan(int mode, int B, int64_t L, int64_t q_len, int H, int D, int64_t g
     off += align_up(std::max(scan_bytes, refine_bytes));
     pl.total = off;
     return DSAIDX_OK;
-}
-
-int num_cus()
-{
-    static thread_local int cached_dev = -1;
-    static thread_local int cached_cus = 0;
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess)
-        return 0;
-    if (dev != cached_dev) {
-        int cus = 0;
-        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
-            return 0;
-        cached_dev = dev;
-        cached_cus = cus;
-    }
-    return cached_cus;
-}
-
-int scan_grid(int H, int D, int NW, int64_t nblocks)
-{
-    const size_t lds = scan_lds_bytes(H, D, NW);
-    const int per_cu = std::max<int>(1, (int)((160 * 1024) / lds));
-    int64_t grid = (int64_t)std::max(1, num_cus()) * per_cu;
-    grid = std::min<int64_t>(grid, kGridSlots);
-    grid = std::min<int64_t>(grid, nblocks);
-    return (int)std::max<int64_t>(grid, 1);
 }
 
 bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }

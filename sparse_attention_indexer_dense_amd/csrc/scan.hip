@@ -72,6 +72,30 @@ __device__ __forceinline__ Level1 level1(const uint32_t *h, RowState st, int sel
     return a;
 }
 
+// Visit buf[0..nbuf) in index order, 64 entries per wave step, with the loads
+// of four steps issued together so that passes are not latency-bound.
+// f(entry, valid) runs once per step and lane.
+template <typename F>
+__device__ __forceinline__ void buffer_pass(const Entry *buf, int nbuf, F &&f)
+{
+    constexpr int U = 4;
+    const int lane = lane_id();
+    for (int base = 0; base < nbuf; base += U * kWave) {
+        Entry e[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int i = base + u * kWave + lane;
+            e[u].score = 0.f;
+            e[u].idx = -1;
+            if (i < nbuf)
+                e[u] = buf[i];
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+            f(e[u], base + u * kWave + lane < nbuf);
+    }
+}
+
 // Finish a cut with levels 2 and 3 (passes over the buffer); h is scratch.
 __device__ Cut finish_cut(const Entry *buf, int nbuf, uint32_t *h, Level1 a)
 {
@@ -84,11 +108,11 @@ __device__ Cut finish_cut(const Entry *buf, int nbuf, uint32_t *h, Level1 a)
         return c;
     }
     clear_hist<kBins2>(h);
-    for (int i = lane; i < nbuf; i += kWave) {
-        uint32_t key = score_key(buf[i].score);
-        if ((int)(key >> 21) == a.b1)
+    buffer_pass(buf, nbuf, [&](const Entry &e, bool v) {
+        const uint32_t key = score_key(e.score);
+        if (v && (int)(key >> 21) == a.b1)
             atomicAdd(&h[(key >> 10) & (kBins2 - 1)], 1u);
-    }
+    });
     int b2, a2;
     find_bin<kBins2>(h, a.r1, b2, a2);
     int r2 = a.r1 - a2;
@@ -101,11 +125,11 @@ __device__ Cut finish_cut(const Entry *buf, int nbuf, uint32_t *h, Level1 a)
         return c;
     }
     clear_hist<kBins3>(h);
-    for (int i = lane; i < nbuf; i += kWave) {
-        uint32_t key = score_key(buf[i].score);
-        if ((key >> 10) == pre)
+    buffer_pass(buf, nbuf, [&](const Entry &e, bool v) {
+        const uint32_t key = score_key(e.score);
+        if (v && (key >> 10) == pre)
             atomicAdd(&h[key & (kBins3 - 1)], 1u);
-    }
+    });
     int b3, a3;
     find_bin<kBins3>(h, r2, b3, a3);
     uint32_t kstar = (pre << 10) | (uint32_t)b3;
@@ -122,21 +146,14 @@ __device__ void emit(const Entry *buf, int nbuf, Cut c, int sel,
 {
     const int lane = lane_id();
     int emitted = 0, eqseen = 0;
-    for (int base = 0; base < nbuf; base += kWave) {
-        int i = base + lane;
-        bool v = i < nbuf;
-        Entry e;
-        e.score = 0.f;
-        e.idx = -1;
-        if (v)
-            e = buf[i];
-        uint32_t key = score_key(e.score);
-        bool eq = v && c.req > 0 && key == c.keq;
-        uint64_t meq = ballot(eq);
-        int er = eqseen + prefix_count(meq);
-        bool in = v && ((int64_t)key > c.kgt || (eq && er < c.req));
-        uint64_t min_ = ballot(in);
-        int pos = emitted + prefix_count(min_);
+    buffer_pass(buf, nbuf, [&](const Entry &e, bool v) {
+        const uint32_t key = score_key(e.score);
+        const bool eq = v && c.req > 0 && key == c.keq;
+        const uint64_t meq = ballot(eq);
+        const int er = eqseen + prefix_count(meq);
+        const bool in = v && ((int64_t)key > c.kgt || (eq && er < c.req));
+        const uint64_t min_ = ballot(in);
+        const int pos = emitted + prefix_count(min_);
         if (in && pos < sel) {
             for (int f = 0; f < fan; ++f) {
                 oidx[f * fstride + pos] = e.idx;
@@ -146,7 +163,7 @@ __device__ void emit(const Entry *buf, int nbuf, Cut c, int sel,
         }
         emitted += __popcll(min_);
         eqseen += __popcll(meq);
-    }
+    });
     for (int x = emitted + lane; x < sel; x += kWave) {
         for (int f = 0; f < fan; ++f) {
             oidx[f * fstride + x] = -1;
@@ -161,34 +178,28 @@ __device__ void emit(const Entry *buf, int nbuf, Cut c, int sel,
 // is about to overflow. (State travels by value so it stays in registers.)
 __device__ __noinline__ RowState compact(Entry *buf, uint32_t *h, RowState st, int sel)
 {
-    const int lane = lane_id();
     __threadfence_block();
     Level1 a = level1(h, st, sel);
     Cut c = finish_cut(buf, st.nbuf, h, a);
     int kept = 0, eqseen = 0;
-    for (int base = 0; base < st.nbuf; base += kWave) {
-        int i = base + lane;
-        bool v = i < st.nbuf;
-        Entry e;
-        e.score = 0.f;
-        e.idx = -1;
-        if (v)
-            e = buf[i];
-        uint32_t key = score_key(e.score);
-        bool eq = v && c.req > 0 && key == c.keq;
-        uint64_t meq = ballot(eq);
-        int er = eqseen + prefix_count(meq);
-        bool in = v && ((int64_t)key > c.kgt || (eq && er < c.req));
-        uint64_t min_ = ballot(in);
-        int pos = kept + prefix_count(min_);
+    // every write lands at or below the index of the entry it moves, and the
+    // loads of a batch precede its writes: no entry is overwritten unread
+    buffer_pass(buf, st.nbuf, [&](const Entry &e, bool v) {
+        const uint32_t key = score_key(e.score);
+        const bool eq = v && c.req > 0 && key == c.keq;
+        const uint64_t meq = ballot(eq);
+        const int er = eqseen + prefix_count(meq);
+        const bool in = v && ((int64_t)key > c.kgt || (eq && er < c.req));
+        const uint64_t min_ = ballot(in);
+        const int pos = kept + prefix_count(min_);
         if (in)
-            buf[pos] = e;  // pos <= i: never overwrites an entry not yet read
+            buf[pos] = e;
         kept += __popcll(min_);
         eqseen += __popcll(meq);
-    }
+    });
     __threadfence_block();
     clear_hist<kBins1>(h);
-    for (int i = lane; i < kept; i += kWave)
+    for (int i = lane_id(); i < kept; i += kWave)
         atomicAdd(&h[bin1(score_key(buf[i].score))], 1u);
     st.nbuf = kept;
     st.count_ge = kept;
@@ -362,8 +373,10 @@ __device__ __forceinline__ void stage_issue(unsigned char *kbuf, int32_t *lbuf, 
     }
 }
 
+// Two waves per SIMD: one 8-wave workgroup, or two 4-wave workgroups, per CU.
 template <int H, int D, int NW, int MODE>
-__global__ __launch_bounds__(NW * kWave) void scan_select_kernel(ScanParams p)
+__global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void scan_select_kernel(ScanParams p)
 {
     using S = Shape<H, D>;
     constexpr int STAGE = ScanStage<NW>::KEYS;
@@ -436,33 +449,66 @@ __global__ __launch_bounds__(NW * kWave) void scan_select_kernel(ScanParams p)
         const int last = (nkeys - 1 < lim) ? nkeys - 1 : lim;
         const int ntiles = (nkeys + STAGE - 1) / STAGE;
 
-        // one 32-key tile of stage t held in (kb, lb)
-        auto tile = [&](const unsigned char *kb, const int32_t *lb, int t, int nt) {
-            const int p0 = t * STAGE + nt * 32;
-            if (MODE == kRefine ? (p0 >= nkeys || lim < 0) : (p0 > last))
-                return;
-            f32x16 acc[MB];
+        // MFMA score tile of 32 keys (tile nt of the stage in kb)
+        auto mfma_tile = [&](const unsigned char *kb, int nt, f32x16 (&acc)[MB]) {
+            constexpr int KB = KS >= 4 ? 4 : KS;  // K fragments in flight at once
 #pragma unroll
             for (int mb = 0; mb < MB; ++mb)
                 acc[mb] = f32x16{};
 #pragma unroll
-            for (int ks = 0; ks < KS; ++ks) {
-                u32x4 kv = *reinterpret_cast<const u32x4 *>(kb + koff[ks] + nt * 32 * ROWB);
-                bf16x8 kf = __builtin_bit_cast(bf16x8, kv);
+            for (int k0 = 0; k0 < KS; k0 += KB) {
+                bf16x8 kf[KB];
 #pragma unroll
-                for (int mb = 0; mb < MB; ++mb)
-                    acc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[mb][ks], kf, acc[mb], 0, 0, 0);
+                for (int ks = 0; ks < KB; ++ks)
+                    kf[ks] = __builtin_bit_cast(
+                        bf16x8, *reinterpret_cast<const u32x4 *>(kb + koff[k0 + ks] + nt * 32 * ROWB));
+#pragma unroll
+                for (int ks = 0; ks < KB; ++ks)
+#pragma unroll
+                    for (int mb = 0; mb < MB; ++mb)
+                        acc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[mb][k0 + ks], kf[ks], acc[mb], 0, 0, 0);
             }
-            // epilogue: ReLU, head weights, head sum
-            float part = 0.f;
+        };
+        // epilogue: ReLU, head weights, head sum (one partial sum per head block)
+        auto epilogue = [&](const f32x16 (&acc)[MB]) {
+            float part[MB];
 #pragma unroll
-            for (int mb = 0; mb < MB; ++mb)
+            for (int mb = 0; mb < MB; ++mb) {
+                part[mb] = 0.f;
 #pragma unroll
                 for (int r = 0; r < 16; ++r)
-                    part = fmaf(wv[mb][r], relu(acc[mb][r]), part);
-            const float total = half_wave_sum(part) + 0.0f;
-
-            // causal mask and threshold filter (lanes 0..31 own the 32 keys)
+                    part[mb] = fmaf(wv[mb][r], relu(acc[mb][r]), part[mb]);
+            }
+            float s = part[0];
+#pragma unroll
+            for (int mb = 1; mb < MB; ++mb)
+                s += part[mb];
+            return half_wave_sum(s) + 0.0f;
+        };
+        // raise the threshold bin while the bins above it hold >= sel entries:
+        // a step or two by walking, a longer jump by searching all bins at once
+        auto advance = [&]() {
+            int bb = st.b, cg = st.count_ge, hv = hb;
+            for (int step = 0; step < 2 && cg - hv >= p.sel && bb < kBins1 - 1; ++step) {
+                cg -= hv;
+                ++bb;
+                hv = uniform((int)h[bb]);
+            }
+            if (cg - hv >= p.sel) {
+                int x, above;
+                find_bin<kBins1>(h, p.sel, x, above);
+                bb = x;
+                hv = uniform((int)h[x]);
+                cg = above + hv;
+            }
+            st.b = bb;
+            st.count_ge = cg;
+            hb = hv;
+            st.theta = fmaxf(st.theta_exact, bin1_floor(st.b));
+        };
+        // causal mask and threshold filter of tile nt (lanes 0..31 own the 32 keys)
+        auto filter = [&](float total, const int32_t *lb, int t, int nt) {
+            const int p0 = t * STAGE + nt * 32;
             int key;
             bool ok;
             if (MODE == kRefine) {
@@ -488,45 +534,58 @@ __global__ __launch_bounds__(NW * kWave) void scan_select_kernel(ScanParams p)
                 st.nbuf += cnt;
                 st.count_ge += cnt;
                 hb += __popcll(ballot(adm && bin == st.b));
+                if (st.count_ge - hb >= p.sel)
+                    advance();
             }
         };
 
-        // after a stage: raise the threshold bin, compact a nearly full buffer
+        // after a stage: compact a nearly full buffer
         auto stage_end = [&]() {
             if (!wr.valid)
                 return;
-            if (st.count_ge - hb >= p.sel) {
-                int bb = st.b, cg = st.count_ge, hv = hb;
-                // a step or two: walk; otherwise search all bins at once
-                for (int step = 0; step < 2 && cg - hv >= p.sel && bb < kBins1 - 1; ++step) {
-                    cg -= hv;
-                    ++bb;
-                    hv = uniform((int)h[bb]);
-                }
-                if (cg - hv >= p.sel) {
-                    int x, above;
-                    find_bin<kBins1>(h, p.sel, x, above);
-                    bb = x;
-                    hv = uniform((int)h[x]);
-                    cg = above + hv;
-                }
-                st.b = bb;
-                st.count_ge = cg;
-                hb = hv;
-                st.theta = fmaxf(st.theta_exact, bin1_floor(st.b));
-            }
             if (st.nbuf > p.cap - STAGE) {
                 st = compact(buf, h, st, p.sel);
                 hb = uniform((int)h[st.b]);
             }
         };
 
+        // the active tiles of a stage, software-pipelined: the MFMAs of tile
+        // nt+1 are issued next to the epilogue of tile nt so that the matrix
+        // pipe and the VALU work at the same time
         auto compute = [&](const unsigned char *kb, const int32_t *lb, int t) {
             if (!wr.valid)
                 return;
+            const int pf = t * STAGE;
+            const int span = (MODE == kRefine) ? nkeys - pf : last - pf + 1;
+            const int ntl = span <= 0 ? 0 : (span >= STAGE ? TILES : (span + 31) / 32);
+            if (ntl == 0)
+                return;
+            f32x16 a0[MB], a1[MB];
+            mfma_tile(kb, 0, a0);
 #pragma unroll
-            for (int nt = 0; nt < TILES; ++nt)
-                tile(kb, lb, t, nt);
+            for (int nt = 0; nt < TILES; ++nt) {
+                if (nt >= ntl)
+                    break;
+                float total;
+                if (nt + 1 < ntl) {
+                    if (nt & 1) {
+                        mfma_tile(kb, nt + 1, a0);
+                        total = epilogue(a1);
+                    } else {
+                        mfma_tile(kb, nt + 1, a1);
+                        total = epilogue(a0);
+                    }
+                    // interleave: one MFMA per four VALU ops
+#pragma unroll
+                    for (int q = 0; q < KS * MB; ++q) {
+                        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                        __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+                    }
+                } else {
+                    total = (nt & 1) ? epilogue(a1) : epilogue(a0);
+                }
+                filter(total, lb, t, nt);
+            }
             stage_end();
         };
 

@@ -42,7 +42,9 @@ def ws(mode, B=1, L=4096, q_len=4096, H=64, d=128, g=4, c=512, k=256):
 def test_workspace_sizes():
     assert ws(dsa.DENSE) > 0
     assert ws(dsa.REUSE) > 0 and ws(dsa.REFINE) > 0
-    assert ws(dsa.DENSE, k=2048) > ws(dsa.DENSE, k=256)
+    # row buffers grow with the selection size (up to one row's keys)
+    assert ws(dsa.DENSE, L=131072, q_len=131072, k=2048) > ws(dsa.DENSE, L=131072, q_len=131072, k=256)
+    assert ws(dsa.DENSE, k=2048) == ws(dsa.DENSE, k=4000)  # capped by L
     # decode shape: per-row score vectors
     assert ws(dsa.DENSE, B=32, L=65536, q_len=2, k=2048) >= 32 * 2 * 65536 * 4
     assert ws(dsa.DENSE, B=0) == 0
