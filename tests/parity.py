@@ -1,7 +1,7 @@
 """GPU-vs-oracle parity drivers shared by the GPU test files and the smoke check.
 
 Every function runs the HIP library through the C ABI (via the Python binding),
-copies the very input tensors it used to the host, recomputes the selected rows
+copies to the host the very input rows it needs, recomputes the selected rows
 with the fp64 oracle and applies the parity rule of ``checker``.
 """
 from __future__ import annotations
@@ -15,12 +15,39 @@ import synth
 from checker import Result, check_row
 
 
-def host(Q, W, K):
-    return synth.to_u16(Q), W.detach().cpu().numpy(), synth.to_u16(K)
-
-
 def _rows_all(B, q_len):
     return [(b, r) for b in range(B) for r in range(q_len)]
+
+
+def groups_all(B, G):
+    return [(b, m) for b in range(B) for m in range(G)]
+
+
+class HostView:
+    """Host copies of K per batch item (on demand) and of individual Q/W rows."""
+
+    def __init__(self, Q, W, K):
+        self.Q, self.W, self.K = Q, W, K
+        self._k = {}
+
+    def keys(self, b):
+        if b not in self._k:
+            self._k[b] = synth.to_u16(self.K[b])
+        return self._k[b]
+
+    def rows(self, b, r0, r1):
+        return synth.to_u16(self.Q[b, r0:r1]), self.W[b, r0:r1].detach().cpu().numpy()
+
+
+def check_dense_rows(idx, sc, hv, L, q_len, k, rows, res=None):
+    """Check GPU dense output rows (host arrays idx/sc [B, q_len, k]) for `rows`."""
+    res = Result() if res is None else res
+    for b, r in rows:
+        pos = L - q_len + r
+        q, w = hv.rows(b, r, r + 1)
+        ref, mass = oracle.scores(q[0], w[0], hv.keys(b), n=pos + 1)
+        check_row(idx[b, r], sc[b, r], np.arange(pos + 1), ref, mass, k, res, f"dense b{b} r{r}")
+    return res
 
 
 def check_dense(Q, W, K, k, rows=None, out=None):
@@ -28,43 +55,27 @@ def check_dense(Q, W, K, k, rows=None, out=None):
     idx, sc = dsa.dense(Q, W, K, k)
     torch.cuda.synchronize()
     idx, sc = idx.cpu().numpy(), sc.cpu().numpy()
-    Qh, Wh, Kh = host(Q, W, K)
-    B, q_len = Qh.shape[:2]
-    L = Kh.shape[1]
-    res = Result() if out is None else out
-    for b, r in (rows or _rows_all(B, q_len)):
-        pos = L - q_len + r
-        ref, mass = oracle.scores(Qh[b, r], Wh[b, r], Kh[b], n=pos + 1)
-        check_row(idx[b, r], sc[b, r], np.arange(pos + 1), ref, mass, k, res, f"dense b{b} r{r}")
+    B, q_len = Q.shape[:2]
+    L = K.shape[1]
+    hv = HostView(Q, W, K)
+    res = check_dense_rows(idx, sc, hv, L, q_len, k, rows or _rows_all(B, q_len), out)
     return res, idx, sc
 
 
-def groups_all(B, G):
-    return [(b, m) for b in range(B) for m in range(G)]
-
-
-def check_pivot(Q, W, K, g, c, k, variant, groups=None, with_cand=True):
-    """PIVOT Reuse or Refine: candidates vs the oracle's proxy scan, Reuse rows
-    vs the proxy top-k (identical within a group), Refine rows vs the oracle
-    re-scoring the GPU's own candidates (checked first)."""
-    if variant == "reuse":
-        idx, sc, cand = dsa.pivot_reuse(Q, W, K, g, k, c=c, cand=with_cand)
-    else:
-        idx, sc, cand = dsa.pivot_refine(Q, W, K, g, c, k, cand=True)
-    torch.cuda.synchronize()
-    idx, sc = idx.cpu().numpy(), sc.cpu().numpy()
-    cand = cand.cpu().numpy() if cand is not None else None
-    Qh, Wh, Kh = host(Q, W, K)
-    B, q_len = Qh.shape[:2]
-    L = Kh.shape[1]
-    G = (q_len + g - 1) // g
+def check_pivot_rows(variant, idx, sc, cand, hv, L, q_len, g, c, k, groups):
+    """Check PIVOT outputs (host arrays) for `groups` [(b, m)]: candidates vs the
+    oracle's proxy scan, Reuse rows vs the proxy top-k (identical within a
+    group), Refine rows vs the oracle re-scoring the GPU's own candidates."""
     res_c, res_r = Result(), Result()
-    for b, m in (groups or groups_all(B, G)):
+    for b, m in groups:
         r0, r1 = m * g, min(m * g + g, q_len)
         t_last = L - q_len + r1 - 1
-        qb, wb = oracle.proxy(Qh[b], Wh[b], g, m)
-        ref, mass = oracle.scores(qb, wb, Kh[b], n=t_last + 1)
-        univ = np.arange(t_last + 1)
+        Qm, Wm = hv.rows(b, r0, r1)
+        qb, wb = oracle.proxy(Qm, Wm, g, 0)
+        univ = None
+        if cand is not None or variant == "reuse":
+            ref, mass = oracle.scores(qb, wb, hv.keys(b), n=t_last + 1)
+            univ = np.arange(t_last + 1)
         if cand is not None:
             check_row(cand[b, m], None, univ, ref, mass, c, res_c, f"cand b{b} m{m}")
         for r in range(r0, r1):
@@ -76,8 +87,26 @@ def check_pivot(Q, W, K, g, c, k, variant, groups=None, with_cand=True):
                 pos = L - q_len + r
                 cm = cand[b, m]
                 cp = cm[(cm >= 0) & (cm <= pos)]
-                ref_i, mass_i = oracle.scores(Qh[b, r], Wh[b, r], np.ascontiguousarray(Kh[b][cp]))
+                kc = np.ascontiguousarray(hv.keys(b)[cp])
+                ref_i, mass_i = oracle.scores(Qm[r - r0], Wm[r - r0], kc)
                 check_row(idx[b, r], sc[b, r], cp, ref_i, mass_i, k, res_r, f"refine b{b} r{r}")
+    return res_c, res_r
+
+
+def check_pivot(Q, W, K, g, c, k, variant, groups=None, with_cand=True):
+    if variant == "reuse":
+        idx, sc, cand = dsa.pivot_reuse(Q, W, K, g, k, c=c, cand=with_cand)
+    else:
+        idx, sc, cand = dsa.pivot_refine(Q, W, K, g, c, k, cand=True)
+    torch.cuda.synchronize()
+    idx, sc = idx.cpu().numpy(), sc.cpu().numpy()
+    cand = cand.cpu().numpy() if cand is not None else None
+    B, q_len = Q.shape[:2]
+    L = K.shape[1]
+    G = (q_len + g - 1) // g
+    hv = HostView(Q, W, K)
+    res_c, res_r = check_pivot_rows(variant, idx, sc, cand, hv, L, q_len, g, c, k,
+                                    groups or groups_all(B, G))
     return res_c, res_r, idx, sc, cand
 
 
