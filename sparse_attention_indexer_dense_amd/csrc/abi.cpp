@@ -212,11 +212,14 @@ int check_ptrs(const void *Q, const float *W, const void *K, const int32_t *out_
     return DSAIDX_OK;
 }
 
+// Positions per workgroup of split_score_kernel: about 4096 waves in all, each
+// covering 128..kSplitSpanMax contiguous positions (long enough to amortise
+// loading its 16 KiB query row).
 int64_t split_chunk(int64_t rows_total, int64_t npos)
 {
-    int64_t ch = ceil_div(rows_total * npos, 4096);
-    ch = ceil_div(ch, 128) * 128;
-    return std::min<int64_t>(std::max<int64_t>(ch, 128), 4096);
+    int64_t per_wave = ceil_div(ceil_div(rows_total * npos, 4096), 32) * 32;
+    per_wave = std::min<int64_t>(std::max<int64_t>(per_wave, 128), kSplitSpanMax);
+    return per_wave * kSplitWaves;
 }
 
 // Score + select `nrows` rows per batch item with the split-key kernels.

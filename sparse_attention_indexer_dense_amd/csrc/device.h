@@ -108,9 +108,24 @@ struct Cut {
     int req;
 };
 
+// Inclusive suffix sum over the lanes of a wave: lane l gets sum_{l' >= l} v.
+__device__ __forceinline__ int wave_suffix_sum(int v)
+{
+    const int l = lane_id();
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) {
+        const int u = __shfl_down(v, o, kWave);
+        if (l + o < kWave)
+            v += u;
+    }
+    return v;
+}
+
 // Largest bin x with sum_{y >= x} h[y] >= target (the caller guarantees the
 // total reaches target); above = sum_{y > x} h[y]. NB is a multiple of 64.
-// One wave; h is this wave's LDS histogram; result is wave-uniform.
+// One wave; h is an LDS histogram; the result is wave-uniform. Lane l first
+// sums bins [l*P, (l+1)*P); the crossing lane's bins are then resolved 64 at
+// a time, top down, with a wave suffix scan (no serial walk).
 template <int NB>
 __device__ __forceinline__ void find_bin(const uint32_t *h, int target, int &x, int &above)
 {
@@ -120,27 +135,24 @@ __device__ __forceinline__ void find_bin(const uint32_t *h, int target, int &x, 
 #pragma unroll
     for (int p = 0; p < P; ++p)
         s += (int)h[l * P + p];
-    // suffix sum over lanes: t_l = sum_{l' >= l} s_l'
-    int t = s;
-#pragma unroll
-    for (int o = 1; o < kWave; o <<= 1) {
-        int u = __shfl_down(t, o, kWave);
-        if (l + o < kWave)
-            t += u;
-    }
-    uint64_t m = ballot(t >= target);
-    int lc = 63 - __builtin_clzll(m);  // highest lane whose suffix reaches target
-    int run = __shfl(t, lc, kWave) - __shfl(s, lc, kWave);
-    int bx = lc * P;
-    int ab = run;
-    for (int p = P - 1; p >= 0; --p) {
-        int v = (int)h[lc * P + p];
-        if (run + v >= target) {
-            bx = lc * P + p;
-            ab = run;
+    const int t = wave_suffix_sum(s);
+    const uint64_t m = ballot(t >= target);
+    const int lc = 63 - __builtin_clzll(m);  // highest lane whose suffix reaches target
+    int run = uniform(__shfl(t, lc, kWave) - __shfl(s, lc, kWave));
+    int bx = lc * P, ab = run;
+    for (int top = P; top > 0; top -= kWave) {
+        const int lo = top > kWave ? top - kWave : 0;  // bins [lo, top) of lane lc's range
+        const int i = lo + l;
+        const int v = (i < top) ? (int)h[lc * P + i] : 0;
+        const int sv = wave_suffix_sum(v) + run;    // run + sum of bins [i, top)
+        const uint64_t mm = ballot(i < top && sv >= target);
+        if (mm) {
+            const int li = 63 - __builtin_clzll(mm);
+            bx = lc * P + lo + li;
+            ab = __shfl(sv - v, li, kWave);
             break;
         }
-        run += v;
+        run = uniform(__shfl(sv, 0, kWave));  // all of [lo, top) added
     }
     x = uniform(bx);
     above = uniform(ab);

@@ -79,6 +79,7 @@ struct SplitSelectParams {
 };
 
 constexpr int kSplitWaves = 4;
+constexpr int kSplitSpanMax = 1024;  // key positions one wave of split_score_kernel covers
 constexpr int kSelectThreads = 1024;
 
 size_t scan_lds_bytes(int H, int D, int NW);

@@ -100,7 +100,6 @@ __device__ __forceinline__ void buffer_pass(const Entry *buf, int nbuf, F &&f)
 __device__ Cut finish_cut(const Entry *buf, int nbuf, uint32_t *h, Level1 a)
 {
     Cut c;
-    const int lane = lane_id();
     if (a.all || a.r1 == a.h1) {
         c.kgt = (int64_t)a.b1 * (1ll << 21) - 1;
         c.keq = 0u;
@@ -392,7 +391,7 @@ void scan_select_kernel(ScanParams p)
     __shared__ uint32_t hist_all[NW * kBins1];
 
     const int tid = threadIdx.x;
-    const int wave = tid / kWave;
+    const int wave = uniform(tid / kWave);  // wave-uniform (SGPR)
     const int lane = tid % kWave;
     const int half = lane >> 5;
     const int col = lane & 31;

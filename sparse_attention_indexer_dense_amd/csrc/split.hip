@@ -4,16 +4,20 @@
 // drafts of one step) scores only g new rows per request against a long
 // cache, so there are too few rows to fill the GPU with one workgroup per row.
 // The key axis is split instead:
-//   split_score_kernel  - workgroups own (batch item, row, key chunk); every
-//                         wave stages 32 keys at a time through its own LDS
-//                         tile with coalesced 16-byte loads (or gathers the
-//                         candidate rows, for Refine), computes the 64-head
-//                         score tile with bf16 MFMA and the ReLU/weight/head-sum
+//   split_score_kernel  - a workgroup owns (batch item, row, span of key
+//                         positions); each wave streams its own contiguous
+//                         part of the span in 32-key tiles through a private
+//                         pair of LDS buffers filled by global->LDS DMA (the
+//                         DMA of tile t+1 overlaps the MFMAs on tile t), runs
+//                         the MFMA score tile and the ReLU/weight/head-sum
 //                         epilogue, and stores one fp32 score per position;
-//   split_select_kernel - one workgroup per score row runs the exact
-//                         three-level radix cut (ties to the lower index) and
-//                         writes the selection in ascending index order.
-// Only per-row score vectors of the few decode rows are stored.
+//   split_select_kernel - one workgroup per score row finds the exact top-sel
+//                         (ties to the lower index) in three passes: a
+//                         level-1 histogram; per-wave counts of the sure
+//                         entries plus the boundary bin gathered into LDS and
+//                         resolved there; one ordered emission in ascending
+//                         index order at per-wave offsets.
+// Only the score vectors of the few decode rows are stored.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -27,12 +31,11 @@ struct SplitRow {
     const uint16_t *q;
     const float *w;
     const int32_t *list;  // kRefine: the group's candidate list
-    int64_t npos;         // positions to consider
-    int64_t lim;          // last eligible key index
+    int npos;             // positions to consider
+    int lim;              // last eligible key index
 };
 
-template <int H, int D>
-__device__ __forceinline__ SplitRow split_row(const SplitScoreParams &p, int bi, int64_t r)
+__device__ __forceinline__ SplitRow split_row(const SplitScoreParams &p, int H, int D, int bi, int64_t r)
 {
     SplitRow s;
     const int64_t off = p.L - p.q_len;
@@ -42,13 +45,13 @@ __device__ __forceinline__ SplitRow split_row(const SplitScoreParams &p, int bi,
         s.q = p.Q + grow * H * D;
         s.w = p.W + grow * H;
         s.list = nullptr;
-        s.lim = off + r1 - 1;
+        s.lim = (int)(off + r1 - 1);
         s.npos = s.lim + 1;
     } else {
         const int64_t row = (int64_t)bi * p.q_len + r;
         s.q = p.Q + row * H * D;
         s.w = p.W + row * H;
-        s.lim = off + r;
+        s.lim = (int)(off + r);
         if (p.mode == kDense) {
             s.list = nullptr;
             s.npos = s.lim + 1;
@@ -57,35 +60,83 @@ __device__ __forceinline__ SplitRow split_row(const SplitScoreParams &p, int bi,
             const int64_t r1 = ((m + 1) * p.g < p.q_len) ? (m + 1) * p.g : p.q_len;
             const int64_t t_last = off + r1 - 1;
             s.list = p.cand + ((int64_t)bi * p.G + m) * p.c;
-            s.npos = (p.c < t_last + 1) ? p.c : t_last + 1;
+            s.npos = (int)((p.c < t_last + 1) ? p.c : t_last + 1);
         }
     }
     return s;
 }
 
-template <int H, int D>
+// ------------------------------------------------------------------ scoring
+// s_waitcnt with only the vector-memory counter constrained to <= n (gfx9
+// encoding: vmcnt bits [3:0] and [15:14]; expcnt and lgkmcnt left at max).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt()
+{
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// Each wave streams its span of positions through a private ring of kRing
+// LDS tiles of 32 keys; tile t+kRing-1 is in flight while tile t is scored.
+// Every tile costs exactly DMA_PER_TILE DMA instructions (lanes without a key
+// fetch row 0 into a slot that is never read) and exactly one score store, so
+// the number of vector-memory operations issued after tile t's DMA is known
+// and the wait for it is exact.
+constexpr int kRing = 4;
+
+template <int H, int D, bool LIST>
 __global__ __launch_bounds__(kSplitWaves * kWave) void split_score_kernel(SplitScoreParams p)
 {
     using S = Shape<H, D>;
-    constexpr int MB = S::MB, KS = S::KS, ROWS = S::ROWS, CHUNKS = S::CHUNKS;
-    constexpr int TILE_CHUNKS = 32 * CHUNKS;
-    constexpr int LPL = (TILE_CHUNKS + kWave - 1) / kWave;  // 16-byte loads per lane per tile
-    __shared__ __align__(16) unsigned char tiles[kSplitWaves][32 * ROWS];
+    constexpr int MB = S::MB, KS = S::KS, ROWB = S::ROWB, CHUNKS = S::CHUNKS;
+    constexpr int TILE_BYTES = 32 * ROWB;
+    constexpr int DMA_PER_TILE = TILE_BYTES / 1024;
+    constexpr int RPI = kWave / CHUNKS;  // key rows per DMA instruction
+    __shared__ __align__(1024) unsigned char ring[kSplitWaves][kRing][TILE_BYTES];
+    __shared__ int32_t lst[kSplitWaves][LIST ? kSplitSpanMax : 1];
 
     const int bi = blockIdx.z;
     const int64_t r = blockIdx.y;
-    const int wave = threadIdx.x / kWave;
+    const int wave = uniform(threadIdx.x / kWave);  // wave-uniform (SGPR)
     const int lane = threadIdx.x % kWave;
     const int half = lane >> 5;
     const int col = lane & 31;
-    const SplitRow sr = split_row<H, D>(p, bi, r);
-    const int64_t p0 = (int64_t)blockIdx.x * p.chunk;
-    if (p0 >= sr.npos)
+    const SplitRow sr = split_row(p, H, D, bi, r);
+    const int span = (int)(p.chunk / kSplitWaves);
+    const int w0 = (int)(blockIdx.x * p.chunk) + wave * span;
+    if (w0 >= sr.npos)
         return;
-    const int64_t p1 = (p0 + p.chunk < sr.npos) ? p0 + p.chunk : sr.npos;
+    const int w1 = (w0 + span < sr.npos) ? w0 + span : sr.npos;
+    const int ntile = (w1 - w0 + 31) / 32;
     const uint16_t *Kb = p.K + (int64_t)bi * p.L * D;
     float *out = p.scores + ((int64_t)bi * p.nrows + r) * p.rowlen;
-    unsigned char *tile = tiles[wave];
+    int32_t *wl = lst[wave];
+
+    if (LIST) {
+        for (int x = lane; x < w1 - w0; x += kWave)
+            wl[x] = sr.list[w0 + x];
+        __builtin_amdgcn_wave_barrier();
+    }
+
+    // DMA of tile t into ring slot t % kRing: lane l of instruction i fetches
+    // the chunk that the XOR swizzle puts in slot l of the i-th KiB
+    auto issue = [&](int t) {
+        unsigned char *dst = ring[wave][t % kRing];
+#pragma unroll
+        for (int i = 0; i < DMA_PER_TILE; ++i) {
+            const int n = i * RPI + lane / CHUNKS;
+            const int pos = w0 + t * 32 + n;
+            const int c = (lane % CHUNKS) ^ (n & (CHUNKS - 1));
+            int key = 0;
+            if (t < ntile && pos < w1) {
+                key = LIST ? wl[pos - w0] : pos;
+                key = (key >= 0 && key < p.L) ? key : 0;
+            }
+            __builtin_amdgcn_global_load_lds(
+                (const __attribute__((address_space(1))) void *)(Kb + (int64_t)key * D + c * 8),
+                (__attribute__((address_space(3))) void *)(dst + i * 1024), 16, 0, 0);
+        }
+    };
 
     bf16x8 qa[MB][KS];
     float wv[MB][16];
@@ -105,90 +156,158 @@ __global__ __launch_bounds__(kSplitWaves * kWave) void split_score_kernel(SplitS
             wv[mb][rr] = hr < H ? sr.w[hr] : 0.f;
         }
     }
-
-    for (int64_t pt = p0 + wave * 32; pt < p1; pt += kSplitWaves * 32) {
-        // stage 32 key rows: consecutive lanes read consecutive 16-byte chunks
-        u32x4 regs[LPL];
+    uint32_t koff[KS];
 #pragma unroll
-        for (int i = 0; i < LPL; ++i) {
-            const int c = lane + i * kWave;
-            u32x4 v = {0u, 0u, 0u, 0u};
-            if (c < TILE_CHUNKS) {
-                const int kk = c / CHUNKS, part = c % CHUNKS;
-                const int64_t pos = pt + kk;
-                if (pos < p1) {
-                    const int64_t key = sr.list ? (int64_t)sr.list[pos] : pos;
-                    if (key >= 0 && key < p.L)
-                        v = *reinterpret_cast<const u32x4 *>(Kb + key * D + part * 8);
-                }
-            }
-            regs[i] = v;
-        }
-        __builtin_amdgcn_wave_barrier();
-#pragma unroll
-        for (int i = 0; i < LPL; ++i) {
-            const int c = lane + i * kWave;
-            if (c < TILE_CHUNKS) {
-                const int kk = c / CHUNKS, part = c % CHUNKS;
-                *reinterpret_cast<u32x4 *>(tile + kk * ROWS + part * 16) = regs[i];
-            }
-        }
-        __builtin_amdgcn_wave_barrier();
+    for (int ks = 0; ks < KS; ++ks)
+        koff[ks] = (uint32_t)(col * ROWB + (((half * KS + ks) ^ (col & (CHUNKS - 1))) * 16));
 
+    auto tile = [&](int t) {
+        const unsigned char *src = ring[wave][t % kRing];
         f32x16 acc[MB];
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb)
             acc[mb] = f32x16{};
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
-            u32x4 kv = *reinterpret_cast<const u32x4 *>(tile + col * ROWS + (half * KS + ks) * 16);
-            bf16x8 kb = __builtin_bit_cast(bf16x8, kv);
+            const bf16x8 kf = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(src + koff[ks]));
 #pragma unroll
             for (int mb = 0; mb < MB; ++mb)
-                acc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[mb][ks], kb, acc[mb], 0, 0, 0);
+                acc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[mb][ks], kf, acc[mb], 0, 0, 0);
         }
-        __builtin_amdgcn_wave_barrier();
-        float part = 0.f;
+        float part[MB];
 #pragma unroll
-        for (int mb = 0; mb < MB; ++mb)
+        for (int mb = 0; mb < MB; ++mb) {
+            part[mb] = 0.f;
 #pragma unroll
             for (int rr = 0; rr < 16; ++rr)
-                part = fmaf(wv[mb][rr], relu(acc[mb][rr]), part);
-        const float total = half_wave_sum(part) + 0.0f;
-        const int64_t pos = pt + col;
-        if (lane < 32 && pos < p1) {
-            const int64_t key = sr.list ? (int64_t)sr.list[pos] : pos;
-            if (key <= sr.lim)
-                out[pos] = total;
+                part[mb] = fmaf(wv[mb][rr], relu(acc[mb][rr]), part[mb]);
         }
+        float s = part[0];
+#pragma unroll
+        for (int mb = 1; mb < MB; ++mb)
+            s += part[mb];
+        const float total = half_wave_sum(s) + 0.0f;
+        // one store instruction per tile: lane 0 always holds a position of
+        // the tile; positions whose key is beyond the row's limit get a score
+        // too, which the selection ignores
+        const int pos = w0 + t * 32 + col;
+        if (lane < 32 && pos < w1)
+            out[pos] = total;
+    };
+
+    // operands loaded, then the ring primed with kRing - 1 tiles
+    __builtin_amdgcn_s_waitcnt(0);
+    for (int t = 0; t < kRing - 1; ++t)
+        issue(t);
+    for (int t = 0; t < ntile; ++t) {
+        __builtin_amdgcn_sched_barrier(0);
+        if (t == 0)
+            wait_vmcnt<(kRing - 2) * DMA_PER_TILE>();
+        else if (t == 1)
+            wait_vmcnt<(kRing - 2) * DMA_PER_TILE + 1>();
+        else if (t == 2)
+            wait_vmcnt<(kRing - 2) * DMA_PER_TILE + 2>();
+        else
+            wait_vmcnt<(kRing - 2) * DMA_PER_TILE + 3>();
+        __builtin_amdgcn_sched_barrier(0);
+        issue(t + kRing - 1);
+        tile(t);
     }
+    // no DMA may still be writing this workgroup's LDS when it exits
+    __builtin_amdgcn_s_waitcnt(0);
 }
 
-// ------------------------------------------------------------- selection
+// ---------------------------------------------------------------- selection
 constexpr int kSelWaves = kSelectThreads / kWave;
+constexpr int kBoundaryCap = 4096;  // boundary-bin entries resolved in LDS
+constexpr int kQuadsPerLane = 8;    // float4 loads in flight per lane and pass
 
 struct SelRow {
     const float *sc;
     const int32_t *list;
-    int64_t npos, lim;
+    int npos, lim;
 };
 
-struct BlockScratch {
-    uint32_t h1[kBins1];
+// Row selection bins: level 1 = top 14 bits of the score key (sign, exponent,
+// five mantissa bits), then 9 + 9 bits inside the boundary bin.
+constexpr int kSelBins1 = 16384;
+constexpr int kSelBins2 = 512;
+
+struct SelScratch {
+    uint32_t h1[kSelBins1];
     uint32_t hs[kBins2];
-    int wtot[kSelWaves];
-    int bc[4];
+    uint32_t bkey[kBoundaryCap];
+    int32_t bpos[kBoundaryCap];
+    int wgt[kSelWaves];  // per wave: sure entries (bin above the cut bin)
+    int wbd[kSelWaves];  // per wave: selected boundary entries
+    int woff[kSelWaves];
+    int nb;
+    int bc[8];
 };
 
-__device__ __forceinline__ bool sel_valid(const SelRow &s, int64_t pos)
+__device__ __forceinline__ bool sel_valid(const SelRow &s, int pos)
 {
-    return pos < s.npos && (s.list == nullptr || (int64_t)s.list[pos] <= s.lim);
+    return pos < s.npos && (s.list == nullptr || s.list[pos] <= s.lim);
 }
 
-// Exclusive prefix count of `flag` over the block in thread order, and the total.
+// The row's positions split into kSelWaves contiguous segments; a wave walks
+// its segment in steps of 256 positions (one float4 per lane), kQuadsPerLane
+// steps per batch with all their loads issued first.
+struct Segment {
+    int b, e;
+};
+
+__device__ __forceinline__ Segment wave_segment(int npos, int wave)
+{
+    const int per = (((npos + kSelWaves - 1) / kSelWaves) + 255) / 256 * 256;
+    Segment g;
+    g.b = wave * per;
+    g.e = (g.b + per < npos) ? g.b + per : npos;
+    if (g.b > npos)
+        g.b = npos;
+    return g;
+}
+
+template <typename F>
+__device__ __forceinline__ void segment_pass(const SelRow &s, Segment g, F &&f)
+{
+    const int lane = threadIdx.x % kWave;
+    for (int base = g.b; base < g.e; base += kQuadsPerLane * 256) {
+        float v[kQuadsPerLane][4];
+#pragma unroll
+        for (int u = 0; u < kQuadsPerLane; ++u) {
+            const int p0 = base + u * 256 + lane * 4;
+#pragma unroll
+            for (int x = 0; x < 4; ++x)
+                v[u][x] = (p0 + x < g.e) ? s.sc[p0 + x] : 0.f;
+        }
+#pragma unroll
+        for (int u = 0; u < kQuadsPerLane; ++u) {
+            const int p0 = base + u * 256 + lane * 4;
+            if (base + u * 256 < g.e)
+                f(v[u], p0);
+        }
+    }
+}
+
+__device__ __forceinline__ int wave_exclusive_sum(int v, int &total)
+{
+    const int lane = threadIdx.x % kWave;
+    int x = v;
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) {
+        const int y = __shfl_up(x, o, kWave);
+        if (lane >= o)
+            x += y;
+    }
+    total = __shfl(x, kWave - 1, kWave);
+    return x - v;
+}
+
+// Exclusive prefix count of `flag` over the block in thread order (fallback path).
 __device__ __forceinline__ int block_prefix(bool flag, int *wtot, int &total)
 {
-    const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+    const int wave = uniform(threadIdx.x / kWave), lane = threadIdx.x % kWave;
     const uint64_t m = ballot(flag);
     if (lane == 0)
         wtot[wave] = __popcll(m);
@@ -210,9 +329,27 @@ __device__ __forceinline__ void block_clear(uint32_t *h, int n)
         h[i] = 0u;
 }
 
-// Cut for the top-`sel` of the valid positions (count of them = count);
-// sm.h1 holds the level-1 histogram (kept), sm.hs is scratch.
-__device__ Cut block_cut(const SelRow &s, BlockScratch &sm, int count, int sel)
+// Largest bin with suffix count >= target, found by wave 0 and broadcast.
+template <int NB>
+__device__ __forceinline__ void block_find_bin(const uint32_t *h, int target, SelScratch &sm, int &x, int &above)
+{
+    if (threadIdx.x < kWave) {
+        int bx, ab;
+        find_bin<NB>(h, target, bx, ab);
+        if (threadIdx.x == 0) {
+            sm.bc[0] = bx;
+            sm.bc[1] = ab;
+        }
+    }
+    __syncthreads();
+    x = sm.bc[0];
+    above = sm.bc[1];
+    __syncthreads();
+}
+
+// Fallback cut over the whole row (used when the boundary bin does not fit
+// in LDS): levels 2 and 3 by passes over the row; ties by index order.
+__device__ Cut block_cut(const SelRow &s, SelScratch &sm, int count, int sel)
 {
     Cut c;
     c.keq = 0u;
@@ -221,25 +358,23 @@ __device__ Cut block_cut(const SelRow &s, BlockScratch &sm, int count, int sel)
         c.kgt = -1;
         return c;
     }
-    if (threadIdx.x < kWave) {
-        int x, above;
-        find_bin<kBins1>(sm.h1, sel, x, above);
-        if (threadIdx.x == 0) {
-            sm.bc[0] = x;
-            sm.bc[1] = sel - above;
-        }
-    }
+    block_clear(sm.h1, kBins1);
     __syncthreads();
-    const int b1 = sm.bc[0], r1 = sm.bc[1];
+    for (int pos = threadIdx.x; pos < s.npos; pos += blockDim.x)
+        if (sel_valid(s, pos))
+            atomicAdd(&sm.h1[bin1(score_key(s.sc[pos]))], 1u);
+    __syncthreads();
+    int b1, above;
+    block_find_bin<kBins1>(sm.h1, sel, sm, b1, above);
+    const int r1 = sel - above;
     const int hb1 = (int)sm.h1[b1];
-    __syncthreads();
     if (r1 == hb1) {
         c.kgt = (int64_t)b1 * (1ll << 21) - 1;
         return c;
     }
     block_clear(sm.hs, kBins2);
     __syncthreads();
-    for (int64_t pos = threadIdx.x; pos < s.npos; pos += blockDim.x) {
+    for (int pos = threadIdx.x; pos < s.npos; pos += blockDim.x) {
         if (!sel_valid(s, pos))
             continue;
         const uint32_t key = score_key(s.sc[pos]);
@@ -247,16 +382,9 @@ __device__ Cut block_cut(const SelRow &s, BlockScratch &sm, int count, int sel)
             atomicAdd(&sm.hs[(key >> 10) & (kBins2 - 1)], 1u);
     }
     __syncthreads();
-    if (threadIdx.x < kWave) {
-        int x, above;
-        find_bin<kBins2>(sm.hs, r1, x, above);
-        if (threadIdx.x == 0) {
-            sm.bc[2] = x;
-            sm.bc[3] = r1 - above;
-        }
-    }
-    __syncthreads();
-    const int b2 = sm.bc[2], r2 = sm.bc[3];
+    int b2, a2;
+    block_find_bin<kBins2>(sm.hs, r1, sm, b2, a2);
+    const int r2 = r1 - a2;
     const int hb2 = (int)sm.hs[b2];
     const uint32_t pre = ((uint32_t)b1 << 11) | (uint32_t)b2;
     __syncthreads();
@@ -266,7 +394,7 @@ __device__ Cut block_cut(const SelRow &s, BlockScratch &sm, int count, int sel)
     }
     block_clear(sm.hs, kBins3);
     __syncthreads();
-    for (int64_t pos = threadIdx.x; pos < s.npos; pos += blockDim.x) {
+    for (int pos = threadIdx.x; pos < s.npos; pos += blockDim.x) {
         if (!sel_valid(s, pos))
             continue;
         const uint32_t key = score_key(s.sc[pos]);
@@ -274,29 +402,21 @@ __device__ Cut block_cut(const SelRow &s, BlockScratch &sm, int count, int sel)
             atomicAdd(&sm.hs[key & (kBins3 - 1)], 1u);
     }
     __syncthreads();
-    if (threadIdx.x < kWave) {
-        int x, above;
-        find_bin<kBins3>(sm.hs, r2, x, above);
-        if (threadIdx.x == 0) {
-            sm.bc[0] = x;
-            sm.bc[1] = r2 - above;
-        }
-    }
-    __syncthreads();
-    const uint32_t kstar = (pre << 10) | (uint32_t)sm.bc[0];
+    int b3, a3;
+    block_find_bin<kBins3>(sm.hs, r2, sm, b3, a3);
+    const uint32_t kstar = (pre << 10) | (uint32_t)b3;
     c.kgt = (int64_t)kstar;
     c.keq = kstar;
-    c.req = sm.bc[1];
-    __syncthreads();
+    c.req = r2 - a3;
     return c;
 }
 
-__device__ void block_emit(const SelRow &s, BlockScratch &sm, const Cut &c, int sel,
-                           int32_t *oidx, float *osc, int fan, int64_t fstride)
+__device__ void block_emit_fallback(const SelRow &s, SelScratch &sm, const Cut &c, int sel, int32_t *oidx,
+                                    float *osc, int fan, int64_t fstride)
 {
     int emitted = 0, eqseen = 0;
-    for (int64_t base = 0; base < s.npos; base += blockDim.x) {
-        const int64_t pos = base + threadIdx.x;
+    for (int base = 0; base < s.npos; base += blockDim.x) {
+        const int pos = base + threadIdx.x;
         const bool v = sel_valid(s, pos);
         float score = 0.f;
         uint32_t key = 0u;
@@ -306,12 +426,12 @@ __device__ void block_emit(const SelRow &s, BlockScratch &sm, const Cut &c, int 
         }
         const bool eq = v && c.req > 0 && key == c.keq;
         int eqtot;
-        const int er = eqseen + block_prefix(eq, sm.wtot, eqtot);
+        const int er = eqseen + block_prefix(eq, sm.wgt, eqtot);
         const bool in = v && ((int64_t)key > c.kgt || (eq && er < c.req));
         int intot;
-        const int opos = emitted + block_prefix(in, sm.wtot, intot);
+        const int opos = emitted + block_prefix(in, sm.wgt, intot);
         if (in && opos < sel) {
-            const int32_t idx = s.list ? s.list[pos] : (int32_t)pos;
+            const int32_t idx = s.list ? s.list[pos] : pos;
             for (int f = 0; f < fan; ++f) {
                 oidx[f * fstride + opos] = idx;
                 if (osc)
@@ -330,9 +450,217 @@ __device__ void block_emit(const SelRow &s, BlockScratch &sm, const Cut &c, int 
     }
 }
 
+// Top-`sel` of the row (level-1 histogram already in sm.h1, `count` valid
+// positions): collect the boundary bin into LDS, resolve it there, then emit.
+// h1 must be rebuilt by the caller before another call (the fallback reuses it).
+__device__ void select_row(const SelRow &s, SelScratch &sm, int count, int sel, int32_t *oidx, float *osc,
+                           int fan, int64_t fstride)
+{
+    const int wave = uniform(threadIdx.x / kWave), lane = threadIdx.x % kWave;
+    const Segment seg = wave_segment(s.npos, wave);
+    // cut bin and how many of its entries are taken
+    int b1 = 0, above = 0;
+    if (count > sel)
+        block_find_bin<kSelBins1>(sm.h1, sel, sm, b1, above);
+    const bool all = count <= sel;
+    const int r1 = all ? 0 : sel - above;
+    const int hb1 = all ? 0 : (int)sm.h1[b1];
+    __syncthreads();
+    if (!all && hb1 > kBoundaryCap) {
+        const Cut c = block_cut(s, sm, count, sel);
+        block_emit_fallback(s, sm, c, sel, oidx, osc, fan, fstride);
+        return;
+    }
+    const bool whole = all || r1 == hb1;  // every entry of the cut bin is taken
+
+    // pass 1: per-wave counts of sure entries; boundary entries into LDS
+    if (threadIdx.x == 0)
+        sm.nb = 0;
+    __syncthreads();
+    int sure = 0;
+    segment_pass(s, seg, [&](const float (&v)[4], int p0) {
+#pragma unroll
+        for (int x = 0; x < 4; ++x) {
+            const int pos = p0 + x;
+            bool bnd = false;
+            uint32_t key = 0u;
+            if (pos < seg.e && sel_valid(s, pos)) {
+                key = score_key(v[x]);
+                const int bn = (int)(key >> 18);
+                if (all || bn > b1 || (whole && bn == b1))
+                    ++sure;
+                else
+                    bnd = bn == b1;
+            }
+            const uint64_t m = ballot(bnd);
+            if (m) {
+                int base = 0;
+                if (lane == 0)
+                    base = atomicAdd(&sm.nb, __popcll(m));
+                base = __shfl(base, 0, kWave);
+                if (bnd) {
+                    const int slot = base + prefix_count(m);
+                    sm.bkey[slot] = key;
+                    sm.bpos[slot] = pos;
+                }
+            }
+        }
+    });
+    sure = wave_sum(sure);
+    if (lane == 0) {
+        sm.wgt[wave] = sure;
+        sm.wbd[wave] = 0;
+    }
+    __syncthreads();
+
+    // resolve the boundary: the r1 best of its nb entries by (key desc, pos asc)
+    uint32_t kcut = 0xFFFFFFFFu;  // boundary entries with key > kcut are in
+    uint32_t keq = 0u;            // ... and those with key == keq and pos <= pcut
+    int pcut = -1;
+    if (!whole) {
+        const int nb = sm.nb;
+        block_clear(sm.hs, kSelBins2);
+        __syncthreads();
+        for (int i = threadIdx.x; i < nb; i += blockDim.x)
+            atomicAdd(&sm.hs[(sm.bkey[i] >> 9) & (kSelBins2 - 1)], 1u);
+        __syncthreads();
+        int b2, a2;
+        block_find_bin<kSelBins2>(sm.hs, r1, sm, b2, a2);
+        const int r2 = r1 - a2;
+        const uint32_t pre = ((uint32_t)b1 << 9) | (uint32_t)b2;
+        block_clear(sm.hs, kSelBins2);
+        __syncthreads();
+        for (int i = threadIdx.x; i < nb; i += blockDim.x)
+            if ((sm.bkey[i] >> 9) == pre)
+                atomicAdd(&sm.hs[sm.bkey[i] & (kSelBins2 - 1)], 1u);
+        __syncthreads();
+        int b3, a3;
+        block_find_bin<kSelBins2>(sm.hs, r2, sm, b3, a3);
+        const int r3 = r2 - a3;
+        keq = (pre << 9) | (uint32_t)b3;
+        kcut = keq;
+        const int m3 = (int)sm.hs[b3];
+        __syncthreads();
+        if (r3 >= m3) {
+            pcut = 0x7FFFFFFF;
+        } else {
+            // the r3 lowest positions among the m3 entries equal to keq: the
+            // entry with exactly r3 - 1 lower equal positions is the last one in
+            if (threadIdx.x == 0)
+                sm.bc[4] = -1;
+            __syncthreads();
+            for (int i = threadIdx.x; i < nb; i += blockDim.x) {
+                if (sm.bkey[i] != keq)
+                    continue;
+                int lower = 0;
+                for (int j2 = 0; j2 < nb; ++j2)
+                    lower += (sm.bkey[j2] == keq && sm.bpos[j2] < sm.bpos[i]) ? 1 : 0;
+                if (lower == r3 - 1)
+                    sm.bc[4] = sm.bpos[i];
+            }
+            __syncthreads();
+            pcut = sm.bc[4];
+        }
+        // selected boundary entries per wave segment (segment = pos / per)
+        const int per = (((s.npos + kSelWaves - 1) / kSelWaves) + 255) / 256 * 256;
+        for (int i = threadIdx.x; i < nb; i += blockDim.x) {
+            const uint32_t key = sm.bkey[i];
+            if (key > kcut || (key == keq && sm.bpos[i] <= pcut))
+                atomicAdd(&sm.wbd[sm.bpos[i] / per], 1);
+        }
+        __syncthreads();
+    }
+    if (threadIdx.x == 0) {
+        int o = 0;
+        for (int w = 0; w < kSelWaves; ++w) {
+            sm.woff[w] = o;
+            o += sm.wgt[w] + sm.wbd[w];
+        }
+        sm.bc[5] = o;
+    }
+    __syncthreads();
+    const int emitted_total = sm.bc[5];
+
+    // pass 2: ordered emission of this wave's segment
+    int run = sm.woff[wave];
+    segment_pass(s, seg, [&](const float (&v)[4], int p0) {
+        bool in[4];
+        int n = 0;
+#pragma unroll
+        for (int x = 0; x < 4; ++x) {
+            const int pos = p0 + x;
+            in[x] = false;
+            if (pos < seg.e && sel_valid(s, pos)) {
+                const uint32_t key = score_key(v[x]);
+                const int bn = (int)(key >> 18);
+                if (all || bn > b1 || (whole && bn == b1))
+                    in[x] = true;
+                else if (bn == b1)
+                    in[x] = key > kcut || (key == keq && pos <= pcut);
+            }
+            n += in[x] ? 1 : 0;
+        }
+        int tot;
+        int o = run + wave_exclusive_sum(n, tot);
+#pragma unroll
+        for (int x = 0; x < 4; ++x) {
+            if (in[x]) {
+                if (o < sel) {
+                    const int pos = p0 + x;
+                    const int32_t idx = s.list ? s.list[pos] : pos;
+                    for (int f = 0; f < fan; ++f) {
+                        oidx[f * fstride + o] = idx;
+                        if (osc)
+                            osc[f * fstride + o] = v[x];
+                    }
+                }
+                ++o;
+            }
+        }
+        run += tot;
+    });
+    for (int x = emitted_total + threadIdx.x; x < sel; x += blockDim.x) {
+        for (int f = 0; f < fan; ++f) {
+            oidx[f * fstride + x] = -1;
+            if (osc)
+                osc[f * fstride + x] = -__builtin_inff();
+        }
+    }
+    __syncthreads();
+}
+
+// pass 0: level-1 histogram of the valid positions; returns their count
+__device__ int row_histogram(const SelRow &s, SelScratch &sm)
+{
+    const int wave = uniform(threadIdx.x / kWave);  // wave-uniform (SGPR)
+    block_clear(sm.h1, kSelBins1);
+    __syncthreads();
+    const Segment seg = wave_segment(s.npos, wave);
+    int cnt = 0;
+    segment_pass(s, seg, [&](const float (&v)[4], int p0) {
+#pragma unroll
+        for (int x = 0; x < 4; ++x) {
+            const int pos = p0 + x;
+            if (pos < seg.e && sel_valid(s, pos)) {
+                atomicAdd(&sm.h1[score_key(v[x]) >> 18], 1u);
+                ++cnt;
+            }
+        }
+    });
+    cnt = wave_sum(cnt);
+    if (threadIdx.x % kWave == 0)
+        sm.wgt[wave] = cnt;
+    __syncthreads();
+    int count = 0;
+    for (int w = 0; w < kSelWaves; ++w)
+        count += sm.wgt[w];
+    __syncthreads();
+    return count;
+}
+
 __global__ __launch_bounds__(kSelectThreads) void split_select_kernel(SplitSelectParams p)
 {
-    __shared__ BlockScratch sm;
+    __shared__ SelScratch sm;
     const int bi = blockIdx.y;
     const int64_t r = blockIdx.x;
     const int64_t off = p.L - p.q_len;
@@ -346,7 +674,7 @@ __global__ __launch_bounds__(kSelectThreads) void split_select_kernel(SplitSelec
         const int64_t r0 = r * p.g;
         const int64_t r1 = (r0 + p.g < p.q_len) ? r0 + p.g : p.q_len;
         s.list = nullptr;
-        s.lim = off + r1 - 1;
+        s.lim = (int)(off + r1 - 1);
         s.npos = s.lim + 1;
         const int64_t mrow = (int64_t)bi * p.q_len + r0;
         const int64_t grow = (int64_t)bi * p.G + r;
@@ -365,7 +693,7 @@ __global__ __launch_bounds__(kSelectThreads) void split_select_kernel(SplitSelec
         }
     } else {
         const int64_t row = (int64_t)bi * p.q_len + r;
-        s.lim = off + r;
+        s.lim = (int)(off + r);
         if (p.mode == kDense) {
             s.list = nullptr;
             s.npos = s.lim + 1;
@@ -374,35 +702,17 @@ __global__ __launch_bounds__(kSelectThreads) void split_select_kernel(SplitSelec
             const int64_t r1 = ((m + 1) * p.g < p.q_len) ? (m + 1) * p.g : p.q_len;
             const int64_t t_last = off + r1 - 1;
             s.list = p.cand + ((int64_t)bi * p.G + m) * p.c;
-            s.npos = (p.c < t_last + 1) ? p.c : t_last + 1;
+            s.npos = (int)((p.c < t_last + 1) ? p.c : t_last + 1);
         }
         o1 = p.o1_idx + row * p.sel;
         s1 = p.o1_score ? p.o1_score + row * p.sel : nullptr;
     }
 
-    block_clear(sm.h1, kBins1);
-    __syncthreads();
-    int cnt = 0;
-    for (int64_t pos = threadIdx.x; pos < s.npos; pos += blockDim.x) {
-        if (!sel_valid(s, pos))
-            continue;
-        atomicAdd(&sm.h1[bin1(score_key(s.sc[pos]))], 1u);
-        ++cnt;
-    }
-    cnt = wave_sum(cnt);
-    if (threadIdx.x % kWave == 0)
-        sm.wtot[threadIdx.x / kWave] = cnt;
-    __syncthreads();
-    int count = 0;
-    for (int w = 0; w < kSelWaves; ++w)
-        count += sm.wtot[w];
-    __syncthreads();
-
-    const Cut c1 = block_cut(s, sm, count, p.sel);
-    block_emit(s, sm, c1, p.sel, o1, s1, fan1, p.sel);
+    const int count = row_histogram(s, sm);
+    select_row(s, sm, count, p.sel, o1, s1, fan1, p.sel);
     if (p.sel2 > 0) {
-        const Cut c2 = block_cut(s, sm, count, p.sel2);
-        block_emit(s, sm, c2, p.sel2, o2, s2, fan2, p.sel2);
+        row_histogram(s, sm);
+        select_row(s, sm, count, p.sel2, o2, s2, fan2, p.sel2);
     }
 }
 
@@ -410,12 +720,17 @@ __global__ __launch_bounds__(kSelectThreads) void split_select_kernel(SplitSelec
 template <int H, int D>
 static hipError_t launch_split_score_t(const SplitScoreParams &prm, dim3 grid, hipStream_t stream)
 {
-    hipLaunchKernelGGL((split_score_kernel<H, D>), grid, dim3(kSplitWaves * kWave), 0, stream, prm);
+    if (prm.mode == kRefine)
+        hipLaunchKernelGGL((split_score_kernel<H, D, true>), grid, dim3(kSplitWaves * kWave), 0, stream, prm);
+    else
+        hipLaunchKernelGGL((split_score_kernel<H, D, false>), grid, dim3(kSplitWaves * kWave), 0, stream, prm);
     return hipGetLastError();
 }
 
 hipError_t launch_split_score(int H, int D, const SplitScoreParams &prm, dim3 grid, hipStream_t stream)
 {
+    if (prm.chunk % (32 * kSplitWaves) != 0 || prm.chunk / kSplitWaves > kSplitSpanMax)
+        return hipErrorInvalidValue;
     if (H == 64 && D == 128)
         return launch_split_score_t<64, 128>(prm, grid, stream);
     if (H == 4 && D == 32)
