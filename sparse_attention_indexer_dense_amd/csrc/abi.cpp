@@ -57,6 +57,9 @@ size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
+// Score rows of the split-key path are padded to a multiple of 64 floats.
+int64_t score_row(int64_t n) { return ceil_div(n, 64) * 64; }
+
 bool supported(int H, int D) { return (H == 64 && D == 128) || (H == 4 && D == 32); }
 
 // Entries per row buffer. A row admits about sel * (1 + ln(n / sel)) keys
@@ -140,7 +143,7 @@ int make_plan(int mode, int B, int64_t L, int64_t q_len, int H, int D, int64_t g
         pl.cap_scan = scan_cap(k, L);
         if (pl.split_scan) {
             pl.off_scores = off;
-            off += align_up((size_t)B * q_len * L * sizeof(float));
+            off += align_up((size_t)B * q_len * score_row(L) * sizeof(float));
         } else {
             pl.off_slots = off;
             off += align_up((size_t)scan_slots(H, D, pl.nw_scan) * pl.nw_scan * pl.cap_scan * sizeof(Entry));
@@ -174,7 +177,7 @@ int make_plan(int mode, int B, int64_t L, int64_t q_len, int H, int D, int64_t g
     }
     // scan stage
     size_t scan_bytes = pl.split_scan
-        ? (size_t)B * pl.G * L * sizeof(float)
+        ? (size_t)B * pl.G * score_row(L) * sizeof(float)
         : (size_t)scan_slots(H, D, pl.nw_scan) * pl.nw_scan * pl.cap_scan * sizeof(Entry);
     size_t refine_bytes = 0;
     if (mode == DSAIDX_REFINE) {
@@ -182,7 +185,7 @@ int make_plan(int mode, int B, int64_t L, int64_t q_len, int H, int D, int64_t g
         pl.nw_refine = g <= 4 ? 4 : 8;
         pl.cap_refine = (int)ceil_div(c + 128, 64) * 64;
         refine_bytes = pl.split_refine
-            ? (size_t)B * q_len * c * sizeof(float)
+            ? (size_t)B * q_len * score_row(c) * sizeof(float)
             : (size_t)scan_slots(H, D, pl.nw_refine) * pl.nw_refine * pl.cap_refine * sizeof(Entry);
     }
     // the scan's buffers/scores and Refine's are used one after the other
@@ -347,7 +350,7 @@ int run_pivot(int mode, const void *Qv, const float *W, const void *Kv, int B, i
         }
     }
     if (pl.split_scan) {
-        s = run_split(kProxy, Qp, Wp, K, nullptr, B, L, q_len, g, c, G, G, L, H, D, pl.sel, pl.sel2, o1, s1,
+        s = run_split(kProxy, Qp, Wp, K, nullptr, B, L, q_len, g, c, G, G, score_row(L), H, D, pl.sel, pl.sel2, o1, s1,
                       o1_members, o2, s2, reinterpret_cast<float *>(wsb + pl.off_scores), stream);
         if (s != DSAIDX_OK)
             return s;
@@ -373,7 +376,7 @@ int run_pivot(int mode, const void *Qv, const float *W, const void *Kv, int B, i
 
     // 3. Refine on the candidates
     if (pl.split_refine) {
-        return run_split(kRefine, Q, W, K, cand, B, L, q_len, g, c, G, q_len, c, H, D, (int)k, 0, out_idx,
+        return run_split(kRefine, Q, W, K, cand, B, L, q_len, g, c, G, q_len, score_row(c), H, D, (int)k, 0, out_idx,
                          out_score, 0, nullptr, nullptr, reinterpret_cast<float *>(wsb + pl.off_scores), stream);
     }
     ScanParams p = scan_base(Q, W, K, B, L, q_len, g, c, G);
@@ -433,7 +436,7 @@ int indexer_dense(const void *Qv, const float *W, const void *Kv, int B, int64_t
     const uint16_t *K = static_cast<const uint16_t *>(Kv);
     unsigned char *wsb = static_cast<unsigned char *>(ws);
     if (pl.split_scan) {
-        return run_split(kDense, Q, W, K, nullptr, B, L, q_len, 1, 0, q_len, q_len, L, H_I, d_I, k, 0, out_idx,
+        return run_split(kDense, Q, W, K, nullptr, B, L, q_len, 1, 0, q_len, q_len, score_row(L), H_I, d_I, k, 0, out_idx,
                          out_score, 0, nullptr, nullptr, reinterpret_cast<float *>(wsb + pl.off_scores), stream);
     }
     ScanParams p = scan_base(Q, W, K, B, L, q_len, 1, 0, q_len);

@@ -218,9 +218,38 @@ __global__ __launch_bounds__(kSplitWaves * kWave) void split_score_kernel(SplitS
 }
 
 // ---------------------------------------------------------------- selection
+// One workgroup per score row. The valid positions of a row always form a
+// prefix [0, n): position p <= lim for keys 0..lim, and candidate lists are
+// ascending, so their causal entries come first.
+//
+// A row that fits in LDS is copied there whole. A longer row is reduced first:
+// an exact order statistic of a strided sample gives a lower bound theta that,
+// with high probability, at least `sel` scores of the row reach; the scores
+// >= theta are packed into LDS in index order (one read of the row, held in
+// registers between counting and packing). The exact top-`sel` lies among
+// them whenever there are at least `sel`; when there are fewer, or more than
+// LDS holds, the selection runs exactly on the row in global memory instead.
+// On the LDS entries, an exact radix cut (digits taken relative to the
+// smallest key, so that close scores still spread over the bins) and one
+// ordered pass write the selection, ties going to the lower index.
 constexpr int kSelWaves = kSelectThreads / kWave;
-constexpr int kBoundaryCap = 4096;  // boundary-bin entries resolved in LDS
-constexpr int kQuadsPerLane = 8;    // float4 loads in flight per lane and pass
+constexpr int kCandCap = 12288;   // scores held in LDS
+constexpr int kSampleMax = 8192;  // strided sample of a long row
+constexpr int kRegSteps = 16;     // float4 steps per lane held in registers
+constexpr int kStageSteps = 4;    // the same when staging a whole row
+constexpr int kBoundaryCap = 1024;  // boundary-bin entries ranked directly
+
+struct SelShared {
+    __attribute__((aligned(16))) float cs[kCandCap];
+    int32_t cp[kCandCap];
+    uint32_t h[kBins1];
+    uint32_t bkey[kBoundaryCap];
+    int32_t bpos[kBoundaryCap];
+    int nbnd;
+    int wt[kSelWaves];
+    uint32_t wlo[kSelWaves], whi[kSelWaves];
+    int bc[5];
+};
 
 struct SelRow {
     const float *sc;
@@ -228,114 +257,63 @@ struct SelRow {
     int npos, lim;
 };
 
-// Row selection bins: level 1 = top 14 bits of the score key (sign, exponent,
-// five mantissa bits), then 9 + 9 bits inside the boundary bin.
-constexpr int kSelBins1 = 16384;
-constexpr int kSelBins2 = 512;
-
-struct SelScratch {
-    uint32_t h1[kSelBins1];
-    uint32_t hs[kBins2];
-    uint32_t bkey[kBoundaryCap];
-    int32_t bpos[kBoundaryCap];
-    int wgt[kSelWaves];  // per wave: sure entries (bin above the cut bin)
-    int wbd[kSelWaves];  // per wave: selected boundary entries
-    int woff[kSelWaves];
-    int nb;
-    int bc[8];
+struct SelOut {
+    int sel;
+    int32_t *idx;
+    float *score;
+    int fan;  // rows the selection is written to, sel entries apart
 };
 
-__device__ __forceinline__ bool sel_valid(const SelRow &s, int pos)
+__device__ __forceinline__ uint32_t wave_min(uint32_t v)
 {
-    return pos < s.npos && (s.list == nullptr || s.list[pos] <= s.lim);
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1)
+        v = min(v, (uint32_t)__shfl_xor((int)v, o, kWave));
+    return v;
 }
 
-// The row's positions split into kSelWaves contiguous segments; a wave walks
-// its segment in steps of 256 positions (one float4 per lane), kQuadsPerLane
-// steps per batch with all their loads issued first.
-struct Segment {
-    int b, e;
+__device__ __forceinline__ uint32_t wave_max(uint32_t v)
+{
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1)
+        v = max(v, (uint32_t)__shfl_xor((int)v, o, kWave));
+    return v;
+}
+
+// Per-wave totals gathered over the block: the exclusive prefix of t in wave
+// order, its total, and the key range. t, lo and hi are wave-uniform.
+struct WaveTotals {
+    int off, total;
+    uint32_t lo, hi;
 };
 
-__device__ __forceinline__ Segment wave_segment(int npos, int wave)
+__device__ __forceinline__ WaveTotals wave_totals(int t, uint32_t lo, uint32_t hi, SelShared &sm)
 {
-    const int per = (((npos + kSelWaves - 1) / kSelWaves) + 255) / 256 * 256;
-    Segment g;
-    g.b = wave * per;
-    g.e = (g.b + per < npos) ? g.b + per : npos;
-    if (g.b > npos)
-        g.b = npos;
-    return g;
-}
-
-template <typename F>
-__device__ __forceinline__ void segment_pass(const SelRow &s, Segment g, F &&f)
-{
-    const int lane = threadIdx.x % kWave;
-    for (int base = g.b; base < g.e; base += kQuadsPerLane * 256) {
-        float v[kQuadsPerLane][4];
-#pragma unroll
-        for (int u = 0; u < kQuadsPerLane; ++u) {
-            const int p0 = base + u * 256 + lane * 4;
-#pragma unroll
-            for (int x = 0; x < 4; ++x)
-                v[u][x] = (p0 + x < g.e) ? s.sc[p0 + x] : 0.f;
-        }
-#pragma unroll
-        for (int u = 0; u < kQuadsPerLane; ++u) {
-            const int p0 = base + u * 256 + lane * 4;
-            if (base + u * 256 < g.e)
-                f(v[u], p0);
-        }
+    const int wave = uniform(threadIdx.x / kWave);
+    if (lane_id() == 0) {
+        sm.wt[wave] = t;
+        sm.wlo[wave] = lo;
+        sm.whi[wave] = hi;
     }
-}
-
-__device__ __forceinline__ int wave_exclusive_sum(int v, int &total)
-{
-    const int lane = threadIdx.x % kWave;
-    int x = v;
-#pragma unroll
-    for (int o = 1; o < kWave; o <<= 1) {
-        const int y = __shfl_up(x, o, kWave);
-        if (lane >= o)
-            x += y;
-    }
-    total = __shfl(x, kWave - 1, kWave);
-    return x - v;
-}
-
-// Exclusive prefix count of `flag` over the block in thread order (fallback path).
-__device__ __forceinline__ int block_prefix(bool flag, int *wtot, int &total)
-{
-    const int wave = uniform(threadIdx.x / kWave), lane = threadIdx.x % kWave;
-    const uint64_t m = ballot(flag);
-    if (lane == 0)
-        wtot[wave] = __popcll(m);
     __syncthreads();
-    int off = 0, tot = 0;
+    WaveTotals r{0, 0, 0xFFFFFFFFu, 0u};
     for (int w = 0; w < kSelWaves; ++w) {
-        const int v = wtot[w];
-        off += (w < wave) ? v : 0;
-        tot += v;
+        const int x = sm.wt[w];
+        r.off += (w < wave) ? x : 0;
+        r.total += x;
+        r.lo = min(r.lo, sm.wlo[w]);
+        r.hi = max(r.hi, sm.whi[w]);
     }
     __syncthreads();
-    total = tot;
-    return off + prefix_count(m);
+    return r;
 }
 
-__device__ __forceinline__ void block_clear(uint32_t *h, int n)
-{
-    for (int i = threadIdx.x; i < n; i += blockDim.x)
-        h[i] = 0u;
-}
-
-// Largest bin with suffix count >= target, found by wave 0 and broadcast.
-template <int NB>
-__device__ __forceinline__ void block_find_bin(const uint32_t *h, int target, SelScratch &sm, int &x, int &above)
+// Largest bin with suffix count >= target (wave 0 finds it, all threads get it).
+__device__ __forceinline__ void block_find_bin(const uint32_t *h, int target, SelShared &sm, int &x, int &above)
 {
     if (threadIdx.x < kWave) {
         int bx, ab;
-        find_bin<NB>(h, target, bx, ab);
+        find_bin<kBins1>(h, target, bx, ab);
         if (threadIdx.x == 0) {
             sm.bc[0] = bx;
             sm.bc[1] = ab;
@@ -344,323 +322,427 @@ __device__ __forceinline__ void block_find_bin(const uint32_t *h, int target, Se
     __syncthreads();
     x = sm.bc[0];
     above = sm.bc[1];
-    __syncthreads();
 }
 
-// Fallback cut over the whole row (used when the boundary bin does not fit
-// in LDS): levels 2 and 3 by passes over the row; ties by index order.
-__device__ Cut block_cut(const SelRow &s, SelScratch &sm, int count, int sel)
+// Exact cut of the best `sel` of m keys key_at(0..m-1), each in [base, hi],
+// where entry order is index order. Level 1 counts 2048 bins of the top bits
+// of u = key - base (so that close keys still spread over the bins). When
+// the bin holding the sel-th key has at most kBoundaryCap entries, they are
+// gathered and ranked exactly (key descending, then entry order); otherwise
+// two more radix levels narrow it down to one key, whose equal entries are
+// then taken in index order when the selection is written.
+template <typename KeyAt>
+__device__ __forceinline__ Cut block_radix_cut(int m, int sel, uint32_t base, uint32_t hi, KeyAt key_at, SelShared &sm)
 {
     Cut c;
     c.keq = 0u;
     c.req = 0;
-    if (count <= sel) {
-        c.kgt = -1;
+    if (m <= sel) {
+        c.kgt = (int64_t)base - 1;
         return c;
     }
-    block_clear(sm.h1, kBins1);
-    __syncthreads();
-    for (int pos = threadIdx.x; pos < s.npos; pos += blockDim.x)
-        if (sel_valid(s, pos))
-            atomicAdd(&sm.h1[bin1(score_key(s.sc[pos]))], 1u);
-    __syncthreads();
-    int b1, above;
-    block_find_bin<kBins1>(sm.h1, sel, sm, b1, above);
-    const int r1 = sel - above;
-    const int hb1 = (int)sm.h1[b1];
-    if (r1 == hb1) {
-        c.kgt = (int64_t)b1 * (1ll << 21) - 1;
-        return c;
-    }
-    block_clear(sm.hs, kBins2);
-    __syncthreads();
-    for (int pos = threadIdx.x; pos < s.npos; pos += blockDim.x) {
-        if (!sel_valid(s, pos))
-            continue;
-        const uint32_t key = score_key(s.sc[pos]);
-        if ((int)(key >> 21) == b1)
-            atomicAdd(&sm.hs[(key >> 10) & (kBins2 - 1)], 1u);
-    }
-    __syncthreads();
-    int b2, a2;
-    block_find_bin<kBins2>(sm.hs, r1, sm, b2, a2);
-    const int r2 = r1 - a2;
-    const int hb2 = (int)sm.hs[b2];
-    const uint32_t pre = ((uint32_t)b1 << 11) | (uint32_t)b2;
-    __syncthreads();
-    if (r2 == hb2) {
-        c.kgt = (int64_t)pre * 1024 - 1;
-        return c;
-    }
-    block_clear(sm.hs, kBins3);
-    __syncthreads();
-    for (int pos = threadIdx.x; pos < s.npos; pos += blockDim.x) {
-        if (!sel_valid(s, pos))
-            continue;
-        const uint32_t key = score_key(s.sc[pos]);
-        if ((key >> 10) == pre)
-            atomicAdd(&sm.hs[key & (kBins3 - 1)], 1u);
-    }
-    __syncthreads();
-    int b3, a3;
-    block_find_bin<kBins3>(sm.hs, r2, sm, b3, a3);
-    const uint32_t kstar = (pre << 10) | (uint32_t)b3;
-    c.kgt = (int64_t)kstar;
-    c.keq = kstar;
-    c.req = r2 - a3;
-    return c;
-}
+    const int lane = lane_id();
+    const uint32_t span = hi - base;
+    const int nb = span ? 32 - __builtin_clz(span) : 0;
+    const int s1 = nb > 11 ? nb - 11 : 0;
+    const int s2 = s1 > 11 ? s1 - 11 : 0;
 
-__device__ void block_emit_fallback(const SelRow &s, SelScratch &sm, const Cut &c, int sel, int32_t *oidx,
-                                    float *osc, int fan, int64_t fstride)
-{
-    int emitted = 0, eqseen = 0;
-    for (int base = 0; base < s.npos; base += blockDim.x) {
-        const int pos = base + threadIdx.x;
-        const bool v = sel_valid(s, pos);
-        float score = 0.f;
-        uint32_t key = 0u;
-        if (v) {
-            score = s.sc[pos];
-            key = score_key(score);
-        }
-        const bool eq = v && c.req > 0 && key == c.keq;
-        int eqtot;
-        const int er = eqseen + block_prefix(eq, sm.wgt, eqtot);
-        const bool in = v && ((int64_t)key > c.kgt || (eq && er < c.req));
-        int intot;
-        const int opos = emitted + block_prefix(in, sm.wgt, intot);
-        if (in && opos < sel) {
-            const int32_t idx = s.list ? s.list[pos] : pos;
-            for (int f = 0; f < fan; ++f) {
-                oidx[f * fstride + opos] = idx;
-                if (osc)
-                    osc[f * fstride + opos] = score;
-            }
-        }
-        emitted += intot;
-        eqseen += eqtot;
-    }
-    for (int x = emitted + threadIdx.x; x < sel; x += blockDim.x) {
-        for (int f = 0; f < fan; ++f) {
-            oidx[f * fstride + x] = -1;
-            if (osc)
-                osc[f * fstride + x] = -__builtin_inff();
-        }
-    }
-}
-
-// Top-`sel` of the row (level-1 histogram already in sm.h1, `count` valid
-// positions): collect the boundary bin into LDS, resolve it there, then emit.
-// h1 must be rebuilt by the caller before another call (the fallback reuses it).
-__device__ void select_row(const SelRow &s, SelScratch &sm, int count, int sel, int32_t *oidx, float *osc,
-                           int fan, int64_t fstride)
-{
-    const int wave = uniform(threadIdx.x / kWave), lane = threadIdx.x % kWave;
-    const Segment seg = wave_segment(s.npos, wave);
-    // cut bin and how many of its entries are taken
-    int b1 = 0, above = 0;
-    if (count > sel)
-        block_find_bin<kSelBins1>(sm.h1, sel, sm, b1, above);
-    const bool all = count <= sel;
-    const int r1 = all ? 0 : sel - above;
-    const int hb1 = all ? 0 : (int)sm.h1[b1];
-    __syncthreads();
-    if (!all && hb1 > kBoundaryCap) {
-        const Cut c = block_cut(s, sm, count, sel);
-        block_emit_fallback(s, sm, c, sel, oidx, osc, fan, fstride);
-        return;
-    }
-    const bool whole = all || r1 == hb1;  // every entry of the cut bin is taken
-
-    // pass 1: per-wave counts of sure entries; boundary entries into LDS
+    // level 1
+    for (int i = threadIdx.x; i < kBins1; i += kSelectThreads)
+        sm.h[i] = 0u;
     if (threadIdx.x == 0)
-        sm.nb = 0;
+        sm.nbnd = 0;
     __syncthreads();
-    int sure = 0;
-    segment_pass(s, seg, [&](const float (&v)[4], int p0) {
-#pragma unroll
-        for (int x = 0; x < 4; ++x) {
-            const int pos = p0 + x;
-            bool bnd = false;
-            uint32_t key = 0u;
-            if (pos < seg.e && sel_valid(s, pos)) {
-                key = score_key(v[x]);
-                const int bn = (int)(key >> 18);
-                if (all || bn > b1 || (whole && bn == b1))
-                    ++sure;
-                else
-                    bnd = bn == b1;
-            }
-            const uint64_t m = ballot(bnd);
-            if (m) {
-                int base = 0;
+    for (int i = threadIdx.x; i < m; i += kSelectThreads)
+        atomicAdd(&sm.h[(key_at(i) - base) >> s1], 1u);
+    __syncthreads();
+    int b1, a1;
+    block_find_bin(sm.h, sel, sm, b1, a1);
+    const int r1 = sel - a1;
+    const int cnt1 = (int)sm.h[b1];
+    if (r1 == cnt1) {  // the whole bin is in
+        c.kgt = (int64_t)base + ((int64_t)b1 << s1) - 1;
+        __syncthreads();
+        return c;
+    }
+    if (s1 == 0) {  // a bin is one key
+        c.keq = base + (uint32_t)b1;
+        c.kgt = (int64_t)c.keq;
+        c.req = r1;
+        __syncthreads();
+        return c;
+    }
+    if (cnt1 <= kBoundaryCap) {
+        // gather the boundary bin (wave-aggregated slots), then rank it
+        const int S = (m + kSelectThreads - 1) / kSelectThreads * kWave;  // per-wave span of entries
+        const int wave = uniform(threadIdx.x / kWave);
+        const int e0 = wave * S;
+        const int e1 = (e0 + S < m) ? e0 + S : m;
+        for (int i0 = e0; i0 < e1; i0 += kWave) {
+            const int i = i0 + lane;
+            const uint32_t k = i < e1 ? key_at(i) : 0u;
+            const bool hit = i < e1 && (int)((k - base) >> s1) == b1;
+            const uint64_t bm = ballot(hit);
+            if (bm) {
+                int slot0 = 0;
                 if (lane == 0)
-                    base = atomicAdd(&sm.nb, __popcll(m));
-                base = __shfl(base, 0, kWave);
-                if (bnd) {
-                    const int slot = base + prefix_count(m);
-                    sm.bkey[slot] = key;
-                    sm.bpos[slot] = pos;
+                    slot0 = atomicAdd(&sm.nbnd, __popcll(bm));
+                slot0 = __shfl(slot0, 0, kWave);
+                if (hit) {
+                    const int sl = slot0 + prefix_count(bm);
+                    sm.bkey[sl] = k;
+                    sm.bpos[sl] = i;
                 }
             }
         }
-    });
-    sure = wave_sum(sure);
-    if (lane == 0) {
-        sm.wgt[wave] = sure;
-        sm.wbd[wave] = 0;
-    }
-    __syncthreads();
-
-    // resolve the boundary: the r1 best of its nb entries by (key desc, pos asc)
-    uint32_t kcut = 0xFFFFFFFFu;  // boundary entries with key > kcut are in
-    uint32_t keq = 0u;            // ... and those with key == keq and pos <= pcut
-    int pcut = -1;
-    if (!whole) {
-        const int nb = sm.nb;
-        block_clear(sm.hs, kSelBins2);
         __syncthreads();
-        for (int i = threadIdx.x; i < nb; i += blockDim.x)
-            atomicAdd(&sm.hs[(sm.bkey[i] >> 9) & (kSelBins2 - 1)], 1u);
+        // entry e has rank (#keys above) + (#equal keys earlier); the one of
+        // rank r1 - 1 fixes the cut
+        for (int e = threadIdx.x; e < cnt1; e += kSelectThreads) {
+            const uint32_t ke = sm.bkey[e];
+            const int pe = sm.bpos[e];
+            int above = 0, before = 0, equal = 0;
+            for (int f = 0; f < cnt1; ++f) {
+                const uint32_t kf = sm.bkey[f];
+                above += kf > ke ? 1 : 0;
+                equal += kf == ke ? 1 : 0;
+                before += (kf == ke && sm.bpos[f] < pe) ? 1 : 0;
+            }
+            if (above + before == r1 - 1) {
+                sm.bc[2] = (int)ke;
+                sm.bc[3] = before + 1;          // equal keys taken
+                sm.bc[4] = equal;
+            }
+        }
         __syncthreads();
-        int b2, a2;
-        block_find_bin<kSelBins2>(sm.hs, r1, sm, b2, a2);
-        const int r2 = r1 - a2;
-        const uint32_t pre = ((uint32_t)b1 << 9) | (uint32_t)b2;
-        block_clear(sm.hs, kSelBins2);
+        const uint32_t kstar = (uint32_t)sm.bc[2];
+        const int take = sm.bc[3], equal = sm.bc[4];
         __syncthreads();
-        for (int i = threadIdx.x; i < nb; i += blockDim.x)
-            if ((sm.bkey[i] >> 9) == pre)
-                atomicAdd(&sm.hs[sm.bkey[i] & (kSelBins2 - 1)], 1u);
-        __syncthreads();
-        int b3, a3;
-        block_find_bin<kSelBins2>(sm.hs, r2, sm, b3, a3);
-        const int r3 = r2 - a3;
-        keq = (pre << 9) | (uint32_t)b3;
-        kcut = keq;
-        const int m3 = (int)sm.hs[b3];
-        __syncthreads();
-        if (r3 >= m3) {
-            pcut = 0x7FFFFFFF;
+        if (take == equal) {
+            c.kgt = (int64_t)kstar - 1;
         } else {
-            // the r3 lowest positions among the m3 entries equal to keq: the
-            // entry with exactly r3 - 1 lower equal positions is the last one in
-            if (threadIdx.x == 0)
-                sm.bc[4] = -1;
-            __syncthreads();
-            for (int i = threadIdx.x; i < nb; i += blockDim.x) {
-                if (sm.bkey[i] != keq)
-                    continue;
-                int lower = 0;
-                for (int j2 = 0; j2 < nb; ++j2)
-                    lower += (sm.bkey[j2] == keq && sm.bpos[j2] < sm.bpos[i]) ? 1 : 0;
-                if (lower == r3 - 1)
-                    sm.bc[4] = sm.bpos[i];
-            }
-            __syncthreads();
-            pcut = sm.bc[4];
+            c.kgt = (int64_t)kstar;
+            c.keq = kstar;
+            c.req = take;
         }
-        // selected boundary entries per wave segment (segment = pos / per)
-        const int per = (((s.npos + kSelWaves - 1) / kSelWaves) + 255) / 256 * 256;
-        for (int i = threadIdx.x; i < nb; i += blockDim.x) {
-            const uint32_t key = sm.bkey[i];
-            if (key > kcut || (key == keq && sm.bpos[i] <= pcut))
-                atomicAdd(&sm.wbd[sm.bpos[i] / per], 1);
+        return c;
+    }
+    // levels 2 and 3
+    __syncthreads();
+    uint32_t pre = (uint32_t)b1;  // digits fixed so far: u >> prev == pre
+    int prev = s1;
+    int r = r1;
+    for (int lev = 1; lev < 3; ++lev) {
+        const int sh = lev == 1 ? s2 : 0;
+        const uint32_t mask = (1u << (prev - sh)) - 1u;
+        for (int i = threadIdx.x; i < kBins1; i += kSelectThreads)
+            sm.h[i] = 0u;
+        __syncthreads();
+        for (int i = threadIdx.x; i < m; i += kSelectThreads) {
+            const uint32_t u = key_at(i) - base;
+            if ((u >> prev) == pre)
+                atomicAdd(&sm.h[(u >> sh) & mask], 1u);
         }
         __syncthreads();
-    }
-    if (threadIdx.x == 0) {
-        int o = 0;
-        for (int w = 0; w < kSelWaves; ++w) {
-            sm.woff[w] = o;
-            o += sm.wgt[w] + sm.wbd[w];
+        int b, a;
+        block_find_bin(sm.h, r, sm, b, a);
+        const int rr = r - a;
+        const int cnt = (int)sm.h[b];
+        pre = (pre << (prev - sh)) | (uint32_t)b;
+        __syncthreads();
+        if (rr == cnt) {
+            c.kgt = (int64_t)base + ((int64_t)pre << sh) - 1;
+            return c;
         }
-        sm.bc[5] = o;
+        if (sh == 0) {
+            c.keq = base + pre;
+            c.kgt = (int64_t)c.keq;
+            c.req = rr;
+            return c;
+        }
+        r = rr;
+        prev = sh;
+    }
+    return c;  // not reached: the last level has shift 0
+}
+
+// Writes the entries of a cut over m entries in index order (entry i: score
+// score_at(i), row position pos_at(i)). Wave w takes the w-th contiguous
+// segment; ballots give ranks among equal keys and output slots. The
+// selection is padded to sel with -1 / -inf.
+template <typename ScoreAt, typename PosAt>
+__device__ __forceinline__ void block_emit(int m, const Cut &c, const SelOut &o, const int32_t *list, ScoreAt score_at,
+                           PosAt pos_at, SelShared &sm)
+{
+    const int wave = uniform(threadIdx.x / kWave), lane = lane_id();
+    const int S = (m + kSelWaves * kWave - 1) / (kSelWaves * kWave) * kWave;
+    const int b0 = wave * S;
+    const int b1 = (b0 + S < m) ? b0 + S : m;
+    int eq0 = 0;
+    if (c.req > 0) {
+        int ceq = 0;
+        for (int i0 = b0; i0 < b1; i0 += kWave) {
+            const int i = i0 + lane;
+            ceq += __popcll(ballot(i < b1 && score_key(score_at(i)) == c.keq));
+        }
+        eq0 = wave_totals(ceq, 0u, 0u, sm).off;
+    }
+    int cin = 0, er = eq0;
+    for (int i0 = b0; i0 < b1; i0 += kWave) {
+        const int i = i0 + lane;
+        const uint32_t k = i < b1 ? score_key(score_at(i)) : 0u;
+        const bool v = i < b1;
+        const uint64_t be = ballot(v && c.req > 0 && k == c.keq);
+        const bool eq = (be >> lane) & 1u;
+        const bool in = v && ((int64_t)k > c.kgt || (eq && er + prefix_count(be) < c.req));
+        cin += __popcll(ballot(in));
+        er += __popcll(be);
+    }
+    const WaveTotals t = wave_totals(cin, 0u, 0u, sm);
+    int slot0 = t.off;
+    er = eq0;
+    for (int i0 = b0; i0 < b1; i0 += kWave) {
+        const int i = i0 + lane;
+        const bool v = i < b1;
+        const float sc = v ? score_at(i) : 0.f;
+        const uint32_t k = score_key(sc);
+        const uint64_t be = ballot(v && c.req > 0 && k == c.keq);
+        const bool eq = (be >> lane) & 1u;
+        const bool in = v && ((int64_t)k > c.kgt || (eq && er + prefix_count(be) < c.req));
+        const uint64_t bi = ballot(in);
+        const int slot = slot0 + prefix_count(bi);
+        if (in && slot < o.sel) {
+            const int pos = pos_at(i);
+            const int32_t idx = list ? list[pos] : pos;
+            for (int f = 0; f < o.fan; ++f) {
+                o.idx[(int64_t)f * o.sel + slot] = idx;
+                if (o.score)
+                    o.score[(int64_t)f * o.sel + slot] = sc;
+            }
+        }
+        slot0 += __popcll(bi);
+        er += __popcll(be);
+    }
+    for (int x = t.total + threadIdx.x; x < o.sel; x += kSelectThreads) {
+        for (int f = 0; f < o.fan; ++f) {
+            o.idx[(int64_t)f * o.sel + x] = -1;
+            if (o.score)
+                o.score[(int64_t)f * o.sel + x] = -__builtin_inff();
+        }
     }
     __syncthreads();
-    const int emitted_total = sm.bc[5];
+}
 
-    // pass 2: ordered emission of this wave's segment
-    int run = sm.woff[wave];
-    segment_pass(s, seg, [&](const float (&v)[4], int p0) {
-        bool in[4];
-        int n = 0;
+// Wave w's contiguous segment of a row of n scores, in float4 steps of 256
+// positions, kRegSteps steps per batch (all loads of a batch issued at once).
+struct RowSeg {
+    int b0, b1, S;
+};
+
+__device__ __forceinline__ RowSeg row_segment(int n)
+{
+    const int wave = uniform(threadIdx.x / kWave);
+    RowSeg g;
+    g.S = (n + kSelWaves * 256 - 1) / (kSelWaves * 256) * 256;
+    g.b0 = wave * g.S;
+    g.b1 = (g.b0 + g.S < n) ? g.b0 + g.S : n;
+    return g;
+}
+
+template <int NQ>
+__device__ __forceinline__ void load_batch(const float *sc, int i0, int b1, float4 (&v)[NQ])
+{
+    const int lane = lane_id();
 #pragma unroll
-        for (int x = 0; x < 4; ++x) {
-            const int pos = p0 + x;
-            in[x] = false;
-            if (pos < seg.e && sel_valid(s, pos)) {
-                const uint32_t key = score_key(v[x]);
-                const int bn = (int)(key >> 18);
-                if (all || bn > b1 || (whole && bn == b1))
-                    in[x] = true;
-                else if (bn == b1)
-                    in[x] = key > kcut || (key == keq && pos <= pcut);
-            }
-            n += in[x] ? 1 : 0;
-        }
-        int tot;
-        int o = run + wave_exclusive_sum(n, tot);
+    for (int q = 0; q < NQ; ++q) {
+        const int p = i0 + q * 256 + 4 * lane;
+        v[q] = p < b1 ? *reinterpret_cast<const float4 *>(sc + p) : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+}
+
+__device__ __forceinline__ float f4(const float4 &v, int x)
+{
+    return x == 0 ? v.x : (x == 1 ? v.y : (x == 2 ? v.z : v.w));
+}
+
+// Top selections of one score row: positions [0, npos), of which those with
+// list[pos] <= lim (all of them without a list) are valid; valid positions
+// form a prefix. Rows are 16-byte aligned and padded to a multiple of 4.
+__device__ __forceinline__ void select_row(const SelRow &s, const SelOut *outs, int nout, SelShared &sm)
+{
+    const int lane = lane_id();
+    const float *sc = s.sc;
+    const int selmax = (nout > 1 && outs[1].sel > outs[0].sel) ? outs[1].sel : outs[0].sel;
+
+    bool staged = true;
+    bool identity = true;  // LDS entry i is row position i
+    int n = s.npos, m;
+    const int32_t *vlist = s.list;  // list still to be checked for validity
+    if (vlist && n > kCandCap) {
+        int v = 0;
+        for (int i = threadIdx.x; i < s.npos; i += kSelectThreads)
+            v += vlist[i] <= s.lim ? 1 : 0;
+        n = wave_totals(wave_sum(v), 0u, 0u, sm).total;
+        vlist = nullptr;
+    }
+    uint32_t lo = 0xFFFFFFFFu, hi = 0u;
+    if (n <= kCandCap) {
+        // the whole row: one batched load, validity from the list on the way
+        const RowSeg g = row_segment(n);
+        int nv = 0;
+        for (int i0 = g.b0; i0 < g.b1; i0 += kStageSteps * 256) {
+            float4 v[kStageSteps];
+            int4 lv[kStageSteps] = {};
+            load_batch(sc, i0, g.b1, v);
+            if (vlist) {
 #pragma unroll
-        for (int x = 0; x < 4; ++x) {
-            if (in[x]) {
-                if (o < sel) {
-                    const int pos = p0 + x;
-                    const int32_t idx = s.list ? s.list[pos] : pos;
-                    for (int f = 0; f < fan; ++f) {
-                        oidx[f * fstride + o] = idx;
-                        if (osc)
-                            osc[f * fstride + o] = v[x];
+                for (int q = 0; q < kStageSteps; ++q) {
+                    const int p = i0 + q * 256 + 4 * lane;
+#pragma unroll
+                    for (int x = 0; x < 4; ++x) {
+                        const int px = p + x;
+                        const int e = px < g.b1 ? vlist[px] : 0;
+                        (x == 0 ? lv[q].x : x == 1 ? lv[q].y : x == 2 ? lv[q].z : lv[q].w) = e;
                     }
                 }
-                ++o;
+            }
+#pragma unroll
+            for (int q = 0; q < kStageSteps; ++q) {
+                const int p = i0 + q * 256 + 4 * lane;
+                if (p + 3 < g.b1)
+                    *reinterpret_cast<float4 *>(&sm.cs[p]) = v[q];
+#pragma unroll
+                for (int x = 0; x < 4; ++x) {
+                    const int px = p + x;
+                    const int e = x == 0 ? lv[q].x : x == 1 ? lv[q].y : x == 2 ? lv[q].z : lv[q].w;
+                    if (px < g.b1 && (vlist == nullptr || e <= s.lim)) {
+                        const float f = f4(v[q], x);
+                        if (p + 3 >= g.b1)
+                            sm.cs[px] = f;
+                        lo = min(lo, score_key(f));
+                        hi = max(hi, score_key(f));
+                        ++nv;
+                    }
+                }
             }
         }
-        run += tot;
-    });
-    for (int x = emitted_total + threadIdx.x; x < sel; x += blockDim.x) {
-        for (int f = 0; f < fan; ++f) {
-            oidx[f * fstride + x] = -1;
-            if (osc)
-                osc[f * fstride + x] = -__builtin_inff();
+        const WaveTotals t = wave_totals(wave_sum(nv), wave_min(lo), wave_max(hi), sm);
+        n = m = t.total;
+        lo = t.lo;
+        hi = t.hi;
+    } else {
+        // 1. theta from a strided sample
+        constexpr int kPer = kSampleMax / kSelectThreads;
+        const int ns = (n >> 1) < kSampleMax ? (n >> 1) : kSampleMax;
+        const int stride = n / ns;
+        uint32_t slo = 0xFFFFFFFFu, shi = 0u;
+        float f[kPer];
+#pragma unroll
+        for (int u = 0; u < kPer; ++u) {
+            const int i = threadIdx.x + u * kSelectThreads;
+            f[u] = i < ns ? sc[(int64_t)i * stride + stride / 2] : 0.f;
+        }
+#pragma unroll
+        for (int u = 0; u < kPer; ++u) {
+            const int i = threadIdx.x + u * kSelectThreads;
+            if (i < ns) {
+                sm.cs[i] = f[u];
+                slo = min(slo, score_key(f[u]));
+                shi = max(shi, score_key(f[u]));
+            }
+        }
+        const WaveTotals st = wave_totals(0, wave_min(slo), wave_max(shi), sm);
+        const float expect = (float)selmax * (float)ns / (float)n;
+        int r = (int)ceilf(expect + 4.f * sqrtf(expect)) + 8;
+        r = r < ns ? r : ns;
+        const Cut sc_cut = block_radix_cut(ns, r, st.lo, st.hi, [&](int i) { return score_key(sm.cs[i]); }, sm);
+        const uint32_t theta = sc_cut.req > 0 ? sc_cut.keq : (uint32_t)(sc_cut.kgt + 1);
+
+        // 2. count the scores >= theta (and the row's key range)
+        const RowSeg g = row_segment(n);
+        const bool held = g.S <= kRegSteps * 256;
+        float4 v[kRegSteps];
+        int cnt = 0;
+        for (int i0 = g.b0; i0 < g.b1; i0 += kRegSteps * 256) {
+            load_batch(sc, i0, g.b1, v);
+#pragma unroll
+            for (int q = 0; q < kRegSteps; ++q) {
+                const int p = i0 + q * 256 + 4 * lane;
+#pragma unroll
+                for (int x = 0; x < 4; ++x) {
+                    if (p + x < g.b1) {
+                        const uint32_t k = score_key(f4(v[q], x));
+                        cnt += k >= theta ? 1 : 0;
+                        lo = min(lo, k);
+                        hi = max(hi, k);
+                    }
+                }
+            }
+        }
+        const WaveTotals t = wave_totals(wave_sum(cnt), wave_min(lo), wave_max(hi), sm);
+        m = t.total;
+        lo = t.lo;
+        hi = t.hi;
+        if (m < selmax || m > kCandCap) {
+            staged = false;  // exact selection on the row in global memory
+        } else {
+            // 3. pack them in index order
+            int slot0 = t.off;
+            for (int i0 = g.b0; i0 < g.b1; i0 += kRegSteps * 256) {
+                if (!held)
+                    load_batch(sc, i0, g.b1, v);
+#pragma unroll
+                for (int q = 0; q < kRegSteps; ++q) {
+                    const int p = i0 + q * 256 + 4 * lane;
+                    bool in[4];
+                    uint64_t b[4];
+                    int before = 0, mine = 0;
+#pragma unroll
+                    for (int x = 0; x < 4; ++x) {
+                        in[x] = p + x < g.b1 && score_key(f4(v[q], x)) >= theta;
+                        b[x] = ballot(in[x]);
+                        before += prefix_count(b[x]);
+                    }
+                    int o = slot0 + before;
+#pragma unroll
+                    for (int x = 0; x < 4; ++x) {
+                        if (in[x]) {
+                            sm.cs[o] = f4(v[q], x);
+                            sm.cp[o] = p + x;
+                            ++o;
+                        }
+                        mine += __popcll(b[x]);
+                    }
+                    slot0 += mine;
+                }
+            }
+            identity = false;
+            lo = theta;
+            __syncthreads();
         }
     }
-    __syncthreads();
-}
 
-// pass 0: level-1 histogram of the valid positions; returns their count
-__device__ int row_histogram(const SelRow &s, SelScratch &sm)
-{
-    const int wave = uniform(threadIdx.x / kWave);  // wave-uniform (SGPR)
-    block_clear(sm.h1, kSelBins1);
-    __syncthreads();
-    const Segment seg = wave_segment(s.npos, wave);
-    int cnt = 0;
-    segment_pass(s, seg, [&](const float (&v)[4], int p0) {
 #pragma unroll
-        for (int x = 0; x < 4; ++x) {
-            const int pos = p0 + x;
-            if (pos < seg.e && sel_valid(s, pos)) {
-                atomicAdd(&sm.h1[score_key(v[x]) >> 18], 1u);
-                ++cnt;
-            }
+    for (int j = 0; j < 2; ++j) {
+        if (j >= nout)
+            break;
+        const SelOut &o = outs[j];
+        if (staged) {
+            const Cut c = block_radix_cut(m, o.sel, lo, hi, [&](int i) { return score_key(sm.cs[i]); }, sm);
+            if (identity)
+                block_emit(m, c, o, s.list, [&](int i) { return sm.cs[i]; }, [&](int i) { return i; }, sm);
+            else
+                block_emit(m, c, o, s.list, [&](int i) { return sm.cs[i]; }, [&](int i) { return sm.cp[i]; }, sm);
+        } else {
+            const Cut c = block_radix_cut(n, o.sel, lo, hi, [&](int i) { return score_key(sc[i]); }, sm);
+            block_emit(n, c, o, s.list, [&](int i) { return sc[i]; }, [&](int i) { return i; }, sm);
         }
-    });
-    cnt = wave_sum(cnt);
-    if (threadIdx.x % kWave == 0)
-        sm.wgt[wave] = cnt;
-    __syncthreads();
-    int count = 0;
-    for (int w = 0; w < kSelWaves; ++w)
-        count += sm.wgt[w];
-    __syncthreads();
-    return count;
+    }
 }
 
 __global__ __launch_bounds__(kSelectThreads) void split_select_kernel(SplitSelectParams p)
 {
-    __shared__ SelScratch sm;
+    __shared__ SelShared sm;
     const int bi = blockIdx.y;
     const int64_t r = blockIdx.x;
     const int64_t off = p.L - p.q_len;
@@ -708,12 +790,10 @@ __global__ __launch_bounds__(kSelectThreads) void split_select_kernel(SplitSelec
         s1 = p.o1_score ? p.o1_score + row * p.sel : nullptr;
     }
 
-    const int count = row_histogram(s, sm);
-    select_row(s, sm, count, p.sel, o1, s1, fan1, p.sel);
-    if (p.sel2 > 0) {
-        row_histogram(s, sm);
-        select_row(s, sm, count, p.sel2, o2, s2, fan2, p.sel2);
-    }
+    SelOut outs[2];
+    outs[0] = SelOut{p.sel, o1, s1, fan1};
+    outs[1] = SelOut{p.sel2, o2, s2, fan2};
+    select_row(s, outs, p.sel2 > 0 ? 2 : 1, sm);
 }
 
 // ------------------------------------------------------------- launchers
