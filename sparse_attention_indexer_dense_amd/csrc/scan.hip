@@ -38,6 +38,17 @@ struct ScanStage {
     static constexpr int KEYS = NW >= 8 ? 128 : 64;
 };
 
+// LDS histogram increment for use while key DMA is in flight. Written as
+// inline asm because the compiler's wait insertion cannot tell an LDS atomic
+// from the DMA's LDS writes and would make every increment wait for all
+// outstanding memory traffic (the key DMA of the next stage included). LDS
+// operations of a wave execute in order, so later reads of the bin see it.
+__device__ __forceinline__ void lds_inc(uint32_t *p)
+{
+    const uint32_t a = (uint32_t)(uintptr_t)((__attribute__((address_space(3))) uint32_t *)p);
+    asm volatile("ds_add_u32 %0, %1" : : "v"(a), "v"(1u) : "memory");
+}
+
 // ----------------------------------------------------------- per-row select
 struct RowState {
     float theta_exact;  // exact floor set by a compaction (-inf before)
@@ -73,12 +84,12 @@ __device__ __forceinline__ Level1 level1(const uint32_t *h, RowState st, int sel
 }
 
 // Visit buf[0..nbuf) in index order, 64 entries per wave step, with the loads
-// of four steps issued together so that passes are not latency-bound.
+// of sixteen steps issued together so that passes are not latency-bound.
 // f(entry, valid) runs once per step and lane.
 template <typename F>
 __device__ __forceinline__ void buffer_pass(const Entry *buf, int nbuf, F &&f)
 {
-    constexpr int U = 4;
+    constexpr int U = 16;
     const int lane = lane_id();
     for (int base = 0; base < nbuf; base += U * kWave) {
         Entry e[U];
@@ -438,7 +449,6 @@ void scan_select_kernel(ScanParams p)
         st.b = 0;
         st.count_ge = 0;
         st.nbuf = 0;
-        int hb = 0;  // h[st.b], kept in step with the histogram
         if (wr.valid)
             clear_hist<kBins1>(h);
 
@@ -449,8 +459,13 @@ void scan_select_kernel(ScanParams p)
         const int ntiles = (nkeys + STAGE - 1) / STAGE;
 
         // MFMA score tile of 32 keys (tile nt of the stage in kb)
+        // (all K fragments of the tile are read before its first MFMA; the
+        // scheduling barrier keeps the compiler from sinking the reads back
+        // next to their MFMAs, where each would wait out the LDS latency)
+        // (Refine, with its candidate-list bookkeeping, reads them in two
+        // halves to stay within the register budget)
         auto mfma_tile = [&](const unsigned char *kb, int nt, f32x16 (&acc)[MB]) {
-            constexpr int KB = KS >= 4 ? 4 : KS;  // K fragments in flight at once
+            constexpr int KB = (MODE == kRefine && KS > 4) ? KS / 2 : KS;
 #pragma unroll
             for (int mb = 0; mb < MB; ++mb)
                 acc[mb] = f32x16{};
@@ -461,6 +476,7 @@ void scan_select_kernel(ScanParams p)
                 for (int ks = 0; ks < KB; ++ks)
                     kf[ks] = __builtin_bit_cast(
                         bf16x8, *reinterpret_cast<const u32x4 *>(kb + koff[k0 + ks] + nt * 32 * ROWB));
+                __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
                 for (int ks = 0; ks < KB; ++ks)
 #pragma unroll
@@ -487,7 +503,9 @@ void scan_select_kernel(ScanParams p)
         // raise the threshold bin while the bins above it hold >= sel entries:
         // a step or two by walking, a longer jump by searching all bins at once
         auto advance = [&]() {
-            int bb = st.b, cg = st.count_ge, hv = hb;
+            int bb = st.b, cg = st.count_ge, hv = uniform((int)h[bb]);
+            if (cg - hv < p.sel)
+                return;
             for (int step = 0; step < 2 && cg - hv >= p.sel && bb < kBins1 - 1; ++step) {
                 cg -= hv;
                 ++bb;
@@ -502,7 +520,6 @@ void scan_select_kernel(ScanParams p)
             }
             st.b = bb;
             st.count_ge = cg;
-            hb = hv;
             st.theta = fmaxf(st.theta_exact, bin1_floor(st.b));
         };
         // causal mask and threshold filter of tile nt (lanes 0..31 own the 32 keys)
@@ -520,32 +537,28 @@ void scan_select_kernel(ScanParams p)
             const bool adm = ok && total > st.theta;
             const uint64_t m = ballot(adm);
             if (m) {
-                const uint32_t sk = score_key(total);
-                const int bin = (int)(sk >> 21);
                 if (adm) {
                     Entry e;
                     e.score = total;
                     e.idx = key;
                     buf[st.nbuf + prefix_count(m)] = e;
-                    atomicAdd(&h[bin], 1u);
+                    lds_inc(&h[bin1(score_key(total))]);
                 }
                 const int cnt = __popcll(m);
                 st.nbuf += cnt;
                 st.count_ge += cnt;
-                hb += __popcll(ballot(adm && bin == st.b));
-                if (st.count_ge - hb >= p.sel)
-                    advance();
             }
         };
 
-        // after a stage: compact a nearly full buffer
+        // after a stage: raise the threshold (once per stage: a lag of at
+        // most one stage of keys), and compact a nearly full buffer
         auto stage_end = [&]() {
             if (!wr.valid)
                 return;
-            if (st.nbuf > p.cap - STAGE) {
+            if (st.count_ge >= p.sel)
+                advance();
+            if (st.nbuf > p.cap - STAGE)
                 st = compact(buf, h, st, p.sel);
-                hb = uniform((int)h[st.b]);
-            }
         };
 
         // the active tiles of a stage, software-pipelined: the MFMAs of tile
