@@ -108,7 +108,7 @@ __device__ __forceinline__ void buffer_pass(const Entry *buf, int nbuf, F &&f)
 }
 
 // Finish a cut with levels 2 and 3 (passes over the buffer); h is scratch.
-__device__ Cut finish_cut(const Entry *buf, int nbuf, uint32_t *h, Level1 a)
+__device__ __forceinline__ Cut finish_cut(const Entry *buf, int nbuf, uint32_t *h, Level1 a)
 {
     Cut c;
     if (a.all || a.r1 == a.h1) {
@@ -151,7 +151,7 @@ __device__ Cut finish_cut(const Entry *buf, int nbuf, uint32_t *h, Level1 a)
 
 // Write the entries of the cut, in buffer (= ascending index) order, to
 // `fan` output rows spaced `fstride` apart; pad each row to `sel` with -1/-inf.
-__device__ void emit(const Entry *buf, int nbuf, Cut c, int sel,
+__device__ __forceinline__ void emit(const Entry *buf, int nbuf, Cut c, int sel,
                      int32_t *oidx, float *osc, int fan, int64_t fstride)
 {
     const int lane = lane_id();
