@@ -215,13 +215,17 @@ int check_ptrs(const void *Q, const float *W, const void *K, const int32_t *out_
     return DSAIDX_OK;
 }
 
-// Positions per workgroup of split_score_kernel: about 4096 waves in all, each
-// covering 128..kSplitSpanMax contiguous positions (long enough to amortise
-// loading its 16 KiB query row).
-int64_t split_chunk(int64_t rows_total, int64_t npos)
+// Positions per workgroup of split_score_kernel: one round of workgroups (one
+// per CU, four waves each) covers all rows, each wave a contiguous span of at
+// least 128 positions (to amortise loading its query row); a span that reads
+// a candidate list is capped by the list's LDS buffer.
+int64_t split_chunk(int64_t rows_total, int64_t npos, bool list)
 {
-    int64_t per_wave = ceil_div(ceil_div(rows_total * npos, 4096), 32) * 32;
-    per_wave = std::min<int64_t>(std::max<int64_t>(per_wave, 128), kSplitSpanMax);
+    const int64_t waves = (int64_t)std::max(1, num_cus()) * kSplitWaves;
+    int64_t per_wave = ceil_div(ceil_div(rows_total * npos, waves), 32) * 32;
+    per_wave = std::max<int64_t>(per_wave, 128);
+    if (list)
+        per_wave = std::min<int64_t>(per_wave, kSplitSpanMax);
     return per_wave * kSplitWaves;
 }
 
@@ -246,7 +250,7 @@ int run_split(int mode, const uint16_t *Q, const float *W, const uint16_t *K, co
     sp.nrows = nrows;
     sp.rowlen = rowlen;
     const int64_t npos_max = (mode == kRefine) ? std::min<int64_t>(c, L) : L;
-    sp.chunk = split_chunk((int64_t)B * nrows, npos_max);
+    sp.chunk = split_chunk((int64_t)B * nrows, npos_max, mode == kRefine);
     sp.scores = scores;
     dim3 grid((unsigned)ceil_div(npos_max, sp.chunk), (unsigned)nrows, (unsigned)B);
     hipError_t e = launch_split_score(H, D, sp, grid, stream);

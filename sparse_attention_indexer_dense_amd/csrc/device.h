@@ -158,6 +158,15 @@ __device__ __forceinline__ void find_bin(const uint32_t *h, int target, int &x, 
     above = uniform(ab);
 }
 
+// Workgroup barrier for LDS traffic only: each wave waits for its own LDS
+// operations, not for its global stores (a __syncthreads would also wait for
+// those, microseconds after a burst of stores). The memory clobber keeps the
+// compiler from moving memory accesses across it.
+__device__ __forceinline__ void lds_sync()
+{
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 template <int NB>
 __device__ __forceinline__ void clear_hist(uint32_t *h)
 {

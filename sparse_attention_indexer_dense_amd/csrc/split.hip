@@ -5,18 +5,20 @@
 // cache, so there are too few rows to fill the GPU with one workgroup per row.
 // The key axis is split instead:
 //   split_score_kernel  - a workgroup owns (batch item, row, span of key
-//                         positions); each wave streams its own contiguous
-//                         part of the span in 32-key tiles through a private
-//                         pair of LDS buffers filled by global->LDS DMA (the
-//                         DMA of tile t+1 overlaps the MFMAs on tile t), runs
-//                         the MFMA score tile and the ReLU/weight/head-sum
-//                         epilogue, and stores one fp32 score per position;
+//                         positions), one round of workgroups for all rows;
+//                         each wave streams its own contiguous part of the
+//                         span in 32-key tiles through a private ring of LDS
+//                         tiles filled by global->LDS DMA (several tiles in
+//                         flight while one is scored), runs the MFMA score
+//                         tile and the ReLU/weight/head-sum epilogue, and
+//                         stores one fp32 score per position;
 //   split_select_kernel - one workgroup per score row finds the exact top-sel
-//                         (ties to the lower index) in three passes: a
-//                         level-1 histogram; per-wave counts of the sure
-//                         entries plus the boundary bin gathered into LDS and
-//                         resolved there; one ordered emission in ascending
-//                         index order at per-wave offsets.
+//                         (ties to the lower index): a row that fits in LDS
+//                         is staged whole; a longer one is first reduced to
+//                         the scores above a threshold taken from a sample,
+//                         with an exact pass over the row as the fallback;
+//                         an exact radix cut and one ordered emission in
+//                         ascending index order follow.
 // Only the score vectors of the few decode rows are stored.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -76,13 +78,17 @@ __device__ __forceinline__ void wait_vmcnt()
     __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
-// Each wave streams its span of positions through a private ring of kRing
-// LDS tiles of 32 keys; tile t+kRing-1 is in flight while tile t is scored.
-// Every tile costs exactly DMA_PER_TILE DMA instructions (lanes without a key
-// fetch row 0 into a slot that is never read) and exactly one score store, so
-// the number of vector-memory operations issued after tile t's DMA is known
-// and the wait for it is exact.
-constexpr int kRing = 4;
+// Each wave streams its span of positions through a private ring of RING
+// LDS tiles of 32 keys; tiles t+1 .. t+RING-1 are in flight while tile t is
+// scored. Every tile costs exactly DMA_PER_TILE DMA instructions (lanes
+// without a key fetch row 0 into a slot that is never read) and exactly one
+// score store, so the number of vector-memory operations issued after tile
+// t's DMA is known and the wait for it is exact. The ring fills the LDS:
+// five tiles per wave for a key prefix, four beside the candidate list.
+template <bool LIST, int ROWB>
+struct SplitRing {
+    static constexpr int RING = (LIST || ROWB < 256) ? 4 : 5;
+};
 
 template <int H, int D, bool LIST>
 __global__ __launch_bounds__(kSplitWaves * kWave) void split_score_kernel(SplitScoreParams p)
@@ -92,8 +98,9 @@ __global__ __launch_bounds__(kSplitWaves * kWave) void split_score_kernel(SplitS
     constexpr int TILE_BYTES = 32 * ROWB;
     constexpr int DMA_PER_TILE = TILE_BYTES / 1024;
     constexpr int RPI = kWave / CHUNKS;  // key rows per DMA instruction
+    constexpr int kRing = SplitRing<LIST, ROWB>::RING;
     __shared__ __align__(1024) unsigned char ring[kSplitWaves][kRing][TILE_BYTES];
-    __shared__ int32_t lst[kSplitWaves][LIST ? kSplitSpanMax : 1];
+    __shared__ int32_t lst[kSplitWaves][LIST ? kSplitSpanMax : 0];
 
     const int bi = blockIdx.z;
     const int64_t r = blockIdx.y;
@@ -161,19 +168,27 @@ __global__ __launch_bounds__(kSplitWaves * kWave) void split_score_kernel(SplitS
     for (int ks = 0; ks < KS; ++ks)
         koff[ks] = (uint32_t)(col * ROWB + (((half * KS + ks) ^ (col & (CHUNKS - 1))) * 16));
 
-    auto tile = [&](int t) {
+    // MFMA score tile t into acc (all K fragments read first)
+    auto mfma_tile = [&](int t, f32x16 (&acc)[MB]) {
         const unsigned char *src = ring[wave][t % kRing];
-        f32x16 acc[MB];
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb)
             acc[mb] = f32x16{};
+        bf16x8 kf[KS];
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-            const bf16x8 kf = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(src + koff[ks]));
+        for (int ks = 0; ks < KS; ++ks)
+            kf[ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(src + koff[ks]));
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
             for (int mb = 0; mb < MB; ++mb)
-                acc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[mb][ks], kf, acc[mb], 0, 0, 0);
-        }
+                acc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[mb][ks], kf[ks], acc[mb], 0, 0, 0);
+    };
+    // epilogue of tile t and its one store instruction: lane 0 always holds a
+    // position of the tile; positions whose key is beyond the row's limit get
+    // a score too, which the selection ignores
+    auto finish = [&](int t, const f32x16 (&acc)[MB]) {
         float part[MB];
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb) {
@@ -187,31 +202,60 @@ __global__ __launch_bounds__(kSplitWaves * kWave) void split_score_kernel(SplitS
         for (int mb = 1; mb < MB; ++mb)
             s += part[mb];
         const float total = half_wave_sum(s) + 0.0f;
-        // one store instruction per tile: lane 0 always holds a position of
-        // the tile; positions whose key is beyond the row's limit get a score
-        // too, which the selection ignores
         const int pos = w0 + t * 32 + col;
         if (lane < 32 && pos < w1)
             out[pos] = total;
     };
+    // tile t's DMA is complete once at most this many vector-memory
+    // operations are outstanding: the DMA of the kRing - 2 tiles issued after
+    // it, and the stores issued since (tile t - 1's in iteration t, one per
+    // iteration from iteration 1 on, at most kRing - 1)
+    auto wait_tile = [&](int t) {
+        constexpr int B0 = (kRing - 2) * DMA_PER_TILE;
+        const int st = t < 1 ? 0 : (t - 1 < kRing - 1 ? t - 1 : kRing - 1);
+        switch (st) {
+        case 0: wait_vmcnt<B0>(); break;
+        case 1: wait_vmcnt<B0 + 1>(); break;
+        case 2: wait_vmcnt<B0 + 2>(); break;
+        case 3: wait_vmcnt<B0 + 3>(); break;
+        default: wait_vmcnt<B0 + 4>(); break;
+        }
+    };
 
-    // operands loaded, then the ring primed with kRing - 1 tiles
-    __builtin_amdgcn_s_waitcnt(0);
+    // the ring primed with kRing - 1 tiles behind the operand loads (waiting
+    // for tile 0 waits for them as well); the MFMAs of tile t run next to the
+    // epilogue of tile t - 1
+    __builtin_amdgcn_sched_barrier(0);
     for (int t = 0; t < kRing - 1; ++t)
         issue(t);
+    f32x16 a0[MB], a1[MB];
     for (int t = 0; t < ntile; ++t) {
         __builtin_amdgcn_sched_barrier(0);
-        if (t == 0)
-            wait_vmcnt<(kRing - 2) * DMA_PER_TILE>();
-        else if (t == 1)
-            wait_vmcnt<(kRing - 2) * DMA_PER_TILE + 1>();
-        else if (t == 2)
-            wait_vmcnt<(kRing - 2) * DMA_PER_TILE + 2>();
-        else
-            wait_vmcnt<(kRing - 2) * DMA_PER_TILE + 3>();
+        wait_tile(t);
         __builtin_amdgcn_sched_barrier(0);
         issue(t + kRing - 1);
-        tile(t);
+        if (t == 0) {
+            mfma_tile(0, a0);
+        } else {
+            if (t & 1) {
+                mfma_tile(t, a1);
+                finish(t - 1, a0);
+            } else {
+                mfma_tile(t, a0);
+                finish(t - 1, a1);
+            }
+#pragma unroll
+            for (int q = 0; q < KS * MB; ++q) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+            }
+        }
+    }
+    if (ntile > 0) {
+        if ((ntile - 1) & 1)
+            finish(ntile - 1, a1);
+        else
+            finish(ntile - 1, a0);
     }
     // no DMA may still be writing this workgroup's LDS when it exits
     __builtin_amdgcn_s_waitcnt(0);
@@ -295,7 +339,7 @@ __device__ __forceinline__ WaveTotals wave_totals(int t, uint32_t lo, uint32_t h
         sm.wlo[wave] = lo;
         sm.whi[wave] = hi;
     }
-    __syncthreads();
+    lds_sync();
     WaveTotals r{0, 0, 0xFFFFFFFFu, 0u};
     for (int w = 0; w < kSelWaves; ++w) {
         const int x = sm.wt[w];
@@ -304,7 +348,7 @@ __device__ __forceinline__ WaveTotals wave_totals(int t, uint32_t lo, uint32_t h
         r.lo = min(r.lo, sm.wlo[w]);
         r.hi = max(r.hi, sm.whi[w]);
     }
-    __syncthreads();
+    lds_sync();
     return r;
 }
 
@@ -319,7 +363,7 @@ __device__ __forceinline__ void block_find_bin(const uint32_t *h, int target, Se
             sm.bc[1] = ab;
         }
     }
-    __syncthreads();
+    lds_sync();
     x = sm.bc[0];
     above = sm.bc[1];
 }
@@ -352,24 +396,24 @@ __device__ __forceinline__ Cut block_radix_cut(int m, int sel, uint32_t base, ui
         sm.h[i] = 0u;
     if (threadIdx.x == 0)
         sm.nbnd = 0;
-    __syncthreads();
+    lds_sync();
     for (int i = threadIdx.x; i < m; i += kSelectThreads)
         atomicAdd(&sm.h[(key_at(i) - base) >> s1], 1u);
-    __syncthreads();
+    lds_sync();
     int b1, a1;
     block_find_bin(sm.h, sel, sm, b1, a1);
     const int r1 = sel - a1;
     const int cnt1 = (int)sm.h[b1];
     if (r1 == cnt1) {  // the whole bin is in
         c.kgt = (int64_t)base + ((int64_t)b1 << s1) - 1;
-        __syncthreads();
+        lds_sync();
         return c;
     }
     if (s1 == 0) {  // a bin is one key
         c.keq = base + (uint32_t)b1;
         c.kgt = (int64_t)c.keq;
         c.req = r1;
-        __syncthreads();
+        lds_sync();
         return c;
     }
     if (cnt1 <= kBoundaryCap) {
@@ -395,7 +439,7 @@ __device__ __forceinline__ Cut block_radix_cut(int m, int sel, uint32_t base, ui
                 }
             }
         }
-        __syncthreads();
+        lds_sync();
         // entry e has rank (#keys above) + (#equal keys earlier); the one of
         // rank r1 - 1 fixes the cut
         for (int e = threadIdx.x; e < cnt1; e += kSelectThreads) {
@@ -414,10 +458,10 @@ __device__ __forceinline__ Cut block_radix_cut(int m, int sel, uint32_t base, ui
                 sm.bc[4] = equal;
             }
         }
-        __syncthreads();
+        lds_sync();
         const uint32_t kstar = (uint32_t)sm.bc[2];
         const int take = sm.bc[3], equal = sm.bc[4];
-        __syncthreads();
+        lds_sync();
         if (take == equal) {
             c.kgt = (int64_t)kstar - 1;
         } else {
@@ -428,7 +472,7 @@ __device__ __forceinline__ Cut block_radix_cut(int m, int sel, uint32_t base, ui
         return c;
     }
     // levels 2 and 3
-    __syncthreads();
+    lds_sync();
     uint32_t pre = (uint32_t)b1;  // digits fixed so far: u >> prev == pre
     int prev = s1;
     int r = r1;
@@ -437,19 +481,19 @@ __device__ __forceinline__ Cut block_radix_cut(int m, int sel, uint32_t base, ui
         const uint32_t mask = (1u << (prev - sh)) - 1u;
         for (int i = threadIdx.x; i < kBins1; i += kSelectThreads)
             sm.h[i] = 0u;
-        __syncthreads();
+        lds_sync();
         for (int i = threadIdx.x; i < m; i += kSelectThreads) {
             const uint32_t u = key_at(i) - base;
             if ((u >> prev) == pre)
                 atomicAdd(&sm.h[(u >> sh) & mask], 1u);
         }
-        __syncthreads();
+        lds_sync();
         int b, a;
         block_find_bin(sm.h, r, sm, b, a);
         const int rr = r - a;
         const int cnt = (int)sm.h[b];
         pre = (pre << (prev - sh)) | (uint32_t)b;
-        __syncthreads();
+        lds_sync();
         if (rr == cnt) {
             c.kgt = (int64_t)base + ((int64_t)pre << sh) - 1;
             return c;
@@ -530,7 +574,7 @@ __device__ __forceinline__ void block_emit(int m, const Cut &c, const SelOut &o,
                 o.score[(int64_t)f * o.sel + x] = -__builtin_inff();
         }
     }
-    __syncthreads();
+    lds_sync();
 }
 
 // Wave w's contiguous segment of a row of n scores, in float4 steps of 256
@@ -563,6 +607,124 @@ __device__ __forceinline__ void load_batch(const float *sc, int i0, int b1, floa
 __device__ __forceinline__ float f4(const float4 &v, int x)
 {
     return x == 0 ? v.x : (x == 1 ? v.y : (x == 2 ? v.z : v.w));
+}
+
+// Lower bound theta for the top-`sel` of the n scores of a row: an exact
+// order statistic of a sample of contiguous 64-score chunks spread evenly over
+// the row, of rank chosen with slack so that, with high probability, at least
+// sel scores of the row reach it. Whether they do is checked by the caller.
+__device__ __forceinline__ uint32_t sample_theta(const float *sc, int n, int sel, SelShared &sm)
+{
+    constexpr int kPer = kSampleMax / kSelectThreads;
+    const int half = n >> 1;
+    const int ns = ((half < kSampleMax ? half : kSampleMax) / kWave) * kWave;  // n > kCandCap: ns >= 6144
+    const int nch = ns / kWave;
+    uint32_t slo = 0xFFFFFFFFu, shi = 0u;
+    float f[kPer];
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) {
+        const int i = threadIdx.x + u * kSelectThreads;
+        const int ch = i / kWave;
+        f[u] = i < ns ? sc[(int)((int64_t)ch * n / nch) + i % kWave] : 0.f;
+    }
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) {
+        const int i = threadIdx.x + u * kSelectThreads;
+        if (i < ns) {
+            sm.cs[i] = f[u];
+            slo = min(slo, score_key(f[u]));
+            shi = max(shi, score_key(f[u]));
+        }
+    }
+    const WaveTotals st = wave_totals(0, wave_min(slo), wave_max(shi), sm);
+    const float expect = (float)sel * (float)ns / (float)n;
+    int r = (int)ceilf(expect + 4.f * sqrtf(expect)) + 8;
+    r = r < ns ? r : ns;
+    const Cut c = block_radix_cut(ns, r, st.lo, st.hi, [&](int i) { return score_key(sm.cs[i]); }, sm);
+    lds_sync();
+    return c.req > 0 ? c.keq : (uint32_t)(c.kgt + 1);
+}
+
+// The scores >= theta among positions [b, e) of a row (b a multiple of 4),
+// counted and then, if there are at most `cap`, written in index order as
+// dst(slot, score, position). Wave w walks the w-th contiguous segment in
+// float4 steps; a segment of at most kRegSteps steps stays in registers
+// between the two passes. Returns the count; kmax gets the largest key among
+// them (in every thread).
+template <typename Dst>
+__device__ __forceinline__ int count_pack(const float *sc, int b, int e, uint32_t theta, int cap, Dst dst,
+                                          SelShared &sm, uint32_t &kmax)
+{
+    const int wave = uniform(threadIdx.x / kWave), lane = lane_id();
+    const int S = (e - b + kSelWaves * 256 - 1) / (kSelWaves * 256) * 256;
+    const int b0 = b + wave * S;
+    const int b1 = (b0 + S < e) ? b0 + S : e;
+    const bool held = S <= kRegSteps * 256;
+    float4 v[kRegSteps];
+    int cnt = 0;
+    uint32_t km = 0u;
+    for (int i0 = b0; i0 < b1; i0 += kRegSteps * 256) {
+        load_batch(sc, i0, b1, v);
+#pragma unroll
+        for (int q = 0; q < kRegSteps; ++q) {
+            const int p = i0 + q * 256 + 4 * lane;
+#pragma unroll
+            for (int x = 0; x < 4; ++x) {
+                const uint32_t k = score_key(f4(v[q], x));
+                const bool in = p + x < b1 && k >= theta;
+                cnt += in ? 1 : 0;
+                km = in ? max(km, k) : km;
+            }
+        }
+    }
+    const WaveTotals t = wave_totals(wave_sum(cnt), 0u, wave_max(km), sm);
+    kmax = t.hi;
+    if (t.total > cap)
+        return t.total;
+    int slot0 = t.off;
+    for (int i0 = b0; i0 < b1; i0 += kRegSteps * 256) {
+        if (!held)
+            load_batch(sc, i0, b1, v);
+#pragma unroll
+        for (int q = 0; q < kRegSteps; ++q) {
+            const int p = i0 + q * 256 + 4 * lane;
+            bool in[4];
+            uint64_t bm[4];
+            int before = 0, mine = 0;
+#pragma unroll
+            for (int x = 0; x < 4; ++x) {
+                in[x] = p + x < b1 && score_key(f4(v[q], x)) >= theta;
+                bm[x] = ballot(in[x]);
+                before += prefix_count(bm[x]);
+            }
+            int o = slot0 + before;
+#pragma unroll
+            for (int x = 0; x < 4; ++x) {
+                if (in[x]) {
+                    dst(o, f4(v[q], x), p + x);
+                    ++o;
+                }
+                mine += __popcll(bm[x]);
+            }
+            slot0 += mine;
+        }
+    }
+    lds_sync();
+    return t.total;
+}
+
+// Key range of positions [0, n) of a row (for the exact path over the row).
+__device__ __forceinline__ void row_range(const float *sc, int n, SelShared &sm, uint32_t &lo, uint32_t &hi)
+{
+    uint32_t a = 0xFFFFFFFFu, z = 0u;
+    for (int i = threadIdx.x; i < n; i += kSelectThreads) {
+        const uint32_t k = score_key(sc[i]);
+        a = min(a, k);
+        z = max(z, k);
+    }
+    const WaveTotals t = wave_totals(0, wave_min(a), wave_max(z), sm);
+    lo = t.lo;
+    hi = t.hi;
 }
 
 // Top selections of one score row: positions [0, npos), of which those with
@@ -631,96 +793,24 @@ __device__ __forceinline__ void select_row(const SelRow &s, const SelOut *outs, 
         lo = t.lo;
         hi = t.hi;
     } else {
-        // 1. theta from a strided sample
-        constexpr int kPer = kSampleMax / kSelectThreads;
-        const int ns = (n >> 1) < kSampleMax ? (n >> 1) : kSampleMax;
-        const int stride = n / ns;
-        uint32_t slo = 0xFFFFFFFFu, shi = 0u;
-        float f[kPer];
-#pragma unroll
-        for (int u = 0; u < kPer; ++u) {
-            const int i = threadIdx.x + u * kSelectThreads;
-            f[u] = i < ns ? sc[(int64_t)i * stride + stride / 2] : 0.f;
-        }
-#pragma unroll
-        for (int u = 0; u < kPer; ++u) {
-            const int i = threadIdx.x + u * kSelectThreads;
-            if (i < ns) {
-                sm.cs[i] = f[u];
-                slo = min(slo, score_key(f[u]));
-                shi = max(shi, score_key(f[u]));
-            }
-        }
-        const WaveTotals st = wave_totals(0, wave_min(slo), wave_max(shi), sm);
-        const float expect = (float)selmax * (float)ns / (float)n;
-        int r = (int)ceilf(expect + 4.f * sqrtf(expect)) + 8;
-        r = r < ns ? r : ns;
-        const Cut sc_cut = block_radix_cut(ns, r, st.lo, st.hi, [&](int i) { return score_key(sm.cs[i]); }, sm);
-        const uint32_t theta = sc_cut.req > 0 ? sc_cut.keq : (uint32_t)(sc_cut.kgt + 1);
-
-        // 2. count the scores >= theta (and the row's key range)
-        const RowSeg g = row_segment(n);
-        const bool held = g.S <= kRegSteps * 256;
-        float4 v[kRegSteps];
-        int cnt = 0;
-        for (int i0 = g.b0; i0 < g.b1; i0 += kRegSteps * 256) {
-            load_batch(sc, i0, g.b1, v);
-#pragma unroll
-            for (int q = 0; q < kRegSteps; ++q) {
-                const int p = i0 + q * 256 + 4 * lane;
-#pragma unroll
-                for (int x = 0; x < 4; ++x) {
-                    if (p + x < g.b1) {
-                        const uint32_t k = score_key(f4(v[q], x));
-                        cnt += k >= theta ? 1 : 0;
-                        lo = min(lo, k);
-                        hi = max(hi, k);
-                    }
-                }
-            }
-        }
-        const WaveTotals t = wave_totals(wave_sum(cnt), wave_min(lo), wave_max(hi), sm);
-        m = t.total;
-        lo = t.lo;
-        hi = t.hi;
+        const uint32_t theta = sample_theta(sc, n, selmax, sm);
+        uint32_t km;
+        m = count_pack(sc, 0, n, theta, kCandCap,
+                       [&](int o, float f, int pos) {
+                           sm.cs[o] = f;
+                           sm.cp[o] = pos;
+                       },
+                       sm, km);
         if (m < selmax || m > kCandCap) {
-            staged = false;  // exact selection on the row in global memory
+            staged = false;
         } else {
-            // 3. pack them in index order
-            int slot0 = t.off;
-            for (int i0 = g.b0; i0 < g.b1; i0 += kRegSteps * 256) {
-                if (!held)
-                    load_batch(sc, i0, g.b1, v);
-#pragma unroll
-                for (int q = 0; q < kRegSteps; ++q) {
-                    const int p = i0 + q * 256 + 4 * lane;
-                    bool in[4];
-                    uint64_t b[4];
-                    int before = 0, mine = 0;
-#pragma unroll
-                    for (int x = 0; x < 4; ++x) {
-                        in[x] = p + x < g.b1 && score_key(f4(v[q], x)) >= theta;
-                        b[x] = ballot(in[x]);
-                        before += prefix_count(b[x]);
-                    }
-                    int o = slot0 + before;
-#pragma unroll
-                    for (int x = 0; x < 4; ++x) {
-                        if (in[x]) {
-                            sm.cs[o] = f4(v[q], x);
-                            sm.cp[o] = p + x;
-                            ++o;
-                        }
-                        mine += __popcll(b[x]);
-                    }
-                    slot0 += mine;
-                }
-            }
             identity = false;
             lo = theta;
-            __syncthreads();
+            hi = km;
         }
     }
+    if (!staged)
+        row_range(sc, n, sm, lo, hi);  // exact selection on the row in global memory
 
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
@@ -740,14 +830,12 @@ __device__ __forceinline__ void select_row(const SelRow &s, const SelOut *outs, 
     }
 }
 
-__global__ __launch_bounds__(kSelectThreads) void split_select_kernel(SplitSelectParams p)
+// Row r of batch item bi of a selection pass: its scores, validity, and the
+// outputs of its selections.
+__device__ __forceinline__ void select_geometry(const SplitSelectParams &p, int bi, int64_t r, SelRow &s,
+                                                SelOut (&outs)[2])
 {
-    __shared__ SelShared sm;
-    const int bi = blockIdx.y;
-    const int64_t r = blockIdx.x;
     const int64_t off = p.L - p.q_len;
-
-    SelRow s;
     s.sc = p.scores + ((int64_t)bi * p.nrows + r) * p.rowlen;
     int32_t *o1, *o2 = nullptr;
     float *s1, *s2 = nullptr;
@@ -789,10 +877,18 @@ __global__ __launch_bounds__(kSelectThreads) void split_select_kernel(SplitSelec
         o1 = p.o1_idx + row * p.sel;
         s1 = p.o1_score ? p.o1_score + row * p.sel : nullptr;
     }
-
-    SelOut outs[2];
     outs[0] = SelOut{p.sel, o1, s1, fan1};
     outs[1] = SelOut{p.sel2, o2, s2, fan2};
+}
+
+__global__ __launch_bounds__(kSelectThreads) void split_select_kernel(SplitSelectParams p)
+{
+    __shared__ SelShared sm;
+    const int bi = blockIdx.y;
+    const int64_t r = blockIdx.x;
+    SelRow s;
+    SelOut outs[2];
+    select_geometry(p, bi, r, s, outs);
     select_row(s, outs, p.sel2 > 0 ? 2 : 1, sm);
 }
 
@@ -809,7 +905,7 @@ static hipError_t launch_split_score_t(const SplitScoreParams &prm, dim3 grid, h
 
 hipError_t launch_split_score(int H, int D, const SplitScoreParams &prm, dim3 grid, hipStream_t stream)
 {
-    if (prm.chunk % (32 * kSplitWaves) != 0 || prm.chunk / kSplitWaves > kSplitSpanMax)
+    if (prm.chunk % (32 * kSplitWaves) != 0 || (prm.mode == kRefine && prm.chunk / kSplitWaves > kSplitSpanMax))
         return hipErrorInvalidValue;
     if (H == 64 && D == 128)
         return launch_split_score_t<64, 128>(prm, grid, stream);
@@ -820,6 +916,7 @@ hipError_t launch_split_score(int H, int D, const SplitScoreParams &prm, dim3 gr
 
 hipError_t launch_split_select(const SplitSelectParams &prm, hipStream_t stream)
 {
+
     hipLaunchKernelGGL(split_select_kernel, dim3((unsigned)prm.nrows, (unsigned)prm.B),
                        dim3(kSelectThreads), 0, stream, prm);
     return hipGetLastError();

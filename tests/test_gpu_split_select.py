@@ -79,6 +79,23 @@ def test_sample_overestimates():
     assert idx[0, 0].tolist() == list(range(1, 2 * 2048, 2))
 
 
+def test_sample_chunks_overestimate():
+    # the positions of the sampled chunks (128 chunks of 64, spread evenly)
+    # score high and fall with the position, all others low: the sample puts
+    # the threshold above the k-th score of the row
+    L, k = 20000, 2048
+    ns = min(L // 2, 8192) // 64 * 64
+    nch = ns // 64
+    hot = np.concatenate([np.arange(c * L // nch, c * L // nch + 64) for c in range(nch)])
+    bits = np.full(L, 0x3C00, np.int64)
+    bits[hot] = 0x4700 - np.arange(len(hot))
+    Q, W, K = keyed(bits, 1)
+    res, idx, _ = check_dense(Q, W, K, k)
+    assert_ok(res)
+    assert res.exact == res.rows
+    assert idx[0, 0].tolist() == sorted(hot[:k].tolist())
+
+
 @pytest.mark.parametrize("plateau", [1, 8, 300])
 def test_plateaus_long_row(plateau):
     L = 30000
