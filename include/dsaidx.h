@@ -129,6 +129,56 @@ int indexer_pivot_refine(const void *Q, const float *W, const void *K,
                          int32_t *out_idx, float *out_score, int32_t *out_cand,
                          void *ws, size_t ws_bytes, hipStream_t stream);
 
+/*
+ * Batches of requests of different lengths (PIVOT paper, Method: query
+ * groups are contiguous, never cross a request boundary, and the last group
+ * of a request may be smaller), with an optional guard for short prefixes
+ * (Results: PIVOT falls back to a dense scan for short groups so that it is
+ * never slower than the dense indexer).
+ *
+ *   L, q_len  host arrays of B entries: request b has L[b] keys and its
+ *             queries are its last q_len[b] positions (1 <= q_len[b] <= L[b]
+ *             < 2^31). The arrays are read during the call only.
+ *   Packed layouts (device memory, requests in order, no padding):
+ *     Q        [sum q_len][H_I][d_I]  bf16
+ *     W        [sum q_len][H_I]       fp32
+ *     K        [sum L][d_I]           bf16
+ *     out_idx  [sum q_len][k]         int32
+ *     out_score[sum q_len][k]         fp32, may be NULL
+ *     out_cand [sum G][c]             int32, may be NULL; G[b] = ceil(q_len[b] / g)
+ *   guard     a group whose last position t_last satisfies t_last + 1 <= guard
+ *             (its whole causal prefix holds at most `guard` keys) is scored
+ *             densely: each of its rows receives its dense top-k, and its
+ *             candidate row, if requested, is filled with -1. guard = 0 turns
+ *             the guard off. For Refine, any guard <= c leaves the results
+ *             unchanged (a group whose prefix fits in c keys has every key as
+ *             a candidate, so Refine equals the dense indexer there) and only
+ *             skips work; for Reuse the guarded rows change from the shared
+ *             proxy selection to each row's own dense selection.
+ *   Everything else (ranking, output order, padding, supported shapes,
+ *   ownership, errors) is as for the uniform entry points. The call uploads
+ *   B small request descriptors into ws through kernel launches on `stream`.
+ */
+size_t indexer_varlen_workspace_bytes(int mode, int B, const int64_t *L, const int64_t *q_len,
+                                      int H_I, int d_I, int g, int c, int k, int64_t guard);
+
+int indexer_dense_varlen(const void *Q, const float *W, const void *K,
+                         int B, const int64_t *L, const int64_t *q_len, int H_I, int d_I, int k,
+                         int32_t *out_idx, float *out_score,
+                         void *ws, size_t ws_bytes, hipStream_t stream);
+
+int indexer_pivot_reuse_varlen(const void *Q, const float *W, const void *K,
+                               int B, const int64_t *L, const int64_t *q_len, int H_I, int d_I,
+                               int g, int c, int k, int64_t guard,
+                               int32_t *out_idx, float *out_score, int32_t *out_cand,
+                               void *ws, size_t ws_bytes, hipStream_t stream);
+
+int indexer_pivot_refine_varlen(const void *Q, const float *W, const void *K,
+                                int B, const int64_t *L, const int64_t *q_len, int H_I, int d_I,
+                                int g, int c, int k, int64_t guard,
+                                int32_t *out_idx, float *out_score, int32_t *out_cand,
+                                void *ws, size_t ws_bytes, hipStream_t stream);
+
 /* Message of the last non-OK return on the calling thread ("" if none). */
 const char *indexer_last_error(void);
 

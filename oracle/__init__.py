@@ -171,3 +171,40 @@ def pivot_groups(Q, W, K, g, c, k, groups, cand_in=None, lib=None):
         _p(out["reuse_score"]), _p(out["refine"]), _p(out["refine_score"])),
         "pivot_groups")
     return out
+
+
+# ------------------------------------------------- batches of requests
+def request_offsets(L, q_len, g=1):
+    """Per request of a packed batch: (first key row, first query row, first
+    group), requests in order and without padding; a group never spans two
+    requests (PIVOT paper, Method: the last group of a request may be
+    smaller)."""
+    key_off, q_off, g_off = [], [], []
+    kk = qq = gg = 0
+    for Lb, qb in zip(L, q_len):
+        key_off.append(kk)
+        q_off.append(qq)
+        g_off.append(gg)
+        kk += int(Lb)
+        qq += int(qb)
+        gg += -(-int(qb) // g)
+    return key_off, q_off, g_off
+
+
+def guarded_groups(L, q_len, g, guard):
+    """Leading groups of one request that the guard scores densely.
+
+    PIVOT paper, Results (the guardrail: PIVOT falls back to a dense scan for
+    short groups). Reading taken: group m, whose last position is
+    t_last = L - q_len + min((m + 1) g, q_len) - 1, is guarded when its whole
+    causal prefix, t_last + 1 keys, is at most ``guard``; guard = 0 guards
+    nothing. t_last grows with m, so the guarded groups are a prefix.
+    """
+    off = L - q_len
+    n = 0
+    for m in range(-(-q_len // g)):
+        if off + min((m + 1) * g, q_len) <= guard:
+            n += 1
+        else:
+            break
+    return n

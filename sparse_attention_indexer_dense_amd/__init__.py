@@ -3,12 +3,15 @@ and PIVOT Reuse/Refine on AMD MI355X (gfx950).
 
 This module only marshals arguments: the functions named like the C entry
 points (``indexer_dense``, ``indexer_pivot_reuse``, ``indexer_pivot_refine``,
-``indexer_workspace_bytes``, ``indexer_last_error``, ``indexer_version``) take
-raw device pointers and sizes, exactly as the C functions do. ``dense``,
-``pivot_reuse`` and ``pivot_refine`` take torch tensors on the GPU, allocate
-the outputs and the workspace with torch (device memory and the current stream
-are the only things torch provides) and call the same entry points. Every step
-of the computation runs in the library's HIP kernels; there is no other path.
+their ``*_varlen`` forms for batches of requests of different lengths,
+``indexer_workspace_bytes``, ``indexer_varlen_workspace_bytes``,
+``indexer_last_error``, ``indexer_version``) take raw device pointers and
+sizes, exactly as the C functions do. ``dense``, ``pivot_reuse``,
+``pivot_refine`` and their ``*_varlen`` forms take torch tensors on the GPU,
+allocate the outputs and the workspace with torch (device memory and the
+current stream are the only things torch provides) and call the same entry
+points. Every step of the computation runs in the library's HIP kernels;
+there is no other path.
 """
 from __future__ import annotations
 
@@ -21,7 +24,9 @@ LIB_PATH = os.path.join(_HERE, "libdsaidx.so")
 DENSE, REUSE, REFINE = 0, 1, 2
 STATUS = {0: "OK", 1: "EINVAL", 2: "EUNSUPPORTED", 3: "EWORKSPACE", 4: "EHIP"}
 EXPORTS = ("indexer_workspace_bytes", "indexer_dense", "indexer_pivot_reuse",
-           "indexer_pivot_refine", "indexer_last_error", "indexer_version")
+           "indexer_pivot_refine", "indexer_varlen_workspace_bytes", "indexer_dense_varlen",
+           "indexer_pivot_reuse_varlen", "indexer_pivot_refine_varlen", "indexer_last_error",
+           "indexer_version")
 
 
 class IndexerError(RuntimeError):
@@ -49,6 +54,13 @@ def load(path: str = LIB_PATH):
     lib.indexer_dense.restype = i32
     for f in (lib.indexer_pivot_reuse, lib.indexer_pivot_refine):
         f.argtypes = [P, P, P, i32, i64, i64, i32, i32, i32, i32, i32, P, P, P, P, sz, P]
+        f.restype = i32
+    lib.indexer_varlen_workspace_bytes.argtypes = [i32, i32, P, P, i32, i32, i32, i32, i32, i64]
+    lib.indexer_varlen_workspace_bytes.restype = sz
+    lib.indexer_dense_varlen.argtypes = [P, P, P, i32, P, P, i32, i32, i32, P, P, P, sz, P]
+    lib.indexer_dense_varlen.restype = i32
+    for f in (lib.indexer_pivot_reuse_varlen, lib.indexer_pivot_refine_varlen):
+        f.argtypes = [P, P, P, i32, P, P, i32, i32, i32, i32, i32, i64, P, P, P, P, sz, P]
         f.restype = i32
     lib.indexer_last_error.argtypes = []
     lib.indexer_last_error.restype = ctypes.c_char_p
@@ -78,6 +90,27 @@ def indexer_pivot_refine(Q, W, K, B, L, q_len, H_I, d_I, g, c, k, out_idx, out_s
                          ws, ws_bytes, stream):
     return load().indexer_pivot_refine(Q, W, K, B, L, q_len, H_I, d_I, g, c, k, out_idx, out_score,
                                        out_cand, ws, ws_bytes, stream)
+
+
+def indexer_varlen_workspace_bytes(mode, B, L, q_len, H_I, d_I, g, c, k, guard):
+    return load().indexer_varlen_workspace_bytes(mode, B, L, q_len, H_I, d_I, g, c, k, guard)
+
+
+def indexer_dense_varlen(Q, W, K, B, L, q_len, H_I, d_I, k, out_idx, out_score, ws, ws_bytes, stream):
+    return load().indexer_dense_varlen(Q, W, K, B, L, q_len, H_I, d_I, k, out_idx, out_score, ws,
+                                       ws_bytes, stream)
+
+
+def indexer_pivot_reuse_varlen(Q, W, K, B, L, q_len, H_I, d_I, g, c, k, guard, out_idx, out_score,
+                               out_cand, ws, ws_bytes, stream):
+    return load().indexer_pivot_reuse_varlen(Q, W, K, B, L, q_len, H_I, d_I, g, c, k, guard, out_idx,
+                                             out_score, out_cand, ws, ws_bytes, stream)
+
+
+def indexer_pivot_refine_varlen(Q, W, K, B, L, q_len, H_I, d_I, g, c, k, guard, out_idx, out_score,
+                                out_cand, ws, ws_bytes, stream):
+    return load().indexer_pivot_refine_varlen(Q, W, K, B, L, q_len, H_I, d_I, g, c, k, guard, out_idx,
+                                              out_score, out_cand, ws, ws_bytes, stream)
 
 
 def indexer_last_error():
@@ -172,3 +205,67 @@ def pivot_reuse(Q, W, K, g, k, c=0, scores=True, cand=False, ws=None, out=None):
 def pivot_refine(Q, W, K, g, c, k, scores=True, cand=False, ws=None, out=None):
     """PIVOT-Refine: (idx, score or None, cand [B,G,c] or None)."""
     return _run(REFINE, Q, W, K, k, g=g, c=c, scores=scores, cand=cand, ws=ws, out=out)
+
+
+# ------------------------------------------------------ variable-length batches
+def _varlen_shapes(Q, W, K, L, q_len):
+    import torch
+    if Q.dtype != torch.bfloat16 or K.dtype != torch.bfloat16 or W.dtype != torch.float32:
+        raise TypeError("Q and K must be bf16, W fp32")
+    if not (Q.is_cuda and W.is_cuda and K.is_cuda):
+        raise ValueError("Q, W and K must be GPU tensors")
+    if Q.dim() != 3 or W.dim() != 2 or K.dim() != 2:
+        raise ValueError("expected packed Q [sum q_len, H, d], W [sum q_len, H], K [sum L, d]")
+    for t in (Q, W, K):
+        if not t.is_contiguous():
+            raise ValueError("Q, W and K must be contiguous")
+    L = [int(x) for x in L]
+    q_len = [int(x) for x in q_len]
+    if len(L) != len(q_len) or not L:
+        raise ValueError("L and q_len must list the same, nonzero number of requests")
+    nq, H, d = Q.shape
+    if nq != sum(q_len) or K.shape[0] != sum(L) or K.shape[1] != d or tuple(W.shape) != (nq, H):
+        raise ValueError("packed shapes do not match the request lengths")
+    arr = ctypes.c_int64 * len(L)
+    return len(L), arr(*L), arr(*q_len), H, d
+
+
+def _run_varlen(mode, Q, W, K, L, q_len, k, g=1, c=0, guard=0, scores=True, cand=False, ws=None):
+    import torch
+    B, La, qa, H, d = _varlen_shapes(Q, W, K, L, q_len)
+    dev = Q.device
+    need = indexer_varlen_workspace_bytes(mode, B, La, qa, H, d, g, c, k, guard)
+    wsb = (ws or _default_ws).get(need, dev)
+    nq = Q.shape[0]
+    out_idx = torch.empty((nq, k), dtype=torch.int32, device=dev)
+    out_score = torch.empty((nq, k), dtype=torch.float32, device=dev) if scores else None
+    ng = sum((int(x) + g - 1) // g for x in q_len)
+    out_cand = torch.empty((ng, c), dtype=torch.int32, device=dev) if cand else None
+    stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+    if mode == DENSE:
+        rc = indexer_dense_varlen(_ptr(Q), _ptr(W), _ptr(K), B, La, qa, H, d, k, _ptr(out_idx),
+                                  _ptr(out_score), _ptr(wsb), wsb.numel(), stream)
+    else:
+        f = indexer_pivot_reuse_varlen if mode == REUSE else indexer_pivot_refine_varlen
+        rc = f(_ptr(Q), _ptr(W), _ptr(K), B, La, qa, H, d, g, c, k, guard, _ptr(out_idx),
+               _ptr(out_score), _ptr(out_cand), _ptr(wsb), wsb.numel(), stream)
+    _check(rc)
+    return out_idx, out_score, out_cand
+
+
+def dense_varlen(Q, W, K, L, q_len, k, scores=True, ws=None):
+    """Dense indexer over packed requests: (idx [sum q_len, k], score or None)."""
+    i, s, _ = _run_varlen(DENSE, Q, W, K, L, q_len, k, scores=scores, ws=ws)
+    return i, s
+
+
+def pivot_reuse_varlen(Q, W, K, L, q_len, g, k, c=0, guard=0, scores=True, cand=False, ws=None):
+    """PIVOT-Reuse over packed requests: (idx, score or None, cand [sum G, c] or None)."""
+    return _run_varlen(REUSE, Q, W, K, L, q_len, k, g=g, c=c, guard=guard, scores=scores,
+                       cand=cand, ws=ws)
+
+
+def pivot_refine_varlen(Q, W, K, L, q_len, g, c, k, guard=0, scores=True, cand=False, ws=None):
+    """PIVOT-Refine over packed requests: (idx, score or None, cand [sum G, c] or None)."""
+    return _run_varlen(REFINE, Q, W, K, L, q_len, k, g=g, c=c, guard=guard, scores=scores,
+                       cand=cand, ws=ws)

@@ -16,6 +16,7 @@
 #include <algorithm>
 #include <cstdio>
 #include <string>
+#include <vector>
 
 #include "../../include/dsaidx.h"
 #include "kernels.h"
@@ -107,58 +108,191 @@ int scan_grid(int H, int D, int NW, int64_t nblocks)
     return (int)std::max<int64_t>(grid, 1);
 }
 
-// Workspace layout of one call.
-struct Plan {
-    int mode;
-    int64_t G;
-    bool split_scan, split_refine;
-    int nw_scan, nw_refine;
-    int cap_scan, cap_refine;
-    int sel, sel2;
-    size_t off_proxy_q, off_proxy_w, off_cand, off_slots, off_scores, total;
+// ------------------------------------------------------------------ batches
+// A batch of requests: uniform (B requests of L keys and q_len queries, no
+// descriptors: the kernels derive each request's geometry) or of variable
+// length (per-request descriptors uploaded to the workspace). A request's
+// groups never reach into another request. `guard` sends the groups whose
+// causal prefix (t_last + 1 keys) is at most guard keys to the dense pass.
+struct Batch {
+    int B = 0;
+    bool varlen = false;
+    std::vector<ReqDesc> req;  // varlen only
+    int64_t L = 0, q_len = 0;  // uniform values; varlen: the largest request's
+    int64_t m0 = 0;            // uniform: guarded groups per request
+    int64_t g = 1;
+    int64_t total_q = 0, total_G = 0, total_keys = 0;
+    int64_t max_G = 0;
+    int64_t max_dense_rows = 0;    // PIVOT: rows of guarded groups (largest request)
+    int64_t max_pivot_groups = 0;  // PIVOT: unguarded groups (largest request)
+    int64_t max_refine_rows = 0;   // PIVOT: rows of unguarded groups (largest request)
 };
 
-// Fills `pl`; returns DSAIDX_OK or an error status (message set).
-int make_plan(int mode, int B, int64_t L, int64_t q_len, int H, int D, int64_t g, int64_t c,
-              int64_t k, bool have_cand, Plan &pl)
+// Groups of a request whose causal prefix holds at most `guard` keys: group m
+// ends at position off + min((m + 1) g, q_len) - 1.
+int64_t guarded_groups(int64_t L, int64_t q_len, int64_t g, int64_t guard)
+{
+    const int64_t G = ceil_div(q_len, g);
+    if (guard >= L)
+        return G;
+    const int64_t off = L - q_len;
+    if (guard < off + std::min(g, q_len))
+        return 0;
+    return std::min<int64_t>((guard - off) / g, G - 1);
+}
+
+void finish_batch(Batch &b, const int64_t *Ls, const int64_t *qs, int64_t guard)
+{
+    b.total_q = b.total_G = b.total_keys = 0;
+    b.max_G = b.max_dense_rows = b.max_pivot_groups = b.max_refine_rows = 0;
+    for (int i = 0; i < b.B; ++i) {
+        const int64_t L = Ls ? Ls[i] : b.L, q = qs ? qs[i] : b.q_len;
+        const int64_t G = ceil_div(q, b.g);
+        const int64_t m0 = guarded_groups(L, q, b.g, guard);
+        const int64_t rg = std::min(m0 * b.g, q);
+        if (b.varlen) {
+            ReqDesc d;
+            d.key_off = b.total_keys;
+            d.q_off = b.total_q;
+            d.g_off = b.total_G;
+            d.L = L;
+            d.q_len = q;
+            d.m0 = m0;
+            b.req.push_back(d);
+        } else {
+            b.m0 = m0;
+        }
+        b.total_keys += L;
+        b.total_q += q;
+        b.total_G += G;
+        b.max_G = std::max(b.max_G, G);
+        b.max_dense_rows = std::max(b.max_dense_rows, rg);
+        b.max_pivot_groups = std::max(b.max_pivot_groups, G - m0);
+        b.max_refine_rows = std::max(b.max_refine_rows, q - rg);
+    }
+}
+
+int check_sizes(int64_t L, int64_t q_len, const char *what, int i)
+{
+    if (L < 1 || L >= (int64_t)INT32_MAX)
+        return fail(DSAIDX_EINVAL, "%s%d: L=%lld must be in [1, 2^31-1)", what, i, (long long)L);
+    if (q_len < 1 || q_len > L)
+        return fail(DSAIDX_EINVAL, "%s%d: q_len=%lld must be in [1, L=%lld]", what, i, (long long)q_len,
+                    (long long)L);
+    return DSAIDX_OK;
+}
+
+int uniform_batch(int B, int64_t L, int64_t q_len, int64_t g, Batch &b)
 {
     if (B < 1 || B > 65535)
         return fail(DSAIDX_EINVAL, "B=%d must be in [1, 65535]", B);
-    if (L < 1 || L >= (int64_t)INT32_MAX)
-        return fail(DSAIDX_EINVAL, "L=%lld must be in [1, 2^31-1)", (long long)L);
-    if (q_len < 1 || q_len > L)
-        return fail(DSAIDX_EINVAL, "q_len=%lld must be in [1, L=%lld]", (long long)q_len, (long long)L);
+    int s = check_sizes(L, q_len, "request ", 0);
+    if (s != DSAIDX_OK)
+        return s;
+    b = Batch{};
+    b.B = B;
+    b.L = L;
+    b.q_len = q_len;
+    b.g = g;
+    finish_batch(b, nullptr, nullptr, 0);
+    return DSAIDX_OK;
+}
+
+int varlen_batch(int B, const int64_t *L, const int64_t *q_len, int64_t g, int64_t guard, Batch &b)
+{
+    if (B < 1 || B > 65535)
+        return fail(DSAIDX_EINVAL, "B=%d must be in [1, 65535]", B);
+    if (!L || !q_len)
+        return fail(DSAIDX_EINVAL, "L and q_len (host arrays of B lengths) must not be NULL");
+    if (guard < 0)
+        return fail(DSAIDX_EINVAL, "guard=%lld must be >= 0", (long long)guard);
+    b = Batch{};
+    b.B = B;
+    b.varlen = true;
+    b.g = g;
+    for (int i = 0; i < B; ++i) {
+        const int s = check_sizes(L[i], q_len[i], "request ", i);
+        if (s != DSAIDX_OK)
+            return s;
+        b.L = std::max(b.L, L[i]);
+        b.q_len = std::max(b.q_len, q_len[i]);
+    }
+    b.req.reserve(B);
+    finish_batch(b, L, q_len, guard);
+    if (b.total_keys >= ((int64_t)1 << 40) || b.total_q >= ((int64_t)1 << 40))
+        return fail(DSAIDX_EINVAL, "batch too large");
+    return DSAIDX_OK;
+}
+
+// ------------------------------------------------------------------ plans
+// Workspace layout of one call. The stages of a call run one after the
+// other on the stream, so the scan buffers or score rows of the dense pass,
+// the proxy scan and Refine share one region.
+struct Plan {
+    int mode;
+    bool dense_pass, pivot_pass;      // PIVOT: some groups guarded / unguarded
+    bool split_dense, split_scan, split_refine;
+    int nw_scan, nw_refine;
+    int cap_dense, cap_scan, cap_refine;
+    int sel, sel2;
+    size_t off_desc, off_proxy_q, off_proxy_w, off_cand, off_work, total;
+};
+
+int check_common(int H, int D, int64_t k)
+{
     if (k < 1 || k > kMaxSel)
         return fail(DSAIDX_EINVAL, "k=%lld must be in [1, 2^20]", (long long)k);
     if (!supported(H, D))
         return fail(DSAIDX_EUNSUPPORTED, "(H_I, d_I) = (%d, %d) has no kernel; supported: (64, 128), (4, 32)", H, D);
+    return DSAIDX_OK;
+}
+
+size_t scan_bytes(int H, int D, int NW, int cap)
+{
+    return (size_t)scan_slots(H, D, NW) * NW * cap * sizeof(Entry);
+}
+
+// Fills `pl`; returns DSAIDX_OK or an error status (message set).
+int make_plan(int mode, const Batch &b, int H, int D, int64_t c, int64_t k, bool have_cand, Plan &pl)
+{
+    int s = check_common(H, D, k);
+    if (s != DSAIDX_OK)
+        return s;
     pl = Plan{};
     pl.mode = mode;
     size_t off = 0;
+    if (b.varlen) {
+        pl.off_desc = off;
+        off += align_up((size_t)b.B * sizeof(ReqDesc));
+    }
+    const int64_t L = b.L;
+    pl.nw_scan = 8;
     if (mode == DSAIDX_DENSE) {
-        pl.split_scan = q_len <= kSplitRowsMax;
+        pl.dense_pass = true;
+        pl.split_dense = b.q_len <= kSplitRowsMax;
         pl.sel = (int)k;
-        pl.sel2 = 0;
-        pl.nw_scan = 8;
-        pl.cap_scan = scan_cap(k, L);
-        if (pl.split_scan) {
-            pl.off_scores = off;
-            off += align_up((size_t)B * q_len * score_row(L) * sizeof(float));
-        } else {
-            pl.off_slots = off;
-            off += align_up((size_t)scan_slots(H, D, pl.nw_scan) * pl.nw_scan * pl.cap_scan * sizeof(Entry));
-        }
+        pl.cap_dense = scan_cap(k, L);
+        pl.off_work = off;
+        off += align_up(pl.split_dense ? (size_t)b.B * b.q_len * score_row(L) * sizeof(float)
+                                       : scan_bytes(H, D, pl.nw_scan, pl.cap_dense));
         pl.total = off;
         return DSAIDX_OK;
     }
+    const int64_t g = b.g;
     if (g < 1)
         return fail(DSAIDX_EINVAL, "g=%lld must be >= 1", (long long)g);
     const bool need_c = (mode == DSAIDX_REFINE) || have_cand;
     if (need_c && (c < k || c > kMaxSel))
         return fail(DSAIDX_EINVAL, "c=%lld must be in [k=%lld, 2^20]", (long long)c, (long long)k);
-    pl.G = ceil_div(q_len, g);
-    pl.split_scan = pl.G <= kSplitRowsMax;
-    pl.nw_scan = 8;
+    pl.dense_pass = b.max_dense_rows > 0;
+    pl.pivot_pass = b.max_pivot_groups > 0;
+    size_t work = 0;
+    if (pl.dense_pass) {
+        pl.split_dense = b.max_dense_rows <= kSplitRowsMax;
+        pl.cap_dense = scan_cap(k, L);
+        work = std::max(work, pl.split_dense ? (size_t)b.B * b.max_dense_rows * score_row(L) * sizeof(float)
+                                             : scan_bytes(H, D, pl.nw_scan, pl.cap_dense));
+    }
     if (mode == DSAIDX_REUSE) {
         pl.sel = (int)(have_cand ? c : k);
         pl.sel2 = have_cand ? (int)k : 0;
@@ -166,32 +300,29 @@ int make_plan(int mode, int B, int64_t L, int64_t q_len, int H, int D, int64_t g
         pl.sel = (int)c;
         pl.sel2 = 0;
     }
-    pl.cap_scan = scan_cap(pl.sel, L);
-    pl.off_proxy_q = off;
-    off += align_up((size_t)B * pl.G * H * D * sizeof(uint16_t));
-    pl.off_proxy_w = off;
-    off += align_up((size_t)B * pl.G * H * sizeof(float));
-    if (mode == DSAIDX_REFINE && !have_cand) {
-        pl.off_cand = off;
-        off += align_up((size_t)B * pl.G * c * sizeof(int32_t));
+    if (pl.pivot_pass) {
+        pl.split_scan = b.max_pivot_groups <= kSplitRowsMax;
+        pl.cap_scan = scan_cap(pl.sel, L);
+        pl.off_proxy_q = off;
+        off += align_up((size_t)b.total_G * H * D * sizeof(uint16_t));
+        pl.off_proxy_w = off;
+        off += align_up((size_t)b.total_G * H * sizeof(float));
+        if (mode == DSAIDX_REFINE && !have_cand) {
+            pl.off_cand = off;
+            off += align_up((size_t)b.total_G * c * sizeof(int32_t));
+        }
+        work = std::max(work, pl.split_scan ? (size_t)b.B * b.max_pivot_groups * score_row(L) * sizeof(float)
+                                            : scan_bytes(H, D, pl.nw_scan, pl.cap_scan));
+        if (mode == DSAIDX_REFINE) {
+            pl.split_refine = b.max_refine_rows <= kSplitRowsMax;
+            pl.nw_refine = g <= 4 ? 4 : 8;
+            pl.cap_refine = (int)ceil_div(c + 128, 64) * 64;
+            work = std::max(work, pl.split_refine ? (size_t)b.B * b.max_refine_rows * score_row(c) * sizeof(float)
+                                                  : scan_bytes(H, D, pl.nw_refine, pl.cap_refine));
+        }
     }
-    // scan stage
-    size_t scan_bytes = pl.split_scan
-        ? (size_t)B * pl.G * score_row(L) * sizeof(float)
-        : (size_t)scan_slots(H, D, pl.nw_scan) * pl.nw_scan * pl.cap_scan * sizeof(Entry);
-    size_t refine_bytes = 0;
-    if (mode == DSAIDX_REFINE) {
-        pl.split_refine = q_len <= kSplitRowsMax;
-        pl.nw_refine = g <= 4 ? 4 : 8;
-        pl.cap_refine = (int)ceil_div(c + 128, 64) * 64;
-        refine_bytes = pl.split_refine
-            ? (size_t)B * q_len * score_row(c) * sizeof(float)
-            : (size_t)scan_slots(H, D, pl.nw_refine) * pl.nw_refine * pl.cap_refine * sizeof(Entry);
-    }
-    // the scan's buffers/scores and Refine's are used one after the other
-    pl.off_slots = off;
-    pl.off_scores = off;
-    off += align_up(std::max(scan_bytes, refine_bytes));
+    pl.off_work = off;
+    off += align_up(work);
     pl.total = off;
     return DSAIDX_OK;
 }
@@ -229,43 +360,57 @@ int64_t split_chunk(int64_t rows_total, int64_t npos, bool list)
     return per_wave * kSplitWaves;
 }
 
-// Score + select `nrows` rows per batch item with the split-key kernels.
-int run_split(int mode, const uint16_t *Q, const float *W, const uint16_t *K, const int32_t *cand, int B,
-              int64_t L, int64_t q_len, int64_t g, int64_t c, int64_t G, int64_t nrows, int64_t rowlen,
-              int H, int D, int sel, int sel2, int32_t *o1, float *s1, int o1_members, int32_t *o2, float *s2,
-              float *scores, hipStream_t stream)
+// Everything a launch needs to know about the batch and its pass.
+struct Pass {
+    const Batch *b;
+    const ReqDesc *req;  // device descriptors (varlen) or nullptr
+    int64_t c;
+    int guard_rows;      // dense pass over the rows of guarded groups
+};
+
+// Score + select `nrows` rows per request with the split-key kernels.
+int run_split(int mode, const Pass &ps, const uint16_t *Q, const float *W, const uint16_t *K, const int32_t *cand,
+              int64_t nrows, int64_t rowlen, int H, int D, int sel, int sel2, int32_t *o1, float *s1,
+              int o1_members, int32_t *o2, float *s2, float *scores, hipStream_t stream)
 {
+    const Batch &b = *ps.b;
     SplitScoreParams sp{};
     sp.Q = Q;
     sp.W = W;
     sp.K = K;
     sp.cand = cand;
+    sp.req = ps.req;
     sp.mode = mode;
-    sp.B = B;
-    sp.L = L;
-    sp.q_len = q_len;
-    sp.g = g;
-    sp.c = c;
-    sp.G = G;
+    sp.B = b.B;
+    sp.L = b.L;
+    sp.q_len = b.q_len;
+    sp.g = (mode == kDense && !ps.guard_rows) ? 1 : b.g;
+    sp.c = ps.c;
+    sp.G = ceil_div(b.q_len, sp.g);
+    sp.m0 = (mode == kDense && !ps.guard_rows) ? 0 : b.m0;
+    sp.guard_rows = ps.guard_rows;
     sp.nrows = nrows;
     sp.rowlen = rowlen;
-    const int64_t npos_max = (mode == kRefine) ? std::min<int64_t>(c, L) : L;
-    sp.chunk = split_chunk((int64_t)B * nrows, npos_max, mode == kRefine);
+    const int64_t npos_max = (mode == kRefine) ? std::min<int64_t>(ps.c, b.L) : b.L;
+    sp.chunk = split_chunk((int64_t)b.B * nrows, npos_max, mode == kRefine);
     sp.scores = scores;
-    dim3 grid((unsigned)ceil_div(npos_max, sp.chunk), (unsigned)nrows, (unsigned)B);
+    dim3 grid((unsigned)ceil_div(npos_max, sp.chunk), (unsigned)nrows, (unsigned)b.B);
     hipError_t e = launch_split_score(H, D, sp, grid, stream);
     if (e != hipSuccess)
         return hip_fail(e, "split score launch");
     SplitSelectParams ss{};
     ss.scores = scores;
     ss.cand = cand;
+    ss.req = ps.req;
     ss.mode = mode;
-    ss.B = B;
-    ss.L = L;
-    ss.q_len = q_len;
-    ss.g = g;
-    ss.c = c;
-    ss.G = G;
+    ss.B = b.B;
+    ss.L = b.L;
+    ss.q_len = b.q_len;
+    ss.g = sp.g;
+    ss.c = ps.c;
+    ss.G = sp.G;
+    ss.m0 = sp.m0;
+    ss.guard_rows = ps.guard_rows;
     ss.nrows = nrows;
     ss.rowlen = rowlen;
     ss.sel = sel;
@@ -281,28 +426,73 @@ int run_split(int mode, const uint16_t *Q, const float *W, const uint16_t *K, co
     return DSAIDX_OK;
 }
 
-ScanParams scan_base(const uint16_t *Q, const float *W, const uint16_t *K, int B, int64_t L, int64_t q_len,
-                     int64_t g, int64_t c, int64_t G)
+ScanParams scan_base(const Pass &ps, int mode, const uint16_t *Q, const float *W, const uint16_t *K)
 {
+    const Batch &b = *ps.b;
     ScanParams p{};
     p.Q = Q;
     p.W = W;
     p.K = K;
-    p.B = B;
-    p.L = L;
-    p.q_len = q_len;
-    p.g = g;
-    p.c = c;
-    p.G = G;
+    p.req = ps.req;
+    p.B = b.B;
+    p.L = b.L;
+    p.q_len = b.q_len;
+    p.g = (mode == kDense && !ps.guard_rows) ? 1 : b.g;
+    p.c = ps.c;
+    p.G = ceil_div(b.q_len, p.g);
+    p.m0 = (mode == kDense && !ps.guard_rows) ? 0 : b.m0;
+    p.guard_rows = ps.guard_rows;
     return p;
 }
 
-int run_pivot(int mode, const void *Qv, const float *W, const void *Kv, int B, int64_t L, int64_t q_len,
-              int H, int D, int64_t g, int64_t c, int64_t k, int32_t *out_idx, float *out_score,
-              int32_t *out_cand, void *ws, size_t ws_bytes, hipStream_t stream)
+// Dense top-k for the rows of every request (all rows, or those of guarded
+// groups), through the split or the scan kernels.
+int run_dense(const Plan &pl, const Pass &ps, const uint16_t *Q, const float *W, const uint16_t *K, int H, int D,
+              int64_t k, int32_t *out_idx, float *out_score, unsigned char *wsb, hipStream_t stream)
+{
+    const Batch &b = *ps.b;
+    const int64_t rows = ps.guard_rows ? b.max_dense_rows : b.q_len;
+    if (pl.split_dense)
+        return run_split(kDense, ps, Q, W, K, nullptr, rows, score_row(b.L), H, D, (int)k, 0, out_idx, out_score, 0,
+                         nullptr, nullptr, reinterpret_cast<float *>(wsb + pl.off_work), stream);
+    ScanParams p = scan_base(ps, kDense, Q, W, K);
+    p.nblk_per_batch = ceil_div(rows, pl.nw_scan);
+    p.nblocks = p.nblk_per_batch * b.B;
+    p.sel = (int)k;
+    p.sel2 = 0;
+    p.o1_idx = out_idx;
+    p.o1_score = out_score;
+    p.slots = reinterpret_cast<Entry *>(wsb + pl.off_work);
+    p.cap = pl.cap_dense;
+    hipError_t e = launch_scan_select(H, D, pl.nw_scan, kDense, p, scan_grid(H, D, pl.nw_scan, p.nblocks), stream);
+    if (e != hipSuccess)
+        return hip_fail(e, "dense scan launch");
+    return DSAIDX_OK;
+}
+
+// The request descriptors of a variable-length batch, written to the
+// workspace by a small kernel that receives them as launch arguments.
+int upload_desc(const Batch &b, ReqDesc *dst, hipStream_t stream)
+{
+    for (int i0 = 0; i0 < b.B; i0 += kDescChunk) {
+        DescChunk ch{};
+        ch.n = std::min(kDescChunk, b.B - i0);
+        ch.first = i0;
+        for (int i = 0; i < ch.n; ++i)
+            ch.d[i] = b.req[i0 + i];
+        hipError_t e = launch_set_desc(ch, dst, stream);
+        if (e != hipSuccess)
+            return hip_fail(e, "descriptor launch");
+    }
+    return DSAIDX_OK;
+}
+
+int run_pivot(int mode, const Batch &b, const void *Qv, const float *W, const void *Kv, int H, int D, int64_t c,
+              int64_t k, int32_t *out_idx, float *out_score, int32_t *out_cand, void *ws, size_t ws_bytes,
+              hipStream_t stream)
 {
     Plan pl;
-    int s = make_plan(mode, B, L, q_len, H, D, g, c, k, out_cand != nullptr, pl);
+    int s = make_plan(mode, b, H, D, c, k, out_cand != nullptr, pl);
     if (s != DSAIDX_OK)
         return s;
     s = check_ptrs(Qv, W, Kv, out_idx, out_score, out_cand, ws, pl.total);
@@ -313,21 +503,48 @@ int run_pivot(int mode, const void *Qv, const float *W, const void *Kv, int B, i
     const uint16_t *Q = static_cast<const uint16_t *>(Qv);
     const uint16_t *K = static_cast<const uint16_t *>(Kv);
     unsigned char *wsb = static_cast<unsigned char *>(ws);
+    Pass ps{&b, nullptr, c, 0};
+    if (b.varlen) {
+        ReqDesc *d = reinterpret_cast<ReqDesc *>(wsb + pl.off_desc);
+        s = upload_desc(b, d, stream);
+        if (s != DSAIDX_OK)
+            return s;
+        ps.req = d;
+    }
+    hipError_t e;
+
+    // 0. guarded groups: dense rows; no candidates
+    if (pl.dense_pass) {
+        Pass pd = ps;
+        pd.guard_rows = 1;
+        s = run_dense(pl, pd, Q, W, K, H, D, k, out_idx, out_score, wsb, stream);
+        if (s != DSAIDX_OK)
+            return s;
+        if (out_cand) {
+            e = launch_fill_guarded(ps.req, b.B, b.L, b.q_len, b.g, b.m0, b.max_G, c, out_cand, stream);
+            if (e != hipSuccess)
+                return hip_fail(e, "candidate fill launch");
+        }
+    }
+    if (!pl.pivot_pass)
+        return DSAIDX_OK;
     uint16_t *Qp = reinterpret_cast<uint16_t *>(wsb + pl.off_proxy_q);
     float *Wp = reinterpret_cast<float *>(wsb + pl.off_proxy_w);
-    const int64_t G = pl.G;
 
-    // 1. proxies
+    // 1. proxies of the unguarded groups
     PoolParams pp{};
     pp.Q = Q;
     pp.W = W;
-    pp.B = B;
-    pp.q_len = q_len;
-    pp.g = g;
-    pp.G = G;
+    pp.req = ps.req;
+    pp.B = b.B;
+    pp.L = b.L;
+    pp.q_len = b.q_len;
+    pp.g = b.g;
+    pp.m0 = b.m0;
+    pp.gmax = b.max_G;
     pp.Qp = Qp;
     pp.Wp = Wp;
-    hipError_t e = launch_pool(H, D, pp, stream);
+    e = launch_pool(H, D, pp, stream);
     if (e != hipSuccess)
         return hip_fail(e, "pool launch");
 
@@ -354,14 +571,14 @@ int run_pivot(int mode, const void *Qv, const float *W, const void *Kv, int B, i
         }
     }
     if (pl.split_scan) {
-        s = run_split(kProxy, Qp, Wp, K, nullptr, B, L, q_len, g, c, G, G, score_row(L), H, D, pl.sel, pl.sel2, o1, s1,
-                      o1_members, o2, s2, reinterpret_cast<float *>(wsb + pl.off_scores), stream);
+        s = run_split(kProxy, ps, Qp, Wp, K, nullptr, b.max_pivot_groups, score_row(b.L), H, D, pl.sel, pl.sel2, o1,
+                      s1, o1_members, o2, s2, reinterpret_cast<float *>(wsb + pl.off_work), stream);
         if (s != DSAIDX_OK)
             return s;
     } else {
-        ScanParams p = scan_base(Qp, Wp, K, B, L, q_len, g, c, G);
-        p.nblk_per_batch = ceil_div(G, pl.nw_scan);
-        p.nblocks = p.nblk_per_batch * B;
+        ScanParams p = scan_base(ps, kProxy, Qp, Wp, K);
+        p.nblk_per_batch = ceil_div(b.max_pivot_groups, pl.nw_scan);
+        p.nblocks = p.nblk_per_batch * b.B;
         p.sel = pl.sel;
         p.sel2 = pl.sel2;
         p.o1_idx = o1;
@@ -369,7 +586,7 @@ int run_pivot(int mode, const void *Qv, const float *W, const void *Kv, int B, i
         p.o1_members = o1_members;
         p.o2_idx = o2;
         p.o2_score = s2;
-        p.slots = reinterpret_cast<Entry *>(wsb + pl.off_slots);
+        p.slots = reinterpret_cast<Entry *>(wsb + pl.off_work);
         p.cap = pl.cap_scan;
         e = launch_scan_select(H, D, pl.nw_scan, kProxy, p, scan_grid(H, D, pl.nw_scan, p.nblocks), stream);
         if (e != hipSuccess)
@@ -380,23 +597,65 @@ int run_pivot(int mode, const void *Qv, const float *W, const void *Kv, int B, i
 
     // 3. Refine on the candidates
     if (pl.split_refine) {
-        return run_split(kRefine, Q, W, K, cand, B, L, q_len, g, c, G, q_len, score_row(c), H, D, (int)k, 0, out_idx,
-                         out_score, 0, nullptr, nullptr, reinterpret_cast<float *>(wsb + pl.off_scores), stream);
+        return run_split(kRefine, ps, Q, W, K, cand, b.max_refine_rows, score_row(c), H, D, (int)k, 0, out_idx,
+                         out_score, 0, nullptr, nullptr, reinterpret_cast<float *>(wsb + pl.off_work), stream);
     }
-    ScanParams p = scan_base(Q, W, K, B, L, q_len, g, c, G);
+    ScanParams p = scan_base(ps, kRefine, Q, W, K);
     p.cand = cand;
-    p.member_chunks = ceil_div(g, pl.nw_refine);
-    p.nblocks = (int64_t)B * G * p.member_chunks;
+    p.member_chunks = ceil_div(b.g, pl.nw_refine);
+    p.nblk_per_batch = b.max_pivot_groups * p.member_chunks;
+    p.nblocks = p.nblk_per_batch * b.B;
     p.sel = (int)k;
     p.sel2 = 0;
     p.o1_idx = out_idx;
     p.o1_score = out_score;
-    p.slots = reinterpret_cast<Entry *>(wsb + pl.off_slots);
+    p.slots = reinterpret_cast<Entry *>(wsb + pl.off_work);
     p.cap = pl.cap_refine;
     e = launch_scan_select(H, D, pl.nw_refine, kRefine, p, scan_grid(H, D, pl.nw_refine, p.nblocks), stream);
     if (e != hipSuccess)
         return hip_fail(e, "refine launch");
     return DSAIDX_OK;
+}
+
+int run_dense_call(const Batch &b, const void *Qv, const float *W, const void *Kv, int H, int D, int k,
+                   int32_t *out_idx, float *out_score, void *ws, size_t ws_bytes, hipStream_t stream)
+{
+    Plan pl;
+    int s = make_plan(DSAIDX_DENSE, b, H, D, 0, k, false, pl);
+    if (s != DSAIDX_OK)
+        return s;
+    s = check_ptrs(Qv, W, Kv, out_idx, out_score, nullptr, ws, pl.total);
+    if (s != DSAIDX_OK)
+        return s;
+    if (ws_bytes < pl.total)
+        return fail(DSAIDX_EWORKSPACE, "workspace of %zu bytes is below the %zu needed", ws_bytes, pl.total);
+    unsigned char *wsb = static_cast<unsigned char *>(ws);
+    Pass ps{&b, nullptr, 0, 0};
+    if (b.varlen) {
+        ReqDesc *d = reinterpret_cast<ReqDesc *>(wsb + pl.off_desc);
+        s = upload_desc(b, d, stream);
+        if (s != DSAIDX_OK)
+            return s;
+        ps.req = d;
+    }
+    return run_dense(pl, ps, static_cast<const uint16_t *>(Qv), W, static_cast<const uint16_t *>(Kv), H, D, k,
+                     out_idx, out_score, wsb, stream);
+}
+
+size_t workspace_for(int mode, const Batch &b, int H, int D, int64_t c, int64_t k)
+{
+    Plan pl;
+    // For Reuse the candidate output may or may not be requested; size for both.
+    const bool have_cand = mode == DSAIDX_REUSE && c >= k;
+    if (make_plan(mode, b, H, D, c, k, have_cand, pl) != DSAIDX_OK)
+        return 0;
+    size_t total = pl.total;
+    if (mode == DSAIDX_REUSE) {
+        Plan p2;
+        if (make_plan(mode, b, H, D, c, k, false, p2) == DSAIDX_OK)
+            total = std::max(total, p2.total);
+    }
+    return total;
 }
 
 }  // namespace
@@ -409,74 +668,107 @@ size_t indexer_workspace_bytes(int mode, int B, int64_t L, int64_t q_len, int H_
         fail(DSAIDX_EINVAL, "unknown mode %d", mode);
         return 0;
     }
-    Plan pl;
-    // For Reuse the candidate output may or may not be requested; size for both.
-    const bool have_cand = mode == DSAIDX_REUSE && c >= k;
-    if (make_plan(mode, B, L, q_len, H_I, d_I, g, c, k, have_cand, pl) != DSAIDX_OK)
+    Batch b;
+    if (uniform_batch(B, L, q_len, mode == DSAIDX_DENSE ? 1 : g, b) != DSAIDX_OK)
         return 0;
-    size_t total = pl.total;
-    if (mode == DSAIDX_REUSE) {
-        Plan p2;
-        if (make_plan(mode, B, L, q_len, H_I, d_I, g, c, k, false, p2) == DSAIDX_OK)
-            total = std::max(total, p2.total);
-    }
-    return total;
+    return workspace_for(mode, b, H_I, d_I, c, k);
 }
 
 int indexer_dense(const void *Qv, const float *W, const void *Kv, int B, int64_t L, int64_t q_len, int H_I,
                   int d_I, int k, int32_t *out_idx, float *out_score, void *ws, size_t ws_bytes,
                   hipStream_t stream)
 {
-    Plan pl;
-    int s = make_plan(DSAIDX_DENSE, B, L, q_len, H_I, d_I, 1, 0, k, false, pl);
+    Batch b;
+    int s = uniform_batch(B, L, q_len, 1, b);
     if (s != DSAIDX_OK)
         return s;
-    s = check_ptrs(Qv, W, Kv, out_idx, out_score, nullptr, ws, pl.total);
-    if (s != DSAIDX_OK)
-        return s;
-    if (ws_bytes < pl.total)
-        return fail(DSAIDX_EWORKSPACE, "workspace of %zu bytes is below the %zu needed", ws_bytes, pl.total);
-    const uint16_t *Q = static_cast<const uint16_t *>(Qv);
-    const uint16_t *K = static_cast<const uint16_t *>(Kv);
-    unsigned char *wsb = static_cast<unsigned char *>(ws);
-    if (pl.split_scan) {
-        return run_split(kDense, Q, W, K, nullptr, B, L, q_len, 1, 0, q_len, q_len, score_row(L), H_I, d_I, k, 0, out_idx,
-                         out_score, 0, nullptr, nullptr, reinterpret_cast<float *>(wsb + pl.off_scores), stream);
-    }
-    ScanParams p = scan_base(Q, W, K, B, L, q_len, 1, 0, q_len);
-    p.nblk_per_batch = ceil_div(q_len, pl.nw_scan);
-    p.nblocks = p.nblk_per_batch * B;
-    p.sel = k;
-    p.sel2 = 0;
-    p.o1_idx = out_idx;
-    p.o1_score = out_score;
-    p.slots = reinterpret_cast<Entry *>(wsb + pl.off_slots);
-    p.cap = pl.cap_scan;
-    hipError_t e = launch_scan_select(H_I, d_I, pl.nw_scan, kDense, p,
-                                      scan_grid(H_I, d_I, pl.nw_scan, p.nblocks), stream);
-    if (e != hipSuccess)
-        return hip_fail(e, "dense scan launch");
-    return DSAIDX_OK;
+    return run_dense_call(b, Qv, W, Kv, H_I, d_I, k, out_idx, out_score, ws, ws_bytes, stream);
 }
 
 int indexer_pivot_reuse(const void *Q, const float *W, const void *K, int B, int64_t L, int64_t q_len, int H_I,
                         int d_I, int g, int c, int k, int32_t *out_idx, float *out_score, int32_t *out_cand,
                         void *ws, size_t ws_bytes, hipStream_t stream)
 {
-    return run_pivot(DSAIDX_REUSE, Q, W, K, B, L, q_len, H_I, d_I, g, c, k, out_idx, out_score, out_cand, ws,
-                     ws_bytes, stream);
+    if (g < 1)
+        return fail(DSAIDX_EINVAL, "g=%d must be >= 1", g);
+    Batch b;
+    int s = uniform_batch(B, L, q_len, g, b);
+    if (s != DSAIDX_OK)
+        return s;
+    return run_pivot(DSAIDX_REUSE, b, Q, W, K, H_I, d_I, c, k, out_idx, out_score, out_cand, ws, ws_bytes, stream);
 }
 
 int indexer_pivot_refine(const void *Q, const float *W, const void *K, int B, int64_t L, int64_t q_len, int H_I,
                          int d_I, int g, int c, int k, int32_t *out_idx, float *out_score, int32_t *out_cand,
                          void *ws, size_t ws_bytes, hipStream_t stream)
 {
-    return run_pivot(DSAIDX_REFINE, Q, W, K, B, L, q_len, H_I, d_I, g, c, k, out_idx, out_score, out_cand, ws,
-                     ws_bytes, stream);
+    if (g < 1)
+        return fail(DSAIDX_EINVAL, "g=%d must be >= 1", g);
+    Batch b;
+    int s = uniform_batch(B, L, q_len, g, b);
+    if (s != DSAIDX_OK)
+        return s;
+    return run_pivot(DSAIDX_REFINE, b, Q, W, K, H_I, d_I, c, k, out_idx, out_score, out_cand, ws, ws_bytes, stream);
+}
+
+size_t indexer_varlen_workspace_bytes(int mode, int B, const int64_t *L, const int64_t *q_len, int H_I, int d_I,
+                                      int g, int c, int k, int64_t guard)
+{
+    if (mode != DSAIDX_DENSE && mode != DSAIDX_REUSE && mode != DSAIDX_REFINE) {
+        fail(DSAIDX_EINVAL, "unknown mode %d", mode);
+        return 0;
+    }
+    if (mode != DSAIDX_DENSE && g < 1) {
+        fail(DSAIDX_EINVAL, "g=%d must be >= 1", g);
+        return 0;
+    }
+    Batch b;
+    if (varlen_batch(B, L, q_len, mode == DSAIDX_DENSE ? 1 : g, mode == DSAIDX_DENSE ? 0 : guard, b) != DSAIDX_OK)
+        return 0;
+    return workspace_for(mode, b, H_I, d_I, c, k);
+}
+
+int indexer_dense_varlen(const void *Q, const float *W, const void *K, int B, const int64_t *L,
+                         const int64_t *q_len, int H_I, int d_I, int k, int32_t *out_idx, float *out_score,
+                         void *ws, size_t ws_bytes, hipStream_t stream)
+{
+    Batch b;
+    int s = varlen_batch(B, L, q_len, 1, 0, b);
+    if (s != DSAIDX_OK)
+        return s;
+    return run_dense_call(b, Q, W, K, H_I, d_I, k, out_idx, out_score, ws, ws_bytes, stream);
+}
+
+int indexer_pivot_reuse_varlen(const void *Q, const float *W, const void *K, int B, const int64_t *L,
+                               const int64_t *q_len, int H_I, int d_I, int g, int c, int k, int64_t guard,
+                               int32_t *out_idx, float *out_score, int32_t *out_cand, void *ws, size_t ws_bytes,
+                               hipStream_t stream)
+{
+    if (g < 1)
+        return fail(DSAIDX_EINVAL, "g=%d must be >= 1", g);
+    Batch b;
+    int s = varlen_batch(B, L, q_len, g, guard, b);
+    if (s != DSAIDX_OK)
+        return s;
+    return run_pivot(DSAIDX_REUSE, b, Q, W, K, H_I, d_I, c, k, out_idx, out_score, out_cand, ws, ws_bytes, stream);
+}
+
+int indexer_pivot_refine_varlen(const void *Q, const float *W, const void *K, int B, const int64_t *L,
+                                const int64_t *q_len, int H_I, int d_I, int g, int c, int k, int64_t guard,
+                                int32_t *out_idx, float *out_score, int32_t *out_cand, void *ws, size_t ws_bytes,
+                                hipStream_t stream)
+{
+    if (g < 1)
+        return fail(DSAIDX_EINVAL, "g=%d must be >= 1", g);
+    Batch b;
+    int s = varlen_batch(B, L, q_len, g, guard, b);
+    if (s != DSAIDX_OK)
+        return s;
+    return run_pivot(DSAIDX_REFINE, b, Q, W, K, H_I, d_I, c, k, out_idx, out_score, out_cand, ws, ws_bytes, stream);
 }
 
 const char *indexer_last_error(void) { return g_last_error.c_str(); }
 
-const char *indexer_version(void) { return "dsaidx 0.1.0 gfx950"; }
+const char *indexer_version(void) { return "dsaidx 0.2.0 gfx950"; }
 
 }  // extern "C"

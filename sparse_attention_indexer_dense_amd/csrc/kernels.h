@@ -10,6 +10,57 @@ namespace dsaidx {
 
 enum { kDense = 0, kProxy = 1, kRefine = 2 };
 
+// One request of a variable-length batch (a device array in the workspace).
+// A group never spans two requests.
+struct ReqDesc {
+    int64_t key_off;  // first row of the request's keys in K
+    int64_t q_off;    // first row of its queries in Q and W, and of its output rows
+    int64_t g_off;    // first of its groups in the proxy and candidate rows
+    int64_t L;        // keys
+    int64_t q_len;    // queries: the last q_len positions
+    int64_t m0;       // groups [0, m0) are guarded: their rows are scored as dense rows
+};
+
+// Geometry of request bi: from the descriptor array, or that of a uniform
+// batch (B requests of L keys and q_len queries, m0 guarded groups each).
+struct Req {
+    int64_t key_off, q_off, g_off, L, q_len, G, m0;
+};
+
+__device__ __forceinline__ Req request_of(const ReqDesc *req, int bi, int64_t L, int64_t q_len, int64_t g,
+                                          int64_t m0)
+{
+    Req r;
+    if (req) {
+        const ReqDesc d = req[bi];
+        r.key_off = d.key_off;
+        r.q_off = d.q_off;
+        r.g_off = d.g_off;
+        r.L = d.L;
+        r.q_len = d.q_len;
+        r.m0 = d.m0;
+    } else {
+        r.key_off = (int64_t)bi * L;
+        r.q_off = (int64_t)bi * q_len;
+        r.g_off = (int64_t)bi * ((q_len + g - 1) / g);
+        r.L = L;
+        r.q_len = q_len;
+        r.m0 = m0;
+    }
+    r.G = (r.q_len + g - 1) / g;
+    return r;
+}
+
+// Rows a dense pass covers in a request: all of them, or (guard_rows) those
+// of its guarded groups.
+__device__ __forceinline__ int64_t dense_rows(const Req &r, int64_t g, int guard_rows)
+{
+    if (!guard_rows)
+        return r.q_len;
+    const int64_t x = r.m0 * g;
+    return x < r.q_len ? x : r.q_len;
+}
+
 // One kept (score, key index) pair of a row's candidate buffer.
 struct Entry {
     float score;
@@ -22,10 +73,13 @@ struct ScanParams {
     const float *W;        // matching weights
     const uint16_t *K;     // keys [B][L][D]
     const int32_t *cand;   // kRefine: candidate lists [B][G][c]
+    const ReqDesc *req;    // requests of a variable-length batch (nullptr: uniform)
     int B;
-    int64_t L, q_len;
+    int64_t L, q_len;      // uniform batch: keys and queries per request
     int64_t g, c, G;
-    int64_t nblk_per_batch;  // kDense/kProxy: row blocks per batch item
+    int64_t m0;            // uniform batch: guarded groups per request
+    int guard_rows;        // kDense: only the rows of guarded groups
+    int64_t nblk_per_batch;  // blocks per request (the largest request's count)
     int64_t nblocks;         // total blocks
     int64_t member_chunks;   // kRefine: member chunks per group
     int sel, sel2;           // selection sizes (sel2 = 0: none)
@@ -41,10 +95,12 @@ struct ScanParams {
 struct PoolParams {
     const uint16_t *Q;
     const float *W;
+    const ReqDesc *req;
     int B;
-    int64_t q_len, g, G;
-    uint16_t *Qp;  // [B][G][H][D]
-    float *Wp;     // [B][G][H]
+    int64_t L, q_len, g, m0;
+    int64_t gmax;  // groups of the largest request
+    uint16_t *Qp;  // [groups][H][D]
+    float *Wp;     // [groups][H]
 };
 
 // Split-key scoring for few rows (split.hip): every workgroup scores a chunk
@@ -54,10 +110,12 @@ struct SplitScoreParams {
     const float *W;
     const uint16_t *K;
     const int32_t *cand;  // kRefine: candidate lists [B][G][c]
+    const ReqDesc *req;
     int mode;
     int B;
-    int64_t L, q_len, g, c, G;
-    int64_t nrows;        // score rows per batch item
+    int64_t L, q_len, g, c, G, m0;
+    int guard_rows;
+    int64_t nrows;        // score rows per batch item (the largest request's count)
     int64_t rowlen;       // positions per score row (L, or c for kRefine)
     int64_t chunk;        // positions per workgroup
     float *scores;        // [B][nrows][rowlen]
@@ -66,9 +124,11 @@ struct SplitScoreParams {
 struct SplitSelectParams {
     const float *scores;
     const int32_t *cand;
+    const ReqDesc *req;
     int mode;
     int B;
-    int64_t L, q_len, g, c, G;
+    int64_t L, q_len, g, c, G, m0;
+    int guard_rows;
     int64_t nrows, rowlen;
     int sel, sel2;
     int32_t *o1_idx;
@@ -82,7 +142,18 @@ constexpr int kSplitWaves = 4;
 constexpr int kSplitSpanMax = 1024;  // key positions one wave of split_score_kernel covers
 constexpr int kSelectThreads = 1024;
 
+// Request descriptors travel to the workspace as launch arguments, in chunks.
+constexpr int kDescChunk = 24;
+struct DescChunk {
+    int n, first;
+    ReqDesc d[kDescChunk];
+};
+
 size_t scan_lds_bytes(int H, int D, int NW);
+hipError_t launch_set_desc(const DescChunk &ch, ReqDesc *dst, hipStream_t stream);
+// Candidate rows [groups][c] of guarded groups (not computed) set to -1.
+hipError_t launch_fill_guarded(const ReqDesc *req, int B, int64_t L, int64_t q_len, int64_t g, int64_t m0,
+                               int64_t gmax, int64_t c, int32_t *cand, hipStream_t stream);
 hipError_t launch_scan_select(int H, int D, int NW, int mode, const ScanParams &prm, int grid,
                               hipStream_t stream);
 hipError_t launch_pool(int H, int D, const PoolParams &prm, hipStream_t stream);

@@ -237,52 +237,59 @@ struct WaveRow {
 };
 
 struct BlockKeys {
-    const uint16_t *Kb;   // keys of this batch item
+    const uint16_t *Kb;   // keys of this request
     const int32_t *list;  // candidate list (kRefine) or nullptr (prefix)
-    int nkeys;            // list length, or number of prefix keys (< 2^31)
+    int nkeys;            // list length, or number of prefix keys (< 2^31); 0: idle block
+    int L;                // keys of the request
 };
 
+// Block j of a launch: request j % B, and the (j / B)-th of that request's
+// blocks, longest first. Requests with fewer blocks than the largest one
+// leave the remaining ones idle (no rows, no keys).
 template <int H, int D, int NW, int MODE>
 __device__ __forceinline__ void plan_block(const ScanParams &p, int64_t j, int wave,
                                            WaveRow &wr, BlockKeys &bk)
 {
     const int bi = (int)(j % p.B);
     const int64_t jj = j / p.B;
-    const int64_t off = p.L - p.q_len;  // position of query row 0
+    const Req rq = request_of(p.req, bi, p.L, p.q_len, p.g, p.m0);
+    const int64_t off = rq.L - rq.q_len;  // position of query row 0
     wr.o2 = nullptr;
     wr.s2 = nullptr;
     wr.fan2 = 0;
+    bk.Kb = p.K + rq.key_off * D;
+    bk.L = (int)rq.L;
     if (MODE == kDense) {
-        const int64_t rb = p.nblk_per_batch - 1 - jj;
+        const int64_t rows = dense_rows(rq, p.g, p.guard_rows);
+        const int64_t rb = (rows + NW - 1) / NW - 1 - jj;
         const int64_t r = rb * NW + wave;
-        const int64_t rlast = (rb * NW + NW < p.q_len ? rb * NW + NW : p.q_len) - 1;
-        wr.valid = r < p.q_len;
-        const int64_t row = (int64_t)bi * p.q_len + r;
+        const int64_t rlast = (rb * NW + NW < rows ? rb * NW + NW : rows) - 1;
+        wr.valid = rb >= 0 && r < rows;
+        const int64_t row = rq.q_off + r;
         wr.q = p.Q + row * H * D;
         wr.w = p.W + row * H;
         wr.lim = (int)(off + r);
         wr.o1 = p.o1_idx + row * p.sel;
         wr.s1 = p.o1_score ? p.o1_score + row * p.sel : nullptr;
         wr.fan1 = 1;
-        bk.Kb = p.K + (int64_t)bi * p.L * D;
         bk.list = nullptr;
-        bk.nkeys = (int)(off + rlast + 1);
+        bk.nkeys = rb >= 0 ? (int)(off + rlast + 1) : 0;
     } else if (MODE == kProxy) {
-        const int64_t rb = p.nblk_per_batch - 1 - jj;
-        const int64_t m = rb * NW + wave;
-        const int64_t mlast = (rb * NW + NW < p.G ? rb * NW + NW : p.G) - 1;
-        wr.valid = m < p.G;
-        const int64_t grow = (int64_t)bi * p.G + m;
+        const int64_t rb = (rq.G - rq.m0 + NW - 1) / NW - 1 - jj;
+        const int64_t m = rq.m0 + rb * NW + wave;
+        const int64_t mlast = (rq.m0 + rb * NW + NW < rq.G ? rq.m0 + rb * NW + NW : rq.G) - 1;
+        wr.valid = rb >= 0 && m < rq.G;
+        const int64_t grow = rq.g_off + m;
         const int64_t r0 = m * p.g;
-        const int64_t r1 = (r0 + p.g < p.q_len) ? r0 + p.g : p.q_len;
+        const int64_t r1 = (r0 + p.g < rq.q_len) ? r0 + p.g : rq.q_len;
         wr.q = p.Q + grow * H * D;
         wr.w = p.W + grow * H;
         wr.lim = (int)(off + r1 - 1);
-        const int64_t r1last = ((mlast + 1) * p.g < p.q_len) ? (mlast + 1) * p.g : p.q_len;
-        bk.nkeys = (int)(off + r1last);
-        // output 1: candidate rows [B][G][sel] or the member rows
+        const int64_t r1last = ((mlast + 1) * p.g < rq.q_len) ? (mlast + 1) * p.g : rq.q_len;
+        bk.nkeys = rb >= 0 ? (int)(off + r1last) : 0;
+        // output 1: candidate rows [groups][sel] or the member rows
         if (p.o1_members) {
-            const int64_t row = (int64_t)bi * p.q_len + r0;
+            const int64_t row = rq.q_off + r0;
             wr.o1 = p.o1_idx + row * p.sel;
             wr.s1 = p.o1_score ? p.o1_score + row * p.sel : nullptr;
             wr.fan1 = (int)(r1 - r0);
@@ -292,21 +299,21 @@ __device__ __forceinline__ void plan_block(const ScanParams &p, int64_t j, int w
             wr.fan1 = 1;
         }
         if (p.sel2 > 0) {
-            const int64_t row = (int64_t)bi * p.q_len + r0;
+            const int64_t row = rq.q_off + r0;
             wr.o2 = p.o2_idx + row * p.sel2;
             wr.s2 = p.o2_score ? p.o2_score + row * p.sel2 : nullptr;
             wr.fan2 = (int)(r1 - r0);
         }
-        bk.Kb = p.K + (int64_t)bi * p.L * D;
         bk.list = nullptr;
     } else {  // kRefine
-        const int64_t m = p.G - 1 - jj / p.member_chunks;
+        const int64_t m = rq.G - 1 - jj / p.member_chunks;
         const int chunk = (int)(jj % p.member_chunks);
+        const bool live = m >= rq.m0;
         const int64_t r0 = m * p.g;
-        const int64_t r1 = (r0 + p.g < p.q_len) ? r0 + p.g : p.q_len;
+        const int64_t r1 = (r0 + p.g < rq.q_len) ? r0 + p.g : rq.q_len;
         const int64_t r = r0 + (int64_t)chunk * NW + wave;
-        wr.valid = r < r1;
-        const int64_t row = (int64_t)bi * p.q_len + r;
+        wr.valid = live && r < r1;
+        const int64_t row = rq.q_off + r;
         wr.q = p.Q + row * H * D;
         wr.w = p.W + row * H;
         wr.lim = (int)(off + r);
@@ -314,9 +321,8 @@ __device__ __forceinline__ void plan_block(const ScanParams &p, int64_t j, int w
         wr.s1 = p.o1_score ? p.o1_score + row * p.sel : nullptr;
         wr.fan1 = 1;
         const int64_t t_last = off + r1 - 1;
-        bk.Kb = p.K + (int64_t)bi * p.L * D;
-        bk.list = p.cand + ((int64_t)bi * p.G + m) * p.c;
-        bk.nkeys = (int)((p.c < t_last + 1) ? p.c : t_last + 1);
+        bk.list = p.cand + (rq.g_off + m) * p.c;
+        bk.nkeys = live ? (int)((p.c < t_last + 1) ? p.c : t_last + 1) : 0;
     }
 }
 
@@ -611,21 +617,21 @@ void scan_select_kernel(ScanParams p)
 
         fetch_keys(0);
         if (ntiles > 0)
-            stage_issue<D, NW, STAGE>(kA, lA, bk, (int)p.L, 0, keys, wave, lane);
+            stage_issue<D, NW, STAGE>(kA, lA, bk, bk.L, 0, keys, wave, lane);
         fetch_keys(1);
         __syncthreads();
         // two stages per trip so that each LDS buffer is a distinct object at
         // every access (the DMA into one overlaps the MFMA reads of the other)
         for (int t = 0; t < ntiles; t += 2) {
             if (t + 1 < ntiles)
-                stage_issue<D, NW, STAGE>(kB, lB, bk, (int)p.L, t + 1, keys, wave, lane);
+                stage_issue<D, NW, STAGE>(kB, lB, bk, bk.L, t + 1, keys, wave, lane);
             fetch_keys(t + 2);
             compute(kA, lA, t);
             __syncthreads();
             if (t + 1 >= ntiles)
                 break;
             if (t + 2 < ntiles)
-                stage_issue<D, NW, STAGE>(kA, lA, bk, (int)p.L, t + 2, keys, wave, lane);
+                stage_issue<D, NW, STAGE>(kA, lA, bk, bk.L, t + 2, keys, wave, lane);
             fetch_keys(t + 3);
             compute(kB, lB, t + 1);
             __syncthreads();
@@ -655,14 +661,17 @@ void scan_select_kernel(ScanParams p)
 template <int H, int D>
 __global__ __launch_bounds__(256) void pool_kernel(PoolParams p)
 {
-    const int64_t grp = blockIdx.x;
-    const int bi = (int)(grp / p.G);
-    const int64_t m = grp % p.G;
+    const int64_t m = blockIdx.x;
+    const int bi = blockIdx.y;
+    const Req rq = request_of(p.req, bi, p.L, p.q_len, p.g, p.m0);
+    if (m < rq.m0 || m >= rq.G)
+        return;  // guarded, or beyond the request's groups
+    const int64_t grp = rq.g_off + m;
     const int64_t r0 = m * p.g;
-    const int64_t r1 = (r0 + p.g < p.q_len) ? r0 + p.g : p.q_len;
+    const int64_t r1 = (r0 + p.g < rq.q_len) ? r0 + p.g : rq.q_len;
     const float n = (float)(r1 - r0);
-    const uint16_t *Qb = p.Q + ((int64_t)bi * p.q_len) * H * D;
-    const float *Wb = p.W + ((int64_t)bi * p.q_len) * H;
+    const uint16_t *Qb = p.Q + rq.q_off * H * D;
+    const float *Wb = p.W + rq.q_off * H;
     for (int x = threadIdx.x * 8; x < H * D; x += blockDim.x * 8) {
         float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
         for (int64_t r = r0; r < r1; ++r) {
@@ -701,7 +710,8 @@ static hipError_t launch_scan(const ScanParams &prm, int grid, hipStream_t strea
 template <int H, int D>
 static hipError_t launch_pool_t(const PoolParams &prm, hipStream_t stream)
 {
-    hipLaunchKernelGGL((pool_kernel<H, D>), dim3((unsigned)(prm.B * prm.G)), dim3(256), 0, stream, prm);
+    // one workgroup per (group, request); gmax = the largest request's groups
+    hipLaunchKernelGGL((pool_kernel<H, D>), dim3((unsigned)prm.gmax, (unsigned)prm.B), dim3(256), 0, stream, prm);
     return hipGetLastError();
 }
 

@@ -32,38 +32,60 @@ namespace dsaidx {
 struct SplitRow {
     const uint16_t *q;
     const float *w;
+    const uint16_t *Kb;   // keys of the request
     const int32_t *list;  // kRefine: the group's candidate list
-    int npos;             // positions to consider
+    int L;                // keys of the request
+    int npos;             // positions to consider (0: no such row)
     int lim;              // last eligible key index
 };
 
+// Score row r of request bi in a split pass: a dense row (r < the request's
+// dense rows), a group proxy (group m0 + r), or a Refine member row (row
+// r_g + r, where rows [0, r_g) belong to guarded groups). Rows beyond the
+// request's count get npos = 0.
 __device__ __forceinline__ SplitRow split_row(const SplitScoreParams &p, int H, int D, int bi, int64_t r)
 {
     SplitRow s;
-    const int64_t off = p.L - p.q_len;
+    const Req rq = request_of(p.req, bi, p.L, p.q_len, p.g, p.m0);
+    const int64_t off = rq.L - rq.q_len;
+    s.list = nullptr;
+    s.npos = 0;
+    s.lim = -1;
+    s.q = p.Q;
+    s.w = p.W;
+    s.Kb = p.K + rq.key_off * D;
+    s.L = (int)rq.L;
     if (p.mode == kProxy) {
-        const int64_t grow = (int64_t)bi * p.G + r;
-        const int64_t r1 = ((r + 1) * p.g < p.q_len) ? (r + 1) * p.g : p.q_len;
+        const int64_t m = rq.m0 + r;
+        if (m >= rq.G)
+            return s;
+        const int64_t grow = rq.g_off + m;
+        const int64_t r1 = ((m + 1) * p.g < rq.q_len) ? (m + 1) * p.g : rq.q_len;
         s.q = p.Q + grow * H * D;
         s.w = p.W + grow * H;
-        s.list = nullptr;
         s.lim = (int)(off + r1 - 1);
         s.npos = s.lim + 1;
-    } else {
-        const int64_t row = (int64_t)bi * p.q_len + r;
+    } else if (p.mode == kDense) {
+        if (r >= dense_rows(rq, p.g, p.guard_rows))
+            return s;
+        const int64_t row = rq.q_off + r;
         s.q = p.Q + row * H * D;
         s.w = p.W + row * H;
         s.lim = (int)(off + r);
-        if (p.mode == kDense) {
-            s.list = nullptr;
-            s.npos = s.lim + 1;
-        } else {
-            const int64_t m = r / p.g;
-            const int64_t r1 = ((m + 1) * p.g < p.q_len) ? (m + 1) * p.g : p.q_len;
-            const int64_t t_last = off + r1 - 1;
-            s.list = p.cand + ((int64_t)bi * p.G + m) * p.c;
-            s.npos = (int)((p.c < t_last + 1) ? p.c : t_last + 1);
-        }
+        s.npos = s.lim + 1;
+    } else {
+        const int64_t rr = dense_rows(rq, p.g, 1) + r;  // rows past the guarded groups
+        if (rr >= rq.q_len)
+            return s;
+        const int64_t row = rq.q_off + rr;
+        s.q = p.Q + row * H * D;
+        s.w = p.W + row * H;
+        s.lim = (int)(off + rr);
+        const int64_t m = rr / p.g;
+        const int64_t r1 = ((m + 1) * p.g < rq.q_len) ? (m + 1) * p.g : rq.q_len;
+        const int64_t t_last = off + r1 - 1;
+        s.list = p.cand + (rq.g_off + m) * p.c;
+        s.npos = (int)((p.c < t_last + 1) ? p.c : t_last + 1);
     }
     return s;
 }
@@ -115,7 +137,7 @@ __global__ __launch_bounds__(kSplitWaves * kWave) void split_score_kernel(SplitS
         return;
     const int w1 = (w0 + span < sr.npos) ? w0 + span : sr.npos;
     const int ntile = (w1 - w0 + 31) / 32;
-    const uint16_t *Kb = p.K + (int64_t)bi * p.L * D;
+    const uint16_t *Kb = sr.Kb;
     float *out = p.scores + ((int64_t)bi * p.nrows + r) * p.rowlen;
     int32_t *wl = lst[wave];
 
@@ -137,7 +159,7 @@ __global__ __launch_bounds__(kSplitWaves * kWave) void split_score_kernel(SplitS
             int key = 0;
             if (t < ntile && pos < w1) {
                 key = LIST ? wl[pos - w0] : pos;
-                key = (key >= 0 && key < p.L) ? key : 0;
+                key = (key >= 0 && key < sr.L) ? key : 0;
             }
             __builtin_amdgcn_global_load_lds(
                 (const __attribute__((address_space(1))) void *)(Kb + (int64_t)key * D + c * 8),
@@ -832,22 +854,26 @@ __device__ __forceinline__ void select_row(const SelRow &s, const SelOut *outs, 
 
 // Row r of batch item bi of a selection pass: its scores, validity, and the
 // outputs of its selections.
-__device__ __forceinline__ void select_geometry(const SplitSelectParams &p, int bi, int64_t r, SelRow &s,
+__device__ __forceinline__ bool select_geometry(const SplitSelectParams &p, int bi, int64_t r, SelRow &s,
                                                 SelOut (&outs)[2])
 {
-    const int64_t off = p.L - p.q_len;
+    const Req rq = request_of(p.req, bi, p.L, p.q_len, p.g, p.m0);
+    const int64_t off = rq.L - rq.q_len;
     s.sc = p.scores + ((int64_t)bi * p.nrows + r) * p.rowlen;
     int32_t *o1, *o2 = nullptr;
     float *s1, *s2 = nullptr;
     int fan1 = 1, fan2 = 0;
     if (p.mode == kProxy) {
-        const int64_t r0 = r * p.g;
-        const int64_t r1 = (r0 + p.g < p.q_len) ? r0 + p.g : p.q_len;
+        const int64_t m = rq.m0 + r;
+        if (m >= rq.G)
+            return false;
+        const int64_t r0 = m * p.g;
+        const int64_t r1 = (r0 + p.g < rq.q_len) ? r0 + p.g : rq.q_len;
         s.list = nullptr;
         s.lim = (int)(off + r1 - 1);
         s.npos = s.lim + 1;
-        const int64_t mrow = (int64_t)bi * p.q_len + r0;
-        const int64_t grow = (int64_t)bi * p.G + r;
+        const int64_t mrow = rq.q_off + r0;
+        const int64_t grow = rq.g_off + m;
         if (p.o1_members) {
             o1 = p.o1_idx + mrow * p.sel;
             s1 = p.o1_score ? p.o1_score + mrow * p.sel : nullptr;
@@ -862,23 +888,31 @@ __device__ __forceinline__ void select_geometry(const SplitSelectParams &p, int 
             fan2 = (int)(r1 - r0);
         }
     } else {
-        const int64_t row = (int64_t)bi * p.q_len + r;
-        s.lim = (int)(off + r);
+        int64_t rr = r;
         if (p.mode == kDense) {
+            if (r >= dense_rows(rq, p.g, p.guard_rows))
+                return false;
             s.list = nullptr;
+            s.lim = (int)(off + rr);
             s.npos = s.lim + 1;
         } else {
-            const int64_t m = r / p.g;
-            const int64_t r1 = ((m + 1) * p.g < p.q_len) ? (m + 1) * p.g : p.q_len;
+            rr = dense_rows(rq, p.g, 1) + r;
+            if (rr >= rq.q_len)
+                return false;
+            s.lim = (int)(off + rr);
+            const int64_t m = rr / p.g;
+            const int64_t r1 = ((m + 1) * p.g < rq.q_len) ? (m + 1) * p.g : rq.q_len;
             const int64_t t_last = off + r1 - 1;
-            s.list = p.cand + ((int64_t)bi * p.G + m) * p.c;
+            s.list = p.cand + (rq.g_off + m) * p.c;
             s.npos = (int)((p.c < t_last + 1) ? p.c : t_last + 1);
         }
+        const int64_t row = rq.q_off + rr;
         o1 = p.o1_idx + row * p.sel;
         s1 = p.o1_score ? p.o1_score + row * p.sel : nullptr;
     }
     outs[0] = SelOut{p.sel, o1, s1, fan1};
     outs[1] = SelOut{p.sel2, o2, s2, fan2};
+    return true;
 }
 
 __global__ __launch_bounds__(kSelectThreads) void split_select_kernel(SplitSelectParams p)
@@ -888,7 +922,8 @@ __global__ __launch_bounds__(kSelectThreads) void split_select_kernel(SplitSelec
     const int64_t r = blockIdx.x;
     SelRow s;
     SelOut outs[2];
-    select_geometry(p, bi, r, s, outs);
+    if (!select_geometry(p, bi, r, s, outs))
+        return;  // no such row in this request
     select_row(s, outs, p.sel2 > 0 ? 2 : 1, sm);
 }
 

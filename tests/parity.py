@@ -113,3 +113,52 @@ def check_pivot(Q, W, K, g, c, k, variant, groups=None, with_cand=True):
 def assert_ok(*results):
     for r in results:
         assert not r.failures, r.summary() + "\n" + "\n".join(r.failures[:10])
+
+
+def merge(dst, src):
+    dst.rows += src.rows
+    dst.exact += src.exact
+    dst.band += src.band
+    dst.max_rel = max(dst.max_rel, src.max_rel)
+    dst.failures += src.failures
+    return dst
+
+
+def check_varlen(variant, Q, W, K, L, q_len, g, c, k, guard, out, max_groups=None, seed=0):
+    """Check the outputs of a packed batch of requests (variant dense, reuse or
+    refine). out = (idx [sum q_len, k], score, cand [sum G, c] or None) on the
+    GPU. Rows of guarded groups must hold their dense selection and their
+    candidate rows -1; the other groups are checked as PIVOT groups. With
+    max_groups, that many seeded-random groups per request (plus the first
+    and last unguarded ones) are checked. Returns (dense rows, cand, PIVOT
+    rows) results."""
+    idx, sc, cand = out
+    idx, sc = idx.cpu().numpy(), sc.cpu().numpy()
+    cand = cand.cpu().numpy() if cand is not None else None
+    key_off, q_off, g_off = oracle.request_offsets(L, q_len, g)
+    rng = np.random.default_rng(seed)
+    res_d, res_c, res_r = Result(), Result(), Result()
+    for b, (Lb, qb) in enumerate(zip(L, q_len)):
+        hv = HostView(Q[q_off[b]:q_off[b] + qb][None], W[q_off[b]:q_off[b] + qb][None],
+                      K[key_off[b]:key_off[b] + Lb][None])
+        ib = idx[q_off[b]:q_off[b] + qb][None]
+        sb = sc[q_off[b]:q_off[b] + qb][None]
+        if variant == "dense":
+            check_dense_rows(ib, sb, hv, Lb, qb, k, [(0, r) for r in range(qb)], res_d)
+            continue
+        G = -(-qb // g)
+        m0 = oracle.guarded_groups(Lb, qb, g, guard)
+        check_dense_rows(ib, sb, hv, Lb, qb, k, [(0, r) for r in range(min(m0 * g, qb))], res_d)
+        cb = None if cand is None else cand[g_off[b]:g_off[b] + G][None]
+        if cb is not None:
+            for m in range(m0):
+                ok = bool((cb[0, m] == -1).all())
+                res_c.add(ok, ok, 0.0, None if ok else f"cand b{b} m{m}: guarded group not -1")
+        groups = list(range(m0, G))
+        if max_groups is not None and len(groups) > max_groups:
+            pick = set(rng.choice(groups, max_groups, replace=False).tolist()) | {groups[0], groups[-1]}
+            groups = sorted(pick)
+        rc, rr = check_pivot_rows(variant, ib, sb, cb, hv, Lb, qb, g, c, k, [(0, m) for m in groups])
+        merge(res_c, rc)
+        merge(res_r, rr)
+    return res_d, res_c, res_r

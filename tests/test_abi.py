@@ -103,3 +103,37 @@ def test_pivot_rejects_bad_arguments(fn):
 def test_refine_requires_c_ge_k():
     assert call_pivot(dsa.indexer_pivot_refine, c=100, k=256) == EINVAL
     assert "c=" in dsa.indexer_last_error()
+
+
+def varlen_ws(mode, L, q, g=4, c=512, k=256, guard=0, H=64, d=128):
+    arr = ctypes.c_int64 * len(L)
+    return dsa.indexer_varlen_workspace_bytes(mode, len(L), arr(*L), arr(*q), H, d, g, c, k, guard)
+
+
+def test_varlen_workspace_sizes():
+    assert varlen_ws(dsa.DENSE, [100, 5000], [100, 2]) > 0
+    assert varlen_ws(dsa.REFINE, [100, 5000], [100, 2]) > 0
+    assert varlen_ws(dsa.REUSE, [100, 5000], [100, 2], guard=50) > 0
+    # the guard removes the PIVOT stages when every group is guarded
+    assert varlen_ws(dsa.REFINE, [4096], [4096], guard=4096) < varlen_ws(dsa.REFINE, [4096], [4096])
+    assert varlen_ws(dsa.DENSE, [100, 50], [100, 60]) == 0   # q_len > L
+    assert varlen_ws(dsa.DENSE, [0], [0]) == 0
+    assert varlen_ws(dsa.REFINE, [100], [100], guard=-1) == 0
+
+
+def test_varlen_rejects_bad_arguments():
+    arr = ctypes.c_int64 * 2
+    L, q = arr(1000, 50), arr(1000, 60)
+    rc = dsa.indexer_dense_varlen(fake(), fake(), fake(), 2, L, q, 64, 128, 64, fake(), None, fake(),
+                                  1 << 40, None)
+    assert rc == EINVAL and "q_len" in dsa.indexer_last_error()
+    rc = dsa.indexer_pivot_refine_varlen(fake(), fake(), fake(), 2, None, q, 64, 128, 4, 128, 64, 0,
+                                         fake(), None, None, fake(), 1 << 40, None)
+    assert rc == EINVAL
+    L, q = arr(1000, 50), arr(1000, 50)
+    rc = dsa.indexer_pivot_reuse_varlen(fake(), fake(), fake(), 2, L, q, 64, 128, 0, 128, 64, 0,
+                                        fake(), None, None, fake(), 1 << 40, None)
+    assert rc == EINVAL
+    rc = dsa.indexer_pivot_refine_varlen(fake(), fake(), fake(), 2, L, q, 64, 128, 4, 32, 64, 0,
+                                         fake(), None, None, fake(), 1 << 40, None)
+    assert rc == EINVAL  # c < k

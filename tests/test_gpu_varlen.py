@@ -1,0 +1,142 @@
+"""Batches of requests of different lengths, through the *_varlen entry points:
+every request's rows against the oracle run on that request alone; groups
+never reach into a neighbouring request; the guard scores short groups as
+dense rows. Covers the scan (many rows) and split-key (few rows) paths, short
+last groups, q_len < L, a request shorter than k, and the guard's limits."""
+import numpy as np
+import pytest
+import torch
+
+import sparse_attention_indexer_dense_amd as dsa
+import synth
+from parity import assert_ok, check_varlen
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+def packed(L, q_len, H=4, d=32, seed=0):
+    """Packed Q, W, K of requests whose queries are their last q_len positions."""
+    Qs, Ws, Ks = [], [], []
+    for i, (Lb, qb) in enumerate(zip(L, q_len)):
+        if qb == Lb:
+            Q, W, K = synth.prefill(Lb, H, d, 0.9, 2, seed + i, DEV)
+        else:
+            Q, W, K = synth.decode(1, Lb, qb, H, d, 0.9, 2, seed + i, DEV)
+        Qs.append(Q[0])
+        Ws.append(W[0])
+        Ks.append(K[0])
+    return torch.cat(Qs).contiguous(), torch.cat(Ws).contiguous(), torch.cat(Ks).contiguous()
+
+
+# many rows per request (scan kernels) and few rows (split-key kernels)
+SCAN = ([1000, 3001, 257, 700], [1000, 120, 257, 65])
+SPLIT = ([5000, 1200, 300, 9000, 77], [2, 3, 1, 2, 3])
+
+
+@pytest.mark.parametrize("shape", [SCAN, SPLIT], ids=["scan", "split"])
+def test_dense_varlen(shape):
+    L, q = shape
+    Q, W, K = packed(L, q)
+    idx, sc = dsa.dense_varlen(Q, W, K, L, q, 64)
+    res, _, _ = check_varlen("dense", Q, W, K, L, q, 1, 0, 64, 0, (idx, sc, None))
+    assert_ok(res)
+    assert res.rows == sum(q)
+
+
+@pytest.mark.parametrize("shape", [SCAN, SPLIT], ids=["scan", "split"])
+@pytest.mark.parametrize("variant", ["reuse", "refine"])
+def test_pivot_varlen(shape, variant):
+    L, q = shape
+    Q, W, K = packed(L, q, seed=3)
+    g, c, k = 4, 128, 64
+    if variant == "reuse":
+        out = dsa.pivot_reuse_varlen(Q, W, K, L, q, g, k, c=c, cand=True)
+    else:
+        out = dsa.pivot_refine_varlen(Q, W, K, L, q, g, c, k, cand=True)
+    rd, rc, rr = check_varlen(variant, Q, W, K, L, q, g, c, k, 0, out)
+    assert_ok(rd, rc, rr)
+    assert rd.rows == 0 and rr.rows == sum(q)
+
+
+def test_reuse_varlen_without_candidates():
+    L, q = SCAN
+    Q, W, K = packed(L, q, seed=5)
+    out = dsa.pivot_reuse_varlen(Q, W, K, L, q, 4, 64)
+    rd, rc, rr = check_varlen("reuse", Q, W, K, L, q, 4, 0, 64, 0, out)
+    assert_ok(rd, rc, rr)
+
+
+@pytest.mark.parametrize("guard", [64, 600, 3001])
+@pytest.mark.parametrize("variant", ["reuse", "refine"])
+def test_guard(variant, guard):
+    L, q = SCAN
+    Q, W, K = packed(L, q, seed=7)
+    g, c, k = 4, 128, 64
+    f = dsa.pivot_reuse_varlen if variant == "reuse" else dsa.pivot_refine_varlen
+    out = (f(Q, W, K, L, q, g, k, c=c, guard=guard, cand=True) if variant == "reuse"
+           else f(Q, W, K, L, q, g, c, k, guard=guard, cand=True))
+    rd, rc, rr = check_varlen(variant, Q, W, K, L, q, g, c, k, guard, out)
+    assert_ok(rd, rc, rr)
+    assert rd.rows > 0
+    if guard >= max(L):
+        assert rr.rows == 0  # everything dense
+
+
+@pytest.mark.parametrize("shape", [SCAN, SPLIT], ids=["scan", "split"])
+def test_refine_guard_up_to_c_changes_nothing(shape):
+    L, q = shape
+    Q, W, K = packed(L, q, seed=11)
+    g, c, k = 4, 512, 64
+    i0, s0, _ = dsa.pivot_refine_varlen(Q, W, K, L, q, g, c, k)
+    i1, s1, _ = dsa.pivot_refine_varlen(Q, W, K, L, q, g, c, k, guard=c)
+    assert torch.equal(i0, i1)
+    assert torch.equal(s0, s1)
+
+
+@pytest.mark.parametrize("variant", ["dense", "reuse", "refine"])
+def test_equal_lengths_match_uniform_batch(variant):
+    B, L, q = 3, 2000, 300
+    Qs, Ws, Ks = [], [], []
+    for b in range(B):
+        Q, W, K = synth.decode(1, L, q, 4, 32, 0.9, 2, 20 + b, DEV)
+        Qs.append(Q)
+        Ws.append(W)
+        Ks.append(K)
+    Qu, Wu, Ku = torch.cat(Qs), torch.cat(Ws), torch.cat(Ks)
+    Qv, Wv, Kv = Qu.reshape(B * q, 4, 32), Wu.reshape(B * q, 4), Ku.reshape(B * L, 32)
+    g, c, k = 4, 256, 64
+    if variant == "dense":
+        iu, su = dsa.dense(Qu, Wu, Ku, k)
+        iv, sv = dsa.dense_varlen(Qv, Wv, Kv, [L] * B, [q] * B, k)
+    elif variant == "reuse":
+        iu, su, _ = dsa.pivot_reuse(Qu, Wu, Ku, g, k)
+        iv, sv, _ = dsa.pivot_reuse_varlen(Qv, Wv, Kv, [L] * B, [q] * B, g, k)
+    else:
+        iu, su, _ = dsa.pivot_refine(Qu, Wu, Ku, g, c, k)
+        iv, sv, _ = dsa.pivot_refine_varlen(Qv, Wv, Kv, [L] * B, [q] * B, g, c, k)
+    assert torch.equal(iu.reshape(B * q, k), iv)
+    assert torch.equal(su.reshape(B * q, k), sv)
+
+
+def test_h64_d128_mixed():
+    L, q = [2500, 700, 4096], [2500, 5, 33]
+    Q, W, K = packed(L, q, H=64, d=128, seed=13)
+    g, c, k = 4, 512, 256
+    out = dsa.pivot_refine_varlen(Q, W, K, L, q, g, c, k, guard=800, cand=True)
+    rd, rc, rr = check_varlen("refine", Q, W, K, L, q, g, c, k, 800, out, max_groups=24)
+    assert_ok(rd, rc, rr)
+
+
+def test_decode_batch_of_lengths():
+    # a decode step of requests with different cache lengths, 2 new rows each
+    L = [40000, 7000, 65536, 12289, 3000, 20000]
+    q = [2] * len(L)
+    Q, W, K = packed(L, q, H=64, d=128, seed=17)
+    g, c, k = 2, 4096, 2048
+    out = dsa.pivot_refine_varlen(Q, W, K, L, q, g, c, k, cand=True)
+    rd, rc, rr = check_varlen("refine", Q, W, K, L, q, g, c, k, 0, out)
+    assert_ok(rd, rc, rr)
+    d_idx, d_sc = dsa.dense_varlen(Q, W, K, L, q, k)
+    res, _, _ = check_varlen("dense", Q, W, K, L, q, 1, 0, k, 0, (d_idx, d_sc, None))
+    assert_ok(res)
