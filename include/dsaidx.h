@@ -130,6 +130,34 @@ int indexer_pivot_refine(const void *Q, const float *W, const void *K,
                          void *ws, size_t ws_bytes, hipStream_t stream);
 
 /*
+ * Options of the variable-length PIVOT entry points (NULL: all defaults).
+ *   guard   see below; 0 (default) turns the guard off.
+ *   proxy   how a group becomes one proxy query and proxy weights (PIVOT
+ *           paper, ablation on the proxy aggregation strategy, and the
+ *           experimental setup's mean pooling within a local window):
+ *             DSAIDX_PROXY_MEAN  (default) the per-head mean of `window`
+ *                                consecutive members ending at the group's
+ *                                last row; window 0, or a window at least
+ *                                the group's size, averages the whole group;
+ *             DSAIDX_PROXY_FIRST the first member's query and weights;
+ *             DSAIDX_PROXY_LAST  the last member's query and weights.
+ *           A mean is an fp32 sum in row order divided in fp32 by the member
+ *           count and rounded to bf16 (nearest even); weights stay fp32.
+ *   window  members averaged by DSAIDX_PROXY_MEAN (>= 0; ignored otherwise).
+ */
+typedef enum {
+    DSAIDX_PROXY_MEAN = 0,
+    DSAIDX_PROXY_FIRST = 1,
+    DSAIDX_PROXY_LAST = 2
+} dsaidx_proxy;
+
+typedef struct {
+    int64_t guard;
+    int32_t proxy;
+    int32_t window;
+} dsaidx_pivot_opts;
+
+/*
  * Batches of requests of different lengths (PIVOT paper, Method: query
  * groups are contiguous, never cross a request boundary, and the last group
  * of a request may be smaller), with an optional guard for short prefixes
@@ -146,7 +174,7 @@ int indexer_pivot_refine(const void *Q, const float *W, const void *K,
  *     out_idx  [sum q_len][k]         int32
  *     out_score[sum q_len][k]         fp32, may be NULL
  *     out_cand [sum G][c]             int32, may be NULL; G[b] = ceil(q_len[b] / g)
- *   guard     a group whose last position t_last satisfies t_last + 1 <= guard
+ *   opts->guard  a group whose last position t_last satisfies t_last + 1 <= guard
  *             (its whole causal prefix holds at most `guard` keys) is scored
  *             densely: each of its rows receives its dense top-k, and its
  *             candidate row, if requested, is filled with -1. guard = 0 turns
@@ -160,7 +188,8 @@ int indexer_pivot_refine(const void *Q, const float *W, const void *K,
  *   B small request descriptors into ws through kernel launches on `stream`.
  */
 size_t indexer_varlen_workspace_bytes(int mode, int B, const int64_t *L, const int64_t *q_len,
-                                      int H_I, int d_I, int g, int c, int k, int64_t guard);
+                                      int H_I, int d_I, int g, int c, int k,
+                                      const dsaidx_pivot_opts *opts);
 
 int indexer_dense_varlen(const void *Q, const float *W, const void *K,
                          int B, const int64_t *L, const int64_t *q_len, int H_I, int d_I, int k,
@@ -169,13 +198,13 @@ int indexer_dense_varlen(const void *Q, const float *W, const void *K,
 
 int indexer_pivot_reuse_varlen(const void *Q, const float *W, const void *K,
                                int B, const int64_t *L, const int64_t *q_len, int H_I, int d_I,
-                               int g, int c, int k, int64_t guard,
+                               int g, int c, int k, const dsaidx_pivot_opts *opts,
                                int32_t *out_idx, float *out_score, int32_t *out_cand,
                                void *ws, size_t ws_bytes, hipStream_t stream);
 
 int indexer_pivot_refine_varlen(const void *Q, const float *W, const void *K,
                                 int B, const int64_t *L, const int64_t *q_len, int H_I, int d_I,
-                                int g, int c, int k, int64_t guard,
+                                int g, int c, int k, const dsaidx_pivot_opts *opts,
                                 int32_t *out_idx, float *out_score, int32_t *out_cand,
                                 void *ws, size_t ws_bytes, hipStream_t stream);
 

@@ -62,8 +62,11 @@ def _bind(lib):
     lib.orc_proxy.argtypes = [P, P, i64, i32, i32, i64, i64, P, P]
     lib.orc_pivot_groups.argtypes = [P, P, P, i64, i64, i32, i32, i64, i64, i64,
                                      P, i64, P, P, P, P, P, P, P]
+    lib.orc_proxy_ex.argtypes = [P, P, i64, i32, i32, i64, i64, i32, i64, P, P]
+    lib.orc_pivot_groups_ex.argtypes = [P, P, P, i64, i64, i32, i32, i64, i64, i64, i32, i64,
+                                        P, i64, P, P, P, P, P, P, P]
     for f in (lib.orc_scores, lib.orc_select, lib.orc_dense_rows, lib.orc_proxy,
-              lib.orc_pivot_groups):
+              lib.orc_pivot_groups, lib.orc_proxy_ex, lib.orc_pivot_groups_ex):
         f.restype = ctypes.c_int
     return lib
 
@@ -116,14 +119,20 @@ def select(score, k, idx=None, lib=None):
     return oi, os_
 
 
-def proxy(Q, W, g, m, lib=None):
-    """Proxy (bf16 bits [H, d], fp32 [H]) of query group m of Q [q_len, H, d]."""
+PROXY = {"mean": 0, "first": 1, "last": 2}
+
+
+def proxy(Q, W, g, m, kind="mean", window=0, lib=None):
+    """Proxy (bf16 bits [H, d], fp32 [H]) of query group m of Q [q_len, H, d]:
+    the mean of the group (or of its last ``window`` members), or its first
+    or last member (``kind``)."""
     lib = lib or load()
     Q, W = _u16(Q), _f32(W)
     q_len, H, d = Q.shape
     qb = np.empty((H, d), np.uint16)
     wb = np.empty(H, np.float32)
-    _check(lib.orc_proxy(_p(Q), _p(W), q_len, H, d, g, m, _p(qb), _p(wb)), "proxy")
+    _check(lib.orc_proxy_ex(_p(Q), _p(W), q_len, H, d, g, m, PROXY[kind], window, _p(qb), _p(wb)),
+           "proxy")
     return qb, wb
 
 
@@ -145,7 +154,7 @@ def dense_rows(Q, W, K, k, rows, lib=None):
     return oi, os_
 
 
-def pivot_groups(Q, W, K, g, c, k, groups, cand_in=None, lib=None):
+def pivot_groups(Q, W, K, g, c, k, groups, cand_in=None, kind="mean", window=0, lib=None):
     """PIVOT proxy scan, candidates, Reuse and Refine for groups ``groups``.
 
     Returns a dict with cand/cand_score [ng, c], reuse/reuse_score [ng, k] and
@@ -165,8 +174,8 @@ def pivot_groups(Q, W, K, g, c, k, groups, cand_in=None, lib=None):
         refine=np.empty((ng, g, k), np.int64),
         refine_score=np.empty((ng, g, k), np.float64),
     )
-    _check(lib.orc_pivot_groups(
-        _p(Q), _p(W), _p(K), L, q_len, H, d, g, c, k, _p(groups), ng, _p(ci),
+    _check(lib.orc_pivot_groups_ex(
+        _p(Q), _p(W), _p(K), L, q_len, H, d, g, c, k, PROXY[kind], window, _p(groups), ng, _p(ci),
         _p(out["cand"]), _p(out["cand_score"]), _p(out["reuse"]),
         _p(out["reuse_score"]), _p(out["refine"]), _p(out["refine_score"])),
         "pivot_groups")

@@ -34,6 +34,13 @@
 #define ORC_OK 0
 #define ORC_EINVAL 1
 
+#define ORC_PROXY_MEAN 0
+#define ORC_PROXY_FIRST 1
+#define ORC_PROXY_LAST 2
+
+int orc_proxy_ex(const uint16_t *Q, const float *W, int64_t q_len, int H, int d,
+                 int64_t g, int64_t m, int proxy, int64_t window, uint16_t *qbar, float *wbar);
+
 /* Exact widening of a bf16 bit pattern (the upper half of an fp32). */
 static double bf16_to_double(uint16_t b)
 {
@@ -207,26 +214,68 @@ int orc_dense_rows(const uint16_t *Q, const float *W, const uint16_t *K,
  * rounded to bf16 (nearest, ties to even); each weight is summed in fp32 and
  * divided in fp32. qbar is [H][d] bf16, wbar is [H] fp32.
  */
-int orc_proxy(const uint16_t *Q, const float *W, int64_t q_len, int H, int d,
-              int64_t g, int64_t m, uint16_t *qbar, float *wbar)
+/* Mean of query rows [a, b) per head and dimension: fp32 sum in row order,
+ * fp32 division by the row count, rounded to bf16 (nearest even); the
+ * weights likewise, kept in fp32. */
+static void mean_rows(const uint16_t *Q, const float *W, int H, int d, int64_t a, int64_t b,
+                      uint16_t *qbar, float *wbar)
 {
-    if (!Q || !W || !qbar || !wbar || g < 1 || m < 0 || m * g >= q_len)
-        return ORC_EINVAL;
-    int64_t r0 = m * g;
-    int64_t r1 = r0 + g < q_len ? r0 + g : q_len;
-    float cnt = (float)(r1 - r0);
+    float cnt = (float)(b - a);
     for (int64_t x = 0; x < (int64_t)H * d; ++x) {
         float acc = 0.0f;
-        for (int64_t r = r0; r < r1; ++r)
+        for (int64_t r = a; r < b; ++r)
             acc += bf16_to_float(Q[r * H * d + x]);
         qbar[x] = float_to_bf16_rne(acc / cnt);
     }
     for (int j = 0; j < H; ++j) {
         float acc = 0.0f;
-        for (int64_t r = r0; r < r1; ++r)
+        for (int64_t r = a; r < b; ++r)
             acc += W[r * H + j];
         wbar[j] = acc / cnt;
     }
+}
+
+int orc_proxy(const uint16_t *Q, const float *W, int64_t q_len, int H, int d,
+              int64_t g, int64_t m, uint16_t *qbar, float *wbar)
+{
+    return orc_proxy_ex(Q, W, q_len, H, d, g, m, ORC_PROXY_MEAN, 0, qbar, wbar);
+}
+
+/*
+ * Proxy of group m (rows r0 .. r1-1) under an aggregation strategy (PIVOT
+ * paper, ablation on the proxy aggregation strategy, and the experimental
+ * setup's mean pooling within a local window):
+ *   ORC_PROXY_MEAN  - mean of the members in a window of `window` rows; the
+ *                     reading taken for a window narrower than the group is
+ *                     its last `window` members (those with the longest
+ *                     prefixes); window 0, or one at least the group's size,
+ *                     averages the whole group;
+ *   ORC_PROXY_FIRST - the first member's query and weights (an endpoint proxy);
+ *   ORC_PROXY_LAST  - the last member's.
+ */
+int orc_proxy_ex(const uint16_t *Q, const float *W, int64_t q_len, int H, int d,
+                 int64_t g, int64_t m, int proxy, int64_t window, uint16_t *qbar, float *wbar)
+{
+    if (!Q || !W || !qbar || !wbar || g < 1 || m < 0 || m * g >= q_len || window < 0)
+        return ORC_EINVAL;
+    int64_t r0 = m * g;
+    int64_t r1 = r0 + g < q_len ? r0 + g : q_len;
+    int64_t a, b;
+    if (proxy == ORC_PROXY_MEAN) {
+        int64_t n = r1 - r0;
+        int64_t wn = (window == 0 || window >= n) ? n : window;
+        a = r1 - wn;
+        b = r1;
+    } else if (proxy == ORC_PROXY_FIRST) {
+        a = r0;
+        b = r0 + 1;
+    } else if (proxy == ORC_PROXY_LAST) {
+        a = r1 - 1;
+        b = r1;
+    } else {
+        return ORC_EINVAL;
+    }
+    mean_rows(Q, W, H, d, a, b, qbar, wbar);
     return ORC_OK;
 }
 
@@ -270,6 +319,15 @@ static int valid_candidates(const int64_t *cand, int64_t c, int64_t t_last)
  * (rows of absent members of a short last group are all -1). Score outputs
  * may be NULL.
  */
+int orc_pivot_groups_ex(const uint16_t *Q, const float *W, const uint16_t *K,
+                        int64_t L, int64_t q_len, int H, int d,
+                        int64_t g, int64_t c, int64_t k, int proxy, int64_t window,
+                        const int64_t *groups, int64_t ngroups,
+                        const int64_t *cand_in,
+                        int64_t *cand_out, double *cand_score,
+                        int64_t *reuse_out, double *reuse_score,
+                        int64_t *refine_out, double *refine_score);
+
 int orc_pivot_groups(const uint16_t *Q, const float *W, const uint16_t *K,
                      int64_t L, int64_t q_len, int H, int d,
                      int64_t g, int64_t c, int64_t k,
@@ -278,6 +336,21 @@ int orc_pivot_groups(const uint16_t *Q, const float *W, const uint16_t *K,
                      int64_t *cand_out, double *cand_score,
                      int64_t *reuse_out, double *reuse_score,
                      int64_t *refine_out, double *refine_score)
+{
+    return orc_pivot_groups_ex(Q, W, K, L, q_len, H, d, g, c, k, ORC_PROXY_MEAN, 0, groups, ngroups,
+                               cand_in, cand_out, cand_score, reuse_out, reuse_score, refine_out,
+                               refine_score);
+}
+
+/* orc_pivot_groups with the proxy of orc_proxy_ex(proxy, window). */
+int orc_pivot_groups_ex(const uint16_t *Q, const float *W, const uint16_t *K,
+                        int64_t L, int64_t q_len, int H, int d,
+                        int64_t g, int64_t c, int64_t k, int proxy, int64_t window,
+                        const int64_t *groups, int64_t ngroups,
+                        const int64_t *cand_in,
+                        int64_t *cand_out, double *cand_score,
+                        int64_t *reuse_out, double *reuse_score,
+                        int64_t *refine_out, double *refine_score)
 {
     if (!Q || !W || !K || !groups || !cand_out || !reuse_out || !refine_out ||
         L < 1 || q_len < 1 || q_len > L || g < 1 || c < 1 || k < 1)
@@ -305,7 +378,7 @@ int orc_pivot_groups(const uint16_t *Q, const float *W, const uint16_t *K,
         int64_t t_last = L - q_len + r1 - 1;
         int64_t n = t_last + 1;
 
-        rc = orc_proxy(Q, W, q_len, H, d, g, m, qbar, wbar);
+        rc = orc_proxy_ex(Q, W, q_len, H, d, g, m, proxy, window, qbar, wbar);
         if (rc != ORC_OK)
             break;
         rc = orc_scores(qbar, wbar, K, H, d, n, sc, NULL);

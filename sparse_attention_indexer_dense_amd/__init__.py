@@ -55,12 +55,12 @@ def load(path: str = LIB_PATH):
     for f in (lib.indexer_pivot_reuse, lib.indexer_pivot_refine):
         f.argtypes = [P, P, P, i32, i64, i64, i32, i32, i32, i32, i32, P, P, P, P, sz, P]
         f.restype = i32
-    lib.indexer_varlen_workspace_bytes.argtypes = [i32, i32, P, P, i32, i32, i32, i32, i32, i64]
+    lib.indexer_varlen_workspace_bytes.argtypes = [i32, i32, P, P, i32, i32, i32, i32, i32, P]
     lib.indexer_varlen_workspace_bytes.restype = sz
     lib.indexer_dense_varlen.argtypes = [P, P, P, i32, P, P, i32, i32, i32, P, P, P, sz, P]
     lib.indexer_dense_varlen.restype = i32
     for f in (lib.indexer_pivot_reuse_varlen, lib.indexer_pivot_refine_varlen):
-        f.argtypes = [P, P, P, i32, P, P, i32, i32, i32, i32, i32, i64, P, P, P, P, sz, P]
+        f.argtypes = [P, P, P, i32, P, P, i32, i32, i32, i32, i32, P, P, P, P, P, sz, P]
         f.restype = i32
     lib.indexer_last_error.argtypes = []
     lib.indexer_last_error.restype = ctypes.c_char_p
@@ -92,8 +92,16 @@ def indexer_pivot_refine(Q, W, K, B, L, q_len, H_I, d_I, g, c, k, out_idx, out_s
                                        out_cand, ws, ws_bytes, stream)
 
 
-def indexer_varlen_workspace_bytes(mode, B, L, q_len, H_I, d_I, g, c, k, guard):
-    return load().indexer_varlen_workspace_bytes(mode, B, L, q_len, H_I, d_I, g, c, k, guard)
+class PivotOpts(ctypes.Structure):
+    """dsaidx_pivot_opts: guard, proxy strategy, proxy window."""
+    _fields_ = [("guard", ctypes.c_int64), ("proxy", ctypes.c_int32), ("window", ctypes.c_int32)]
+
+
+PROXY = {"mean": 0, "first": 1, "last": 2}
+
+
+def indexer_varlen_workspace_bytes(mode, B, L, q_len, H_I, d_I, g, c, k, opts):
+    return load().indexer_varlen_workspace_bytes(mode, B, L, q_len, H_I, d_I, g, c, k, opts)
 
 
 def indexer_dense_varlen(Q, W, K, B, L, q_len, H_I, d_I, k, out_idx, out_score, ws, ws_bytes, stream):
@@ -101,15 +109,15 @@ def indexer_dense_varlen(Q, W, K, B, L, q_len, H_I, d_I, k, out_idx, out_score, 
                                        ws_bytes, stream)
 
 
-def indexer_pivot_reuse_varlen(Q, W, K, B, L, q_len, H_I, d_I, g, c, k, guard, out_idx, out_score,
+def indexer_pivot_reuse_varlen(Q, W, K, B, L, q_len, H_I, d_I, g, c, k, opts, out_idx, out_score,
                                out_cand, ws, ws_bytes, stream):
-    return load().indexer_pivot_reuse_varlen(Q, W, K, B, L, q_len, H_I, d_I, g, c, k, guard, out_idx,
+    return load().indexer_pivot_reuse_varlen(Q, W, K, B, L, q_len, H_I, d_I, g, c, k, opts, out_idx,
                                              out_score, out_cand, ws, ws_bytes, stream)
 
 
-def indexer_pivot_refine_varlen(Q, W, K, B, L, q_len, H_I, d_I, g, c, k, guard, out_idx, out_score,
+def indexer_pivot_refine_varlen(Q, W, K, B, L, q_len, H_I, d_I, g, c, k, opts, out_idx, out_score,
                                 out_cand, ws, ws_bytes, stream):
-    return load().indexer_pivot_refine_varlen(Q, W, K, B, L, q_len, H_I, d_I, g, c, k, guard, out_idx,
+    return load().indexer_pivot_refine_varlen(Q, W, K, B, L, q_len, H_I, d_I, g, c, k, opts, out_idx,
                                               out_score, out_cand, ws, ws_bytes, stream)
 
 
@@ -230,11 +238,15 @@ def _varlen_shapes(Q, W, K, L, q_len):
     return len(L), arr(*L), arr(*q_len), H, d
 
 
-def _run_varlen(mode, Q, W, K, L, q_len, k, g=1, c=0, guard=0, scores=True, cand=False, ws=None):
+def _run_varlen(mode, Q, W, K, L, q_len, k, g=1, c=0, guard=0, proxy="mean", window=0, scores=True,
+                cand=False, ws=None):
     import torch
     B, La, qa, H, d = _varlen_shapes(Q, W, K, L, q_len)
     dev = Q.device
-    need = indexer_varlen_workspace_bytes(mode, B, La, qa, H, d, g, c, k, guard)
+    if proxy not in PROXY:
+        raise ValueError(f"proxy must be one of {sorted(PROXY)}")
+    opts = ctypes.byref(PivotOpts(int(guard), PROXY[proxy], int(window)))
+    need = indexer_varlen_workspace_bytes(mode, B, La, qa, H, d, g, c, k, opts)
     wsb = (ws or _default_ws).get(need, dev)
     nq = Q.shape[0]
     out_idx = torch.empty((nq, k), dtype=torch.int32, device=dev)
@@ -247,7 +259,7 @@ def _run_varlen(mode, Q, W, K, L, q_len, k, g=1, c=0, guard=0, scores=True, cand
                                   _ptr(out_score), _ptr(wsb), wsb.numel(), stream)
     else:
         f = indexer_pivot_reuse_varlen if mode == REUSE else indexer_pivot_refine_varlen
-        rc = f(_ptr(Q), _ptr(W), _ptr(K), B, La, qa, H, d, g, c, k, guard, _ptr(out_idx),
+        rc = f(_ptr(Q), _ptr(W), _ptr(K), B, La, qa, H, d, g, c, k, opts, _ptr(out_idx),
                _ptr(out_score), _ptr(out_cand), _ptr(wsb), wsb.numel(), stream)
     _check(rc)
     return out_idx, out_score, out_cand
@@ -259,13 +271,15 @@ def dense_varlen(Q, W, K, L, q_len, k, scores=True, ws=None):
     return i, s
 
 
-def pivot_reuse_varlen(Q, W, K, L, q_len, g, k, c=0, guard=0, scores=True, cand=False, ws=None):
+def pivot_reuse_varlen(Q, W, K, L, q_len, g, k, c=0, guard=0, proxy="mean", window=0, scores=True,
+                       cand=False, ws=None):
     """PIVOT-Reuse over packed requests: (idx, score or None, cand [sum G, c] or None)."""
-    return _run_varlen(REUSE, Q, W, K, L, q_len, k, g=g, c=c, guard=guard, scores=scores,
-                       cand=cand, ws=ws)
+    return _run_varlen(REUSE, Q, W, K, L, q_len, k, g=g, c=c, guard=guard, proxy=proxy,
+                       window=window, scores=scores, cand=cand, ws=ws)
 
 
-def pivot_refine_varlen(Q, W, K, L, q_len, g, c, k, guard=0, scores=True, cand=False, ws=None):
+def pivot_refine_varlen(Q, W, K, L, q_len, g, c, k, guard=0, proxy="mean", window=0, scores=True,
+                        cand=False, ws=None):
     """PIVOT-Refine over packed requests: (idx, score or None, cand [sum G, c] or None)."""
-    return _run_varlen(REFINE, Q, W, K, L, q_len, k, g=g, c=c, guard=guard, scores=scores,
-                       cand=cand, ws=ws)
+    return _run_varlen(REFINE, Q, W, K, L, q_len, k, g=g, c=c, guard=guard, proxy=proxy,
+                       window=window, scores=scores, cand=cand, ws=ws)

@@ -121,6 +121,8 @@ struct Batch {
     int64_t L = 0, q_len = 0;  // uniform values; varlen: the largest request's
     int64_t m0 = 0;            // uniform: guarded groups per request
     int64_t g = 1;
+    int proxy = DSAIDX_PROXY_MEAN;
+    int64_t window = 0;
     int64_t total_q = 0, total_G = 0, total_keys = 0;
     int64_t max_G = 0;
     int64_t max_dense_rows = 0;    // PIVOT: rows of guarded groups (largest request)
@@ -198,8 +200,15 @@ int uniform_batch(int B, int64_t L, int64_t q_len, int64_t g, Batch &b)
     return DSAIDX_OK;
 }
 
-int varlen_batch(int B, const int64_t *L, const int64_t *q_len, int64_t g, int64_t guard, Batch &b)
+int varlen_batch(int B, const int64_t *L, const int64_t *q_len, int64_t g, const dsaidx_pivot_opts *opts, Batch &b)
 {
+    const int64_t guard = opts ? opts->guard : 0;
+    const int proxy = opts ? opts->proxy : DSAIDX_PROXY_MEAN;
+    const int64_t window = opts ? opts->window : 0;
+    if (proxy != DSAIDX_PROXY_MEAN && proxy != DSAIDX_PROXY_FIRST && proxy != DSAIDX_PROXY_LAST)
+        return fail(DSAIDX_EINVAL, "unknown proxy strategy %d", proxy);
+    if (window < 0)
+        return fail(DSAIDX_EINVAL, "window=%lld must be >= 0", (long long)window);
     if (B < 1 || B > 65535)
         return fail(DSAIDX_EINVAL, "B=%d must be in [1, 65535]", B);
     if (!L || !q_len)
@@ -210,6 +219,8 @@ int varlen_batch(int B, const int64_t *L, const int64_t *q_len, int64_t g, int64
     b.B = B;
     b.varlen = true;
     b.g = g;
+    b.proxy = proxy;
+    b.window = window;
     for (int i = 0; i < B; ++i) {
         const int s = check_sizes(L[i], q_len[i], "request ", i);
         if (s != DSAIDX_OK)
@@ -542,6 +553,8 @@ int run_pivot(int mode, const Batch &b, const void *Qv, const float *W, const vo
     pp.g = b.g;
     pp.m0 = b.m0;
     pp.gmax = b.max_G;
+    pp.proxy = b.proxy;
+    pp.window = b.window;
     pp.Qp = Qp;
     pp.Wp = Wp;
     e = launch_pool(H, D, pp, stream);
@@ -712,7 +725,7 @@ int indexer_pivot_refine(const void *Q, const float *W, const void *K, int B, in
 }
 
 size_t indexer_varlen_workspace_bytes(int mode, int B, const int64_t *L, const int64_t *q_len, int H_I, int d_I,
-                                      int g, int c, int k, int64_t guard)
+                                      int g, int c, int k, const dsaidx_pivot_opts *opts)
 {
     if (mode != DSAIDX_DENSE && mode != DSAIDX_REUSE && mode != DSAIDX_REFINE) {
         fail(DSAIDX_EINVAL, "unknown mode %d", mode);
@@ -723,7 +736,8 @@ size_t indexer_varlen_workspace_bytes(int mode, int B, const int64_t *L, const i
         return 0;
     }
     Batch b;
-    if (varlen_batch(B, L, q_len, mode == DSAIDX_DENSE ? 1 : g, mode == DSAIDX_DENSE ? 0 : guard, b) != DSAIDX_OK)
+    if (varlen_batch(B, L, q_len, mode == DSAIDX_DENSE ? 1 : g, mode == DSAIDX_DENSE ? nullptr : opts, b) !=
+        DSAIDX_OK)
         return 0;
     return workspace_for(mode, b, H_I, d_I, c, k);
 }
@@ -733,35 +747,35 @@ int indexer_dense_varlen(const void *Q, const float *W, const void *K, int B, co
                          void *ws, size_t ws_bytes, hipStream_t stream)
 {
     Batch b;
-    int s = varlen_batch(B, L, q_len, 1, 0, b);
+    int s = varlen_batch(B, L, q_len, 1, nullptr, b);
     if (s != DSAIDX_OK)
         return s;
     return run_dense_call(b, Q, W, K, H_I, d_I, k, out_idx, out_score, ws, ws_bytes, stream);
 }
 
 int indexer_pivot_reuse_varlen(const void *Q, const float *W, const void *K, int B, const int64_t *L,
-                               const int64_t *q_len, int H_I, int d_I, int g, int c, int k, int64_t guard,
-                               int32_t *out_idx, float *out_score, int32_t *out_cand, void *ws, size_t ws_bytes,
-                               hipStream_t stream)
+                               const int64_t *q_len, int H_I, int d_I, int g, int c, int k,
+                               const dsaidx_pivot_opts *opts, int32_t *out_idx, float *out_score,
+                               int32_t *out_cand, void *ws, size_t ws_bytes, hipStream_t stream)
 {
     if (g < 1)
         return fail(DSAIDX_EINVAL, "g=%d must be >= 1", g);
     Batch b;
-    int s = varlen_batch(B, L, q_len, g, guard, b);
+    int s = varlen_batch(B, L, q_len, g, opts, b);
     if (s != DSAIDX_OK)
         return s;
     return run_pivot(DSAIDX_REUSE, b, Q, W, K, H_I, d_I, c, k, out_idx, out_score, out_cand, ws, ws_bytes, stream);
 }
 
 int indexer_pivot_refine_varlen(const void *Q, const float *W, const void *K, int B, const int64_t *L,
-                                const int64_t *q_len, int H_I, int d_I, int g, int c, int k, int64_t guard,
-                                int32_t *out_idx, float *out_score, int32_t *out_cand, void *ws, size_t ws_bytes,
-                                hipStream_t stream)
+                                const int64_t *q_len, int H_I, int d_I, int g, int c, int k,
+                                const dsaidx_pivot_opts *opts, int32_t *out_idx, float *out_score,
+                                int32_t *out_cand, void *ws, size_t ws_bytes, hipStream_t stream)
 {
     if (g < 1)
         return fail(DSAIDX_EINVAL, "g=%d must be >= 1", g);
     Batch b;
-    int s = varlen_batch(B, L, q_len, g, guard, b);
+    int s = varlen_batch(B, L, q_len, g, opts, b);
     if (s != DSAIDX_OK)
         return s;
     return run_pivot(DSAIDX_REFINE, b, Q, W, K, H_I, d_I, c, k, out_idx, out_score, out_cand, ws, ws_bytes, stream);

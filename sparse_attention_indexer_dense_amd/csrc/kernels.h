@@ -99,6 +99,8 @@ struct PoolParams {
     int B;
     int64_t L, q_len, g, m0;
     int64_t gmax;  // groups of the largest request
+    int proxy;     // 0: mean of `window` members ending at the last (0: all), 1: first, 2: last member
+    int64_t window;
     uint16_t *Qp;  // [groups][H][D]
     float *Wp;     // [groups][H]
 };

@@ -655,9 +655,10 @@ void scan_select_kernel(ScanParams p)
 }
 
 // -------------------------------------------------------------- pooling
-// Proxy of group m (PIVOT, experimental setup: mean pooling per head): the
-// members' queries summed in row order in fp32, divided by the member count
-// (IEEE division), rounded to bf16 nearest-even; weights likewise in fp32.
+// Proxy of group m (PIVOT, experimental setup: mean pooling per head, within
+// a window; ablation: endpoint proxies): the averaged members' queries summed
+// in row order in fp32, divided by their count (IEEE division), rounded to
+// bf16 nearest-even; weights likewise in fp32.
 template <int H, int D>
 __global__ __launch_bounds__(256) void pool_kernel(PoolParams p)
 {
@@ -667,8 +668,18 @@ __global__ __launch_bounds__(256) void pool_kernel(PoolParams p)
     if (m < rq.m0 || m >= rq.G)
         return;  // guarded, or beyond the request's groups
     const int64_t grp = rq.g_off + m;
-    const int64_t r0 = m * p.g;
-    const int64_t r1 = (r0 + p.g < rq.q_len) ? r0 + p.g : rq.q_len;
+    const int64_t g0 = m * p.g;
+    const int64_t g1 = (g0 + p.g < rq.q_len) ? g0 + p.g : rq.q_len;
+    // the members averaged: a window ending at the group's last row, or one
+    // endpoint member
+    int64_t r0 = g0, r1 = g1;
+    if (p.proxy == 1) {
+        r1 = g0 + 1;
+    } else if (p.proxy == 2) {
+        r0 = g1 - 1;
+    } else if (p.window > 0 && p.window < g1 - g0) {
+        r0 = g1 - p.window;
+    }
     const float n = (float)(r1 - r0);
     const uint16_t *Qb = p.Q + rq.q_off * H * D;
     const float *Wb = p.W + rq.q_off * H;

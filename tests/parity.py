@@ -62,7 +62,7 @@ def check_dense(Q, W, K, k, rows=None, out=None):
     return res, idx, sc
 
 
-def check_pivot_rows(variant, idx, sc, cand, hv, L, q_len, g, c, k, groups):
+def check_pivot_rows(variant, idx, sc, cand, hv, L, q_len, g, c, k, groups, kind="mean", window=0):
     """Check PIVOT outputs (host arrays) for `groups` [(b, m)]: candidates vs the
     oracle's proxy scan, Reuse rows vs the proxy top-k (identical within a
     group), Refine rows vs the oracle re-scoring the GPU's own candidates."""
@@ -71,7 +71,7 @@ def check_pivot_rows(variant, idx, sc, cand, hv, L, q_len, g, c, k, groups):
         r0, r1 = m * g, min(m * g + g, q_len)
         t_last = L - q_len + r1 - 1
         Qm, Wm = hv.rows(b, r0, r1)
-        qb, wb = oracle.proxy(Qm, Wm, g, 0)
+        qb, wb = oracle.proxy(Qm, Wm, g, 0, kind=kind, window=window)
         univ = None
         if cand is not None or variant == "reuse":
             ref, mass = oracle.scores(qb, wb, hv.keys(b), n=t_last + 1)
@@ -124,7 +124,8 @@ def merge(dst, src):
     return dst
 
 
-def check_varlen(variant, Q, W, K, L, q_len, g, c, k, guard, out, max_groups=None, seed=0):
+def check_varlen(variant, Q, W, K, L, q_len, g, c, k, guard, out, max_groups=None, seed=0,
+                 kind="mean", window=0):
     """Check the outputs of a packed batch of requests (variant dense, reuse or
     refine). out = (idx [sum q_len, k], score, cand [sum G, c] or None) on the
     GPU. Rows of guarded groups must hold their dense selection and their
@@ -158,7 +159,8 @@ def check_varlen(variant, Q, W, K, L, q_len, g, c, k, guard, out, max_groups=Non
         if max_groups is not None and len(groups) > max_groups:
             pick = set(rng.choice(groups, max_groups, replace=False).tolist()) | {groups[0], groups[-1]}
             groups = sorted(pick)
-        rc, rr = check_pivot_rows(variant, ib, sb, cb, hv, Lb, qb, g, c, k, [(0, m) for m in groups])
+        rc, rr = check_pivot_rows(variant, ib, sb, cb, hv, Lb, qb, g, c, k, [(0, m) for m in groups],
+                                  kind=kind, window=window)
         merge(res_c, rc)
         merge(res_r, rr)
     return res_d, res_c, res_r

@@ -341,6 +341,35 @@ def pin_short_last_group(lib):
     assert np.all(o["refine"][0, 2:] == -1)
 
 
+def pin_proxy_strategies(lib):
+    """Endpoint proxies are the endpoint member exactly; a window of w members
+    is the mean of the group's last w rows (the mean of two bf16 values is
+    exact before rounding); a window as wide as the group is the group mean;
+    with g = 1 every strategy is the row itself."""
+    rng = np.random.default_rng(23)
+    L, H, d, g = 12, 2, 4, 4
+    Q, W, K = rand_inputs(rng, L, H, d)
+    for m in (0, 1, 2):
+        r0, r1 = m * g, min(m * g + g, L)
+        qf, wf = oracle.proxy(Q, W, g, m, kind="first", lib=lib)
+        assert np.array_equal(qf, Q[r0]) and np.array_equal(wf, W[r0])
+        ql, wl = oracle.proxy(Q, W, g, m, kind="last", lib=lib)
+        assert np.array_equal(ql, Q[r1 - 1]) and np.array_equal(wl, W[r1 - 1])
+        q1, w1 = oracle.proxy(Q, W, g, m, kind="mean", window=1, lib=lib)
+        assert np.array_equal(q1, Q[r1 - 1]) and np.array_equal(w1, W[r1 - 1])
+        q2, w2 = oracle.proxy(Q, W, g, m, kind="mean", window=2, lib=lib)
+        mean2 = (bits_to_f64(Q[r1 - 2]) + bits_to_f64(Q[r1 - 1])) / 2
+        assert np.array_equal(bits_to_f64(q2), bits_to_f64(bf16_bits(mean2)))
+        assert np.array_equal(w2, ((W[r1 - 2] + W[r1 - 1]) / np.float32(2)).astype(np.float32))
+        qa, wa = oracle.proxy(Q, W, g, m, lib=lib)
+        qw, ww = oracle.proxy(Q, W, g, m, kind="mean", window=g, lib=lib)
+        assert np.array_equal(qa, qw) and np.array_equal(wa, ww)
+    for kind in ("first", "last", "mean"):
+        o1 = oracle.pivot_groups(Q, W, K, 1, 5, 3, [4], kind=kind, lib=lib)
+        ref = oracle.dense_rows(Q, W, K, 3, [4], lib=lib)
+        assert np.array_equal(o1["reuse"][0], ref[0][0])
+
+
 ALL_PINS = [
     pin_golden_scores,
     pin_golden_topk,
@@ -354,4 +383,5 @@ ALL_PINS = [
     pin_pivot_invariants,
     pin_candidate_injection,
     pin_short_last_group,
+    pin_proxy_strategies,
 ]

@@ -105,9 +105,10 @@ def test_refine_requires_c_ge_k():
     assert "c=" in dsa.indexer_last_error()
 
 
-def varlen_ws(mode, L, q, g=4, c=512, k=256, guard=0, H=64, d=128):
+def varlen_ws(mode, L, q, g=4, c=512, k=256, guard=0, H=64, d=128, proxy=0, window=0):
     arr = ctypes.c_int64 * len(L)
-    return dsa.indexer_varlen_workspace_bytes(mode, len(L), arr(*L), arr(*q), H, d, g, c, k, guard)
+    opts = ctypes.byref(dsa.PivotOpts(guard, proxy, window))
+    return dsa.indexer_varlen_workspace_bytes(mode, len(L), arr(*L), arr(*q), H, d, g, c, k, opts)
 
 
 def test_varlen_workspace_sizes():
@@ -119,6 +120,9 @@ def test_varlen_workspace_sizes():
     assert varlen_ws(dsa.DENSE, [100, 50], [100, 60]) == 0   # q_len > L
     assert varlen_ws(dsa.DENSE, [0], [0]) == 0
     assert varlen_ws(dsa.REFINE, [100], [100], guard=-1) == 0
+    assert varlen_ws(dsa.REFINE, [100], [100], proxy=3) == 0
+    assert varlen_ws(dsa.REFINE, [100], [100], window=-2) == 0
+    assert varlen_ws(dsa.REFINE, [100], [100], proxy=2, window=4) > 0
 
 
 def test_varlen_rejects_bad_arguments():
@@ -127,13 +131,17 @@ def test_varlen_rejects_bad_arguments():
     rc = dsa.indexer_dense_varlen(fake(), fake(), fake(), 2, L, q, 64, 128, 64, fake(), None, fake(),
                                   1 << 40, None)
     assert rc == EINVAL and "q_len" in dsa.indexer_last_error()
-    rc = dsa.indexer_pivot_refine_varlen(fake(), fake(), fake(), 2, None, q, 64, 128, 4, 128, 64, 0,
+    rc = dsa.indexer_pivot_refine_varlen(fake(), fake(), fake(), 2, None, q, 64, 128, 4, 128, 64, None,
                                          fake(), None, None, fake(), 1 << 40, None)
     assert rc == EINVAL
     L, q = arr(1000, 50), arr(1000, 50)
-    rc = dsa.indexer_pivot_reuse_varlen(fake(), fake(), fake(), 2, L, q, 64, 128, 0, 128, 64, 0,
+    rc = dsa.indexer_pivot_reuse_varlen(fake(), fake(), fake(), 2, L, q, 64, 128, 0, 128, 64, None,
                                         fake(), None, None, fake(), 1 << 40, None)
     assert rc == EINVAL
-    rc = dsa.indexer_pivot_refine_varlen(fake(), fake(), fake(), 2, L, q, 64, 128, 4, 32, 64, 0,
+    rc = dsa.indexer_pivot_refine_varlen(fake(), fake(), fake(), 2, L, q, 64, 128, 4, 32, 64, None,
                                          fake(), None, None, fake(), 1 << 40, None)
     assert rc == EINVAL  # c < k
+    bad = ctypes.byref(dsa.PivotOpts(0, 7, 0))
+    rc = dsa.indexer_pivot_refine_varlen(fake(), fake(), fake(), 2, L, q, 64, 128, 4, 128, 64, bad,
+                                         fake(), None, None, fake(), 1 << 40, None)
+    assert rc == EINVAL and "proxy" in dsa.indexer_last_error()

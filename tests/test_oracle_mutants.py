@@ -34,8 +34,11 @@ MUTANTS = {
     "proxy_not_divided": ("qbar[x] = float_to_bf16_rne(acc / cnt);", "qbar[x] = float_to_bf16_rne(acc);"),
     "proxy_truncates": ("u += 0x7FFFu + lsb;", "u += 0u * lsb;"),
     "proxy_rounds_half_up": ("u += 0x7FFFu + lsb;", "u += 0x8000u + 0u * lsb;"),
-    "proxy_count_is_g": ("float cnt = (float)(r1 - r0);", "float cnt = (float)g;"),
-    "proxy_weight_first_member": ("wbar[j] = acc / cnt;", "wbar[j] = W[r0 * H + j];"),
+    "proxy_count_is_g": ("int64_t wn = (window == 0 || window >= n) ? n : window;",
+                         "int64_t wn = (window == 0 || window >= n) ? g : window;"),
+    "proxy_weight_first_member": ("wbar[j] = acc / cnt;", "wbar[j] = W[a * H + j];"),
+    "proxy_window_from_first_member": ("        a = r1 - wn;\n", "        a = r0;\n"),
+    "proxy_last_is_first": ("        a = r1 - 1;\n", "        a = r0;\n        b = r0 + 1;\n        (void)0;\n"),
     "refine_not_causal": ("if (cand[x] >= 0 && cand[x] <= pos)", "if (cand[x] >= 0 && cand[x] <= t_last)"),
     "scan_stops_early": ("int64_t t_last = L - q_len + r1 - 1;", "int64_t t_last = L - q_len + r1 - 2;"),
     "scan_starts_group": ("int64_t t_last = L - q_len + r1 - 1;", "int64_t t_last = L - q_len + r0;"),
