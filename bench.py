@@ -10,7 +10,7 @@ recall of Reuse/Refine against dense, a decode step (32 requests x 65536
 cached keys, 2 new rows each, Refine) against the HBM roofline, and the CPU
 oracle timed on a bounded sample of the same workload.
 
-usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--sweep]
 """
 from __future__ import annotations
 
@@ -184,6 +184,53 @@ def bench_decode(dsa, synth, torch, iters=20, warmup=3):
             "hbm_frac": gbs / PEAK_HBM_GBS, "recall_vs_dense": rec}
 
 
+# -------------------------------------------------------------------- sweep
+SWEEP_G = (2, 4, 8, 16)
+SWEEP_C = (2048, 4096, 8192)
+SWEEP_PROXY = (("mean", 0), ("mean", 4), ("first", 0), ("last", 0))
+
+
+def sweep(dsa, torch, Q, W, K, k, steps=2):
+    """Recall of Reuse and Refine against dense, and kernel time, over group
+    sizes, candidate budgets and proxy strategies (one sequence). Prints one
+    JSON line per configuration."""
+    Qp, Wp, Kp = Q[0].contiguous(), W[0].contiguous(), K[0].contiguous()
+    L, q = [K.shape[1]], [Q.shape[1]]
+    ws = dsa.Workspace()
+
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(steps):
+            out = fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return out, e0.elapsed_time(e1) / steps
+
+    (d_idx, _), d_ms = timed(lambda: dsa.dense_varlen(Qp, Wp, Kp, L, q, k, scores=False, ws=ws))
+    print(json.dumps({"sweep": "dense", "ms": d_ms}), flush=True)
+    for g in SWEEP_G:
+        for kind, window in SWEEP_PROXY:
+            if window and window >= g:
+                continue
+            (r_idx, _, _), r_ms = timed(lambda: dsa.pivot_reuse_varlen(
+                Qp, Wp, Kp, L, q, g, k, proxy=kind, window=window, scores=False, ws=ws))
+            print(json.dumps({"sweep": "reuse", "g": g, "proxy": kind, "window": window, "ms": r_ms,
+                              "speedup_vs_dense": d_ms / r_ms, "recall_vs_dense": recall(r_idx, d_idx)}),
+                  flush=True)
+            del r_idx
+            for c in SWEEP_C:
+                (f_idx, _, _), f_ms = timed(lambda: dsa.pivot_refine_varlen(
+                    Qp, Wp, Kp, L, q, g, c, k, proxy=kind, window=window, scores=False, ws=ws))
+                print(json.dumps({"sweep": "refine", "g": g, "c": c, "proxy": kind, "window": window,
+                                  "ms": f_ms, "speedup_vs_dense": d_ms / f_ms,
+                                  "recall_vs_dense": recall(f_idx, d_idx)}), flush=True)
+                del f_idx
+
+
 # --------------------------------------------------------------------- main
 def main():
     ap = argparse.ArgumentParser()
@@ -196,6 +243,8 @@ def main():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run one 1 GiB device copy (counter calibration)")
+    ap.add_argument("--sweep", action="store_true",
+                    help="instead of the step: recall and time of Reuse/Refine over g, c and proxy")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the indexer is not "
@@ -219,6 +268,9 @@ def main():
     B, L, q_len, H, d = dsa._shapes(Q, W, K)
     k, g, c = w.k, w.g, w.c
     variants = list(w.variants)
+    if args.sweep:
+        sweep(dsa, torch, Q, W, K, k)
+        return
 
     def alloc(cand_c=None):
         G = (q_len + g - 1) // g
