@@ -31,9 +31,10 @@ CFLAGS = ["-O2", "-std=c99", "-fPIC", "-shared", "-fno-fast-math", "-ffp-contrac
 
 def build(src: str = _SRC, out: str = _LIB) -> str:
     """Compile the oracle with gcc. Returns the path of the shared library."""
-    cmd = ["gcc", *CFLAGS, src, "-o", out + ".tmp", "-lm"]
+    tmp = f"{out}.{os.getpid()}.tmp"  # parallel builders never share a file
+    cmd = ["gcc", *CFLAGS, src, "-o", tmp, "-lm"]
     subprocess.run(cmd, check=True)
-    os.replace(out + ".tmp", out)
+    os.replace(tmp, out)
     return out
 
 
@@ -65,8 +66,13 @@ def _bind(lib):
     lib.orc_proxy_ex.argtypes = [P, P, i64, i32, i32, i64, i64, i32, i64, P, P]
     lib.orc_pivot_groups_ex.argtypes = [P, P, P, i64, i64, i32, i32, i64, i64, i64, i32, i64,
                                         P, i64, P, P, P, P, P, P, P]
+    lib.orc_chunk_means.argtypes = [P, i64, i32, P, i64, P]
+    lib.orc_chunk_adaptive.argtypes = [P, i64, i32, i64, P]
+    lib.orc_chunk_groups.argtypes = [P, P, P, i64, i64, i32, i32, i64, i32, i64, P, i64, i64, i64, i64,
+                                     P, i64, P, P, P, P, P]
     for f in (lib.orc_scores, lib.orc_select, lib.orc_dense_rows, lib.orc_proxy,
-              lib.orc_pivot_groups, lib.orc_proxy_ex, lib.orc_pivot_groups_ex):
+              lib.orc_pivot_groups, lib.orc_proxy_ex, lib.orc_pivot_groups_ex,
+              lib.orc_chunk_means, lib.orc_chunk_adaptive, lib.orc_chunk_groups):
         f.restype = ctypes.c_int
     return lib
 
@@ -179,6 +185,60 @@ def pivot_groups(Q, W, K, g, c, k, groups, cand_in=None, kind="mean", window=0, 
         _p(out["cand"]), _p(out["cand_score"]), _p(out["reuse"]),
         _p(out["reuse_score"]), _p(out["refine"]), _p(out["refine_score"])),
         "pivot_groups")
+    return out
+
+
+# ------------------------------------------------- key chunks (coarse stage)
+def fixed_chunks(L, block):
+    """Chunk ends of fixed blocks of ``block`` keys (the last one short when
+    ``block`` does not divide L): the fixed-block hierarchical baseline of the
+    SCALE paper's abstract (HISA-64 at block = 64)."""
+    return np.minimum(np.arange(1, -(-L // block) + 1, dtype=np.int64) * block, L).astype(np.int32)
+
+
+def adaptive_chunks(K, block, lib=None):
+    """Score-adaptive chunk ends (the reading of SCALE's split/merge rule that
+    ``oracle.c`` states) for keys K [L, d]: ceil(L / block) chunks."""
+    lib = lib or load()
+    K = _u16(K)
+    L, d = K.shape
+    out = np.empty(-(-L // block), np.int32)
+    _check(lib.orc_chunk_adaptive(_p(K), L, d, block, _p(out)), "chunk_adaptive")
+    return out
+
+
+def chunk_means(K, cend, lib=None):
+    """Mean key (bf16 bits [nc, d]) of every chunk of K [L, d]."""
+    lib = lib or load()
+    K = _u16(K)
+    L, d = K.shape
+    cend = np.ascontiguousarray(cend, dtype=np.int32)
+    out = np.empty((cend.size, d), np.uint16)
+    _check(lib.orc_chunk_means(_p(K), L, d, _p(cend), cend.size, _p(out)), "chunk_means")
+    return out
+
+
+def chunk_groups(Q, W, K, g, cend, nsel, cw, k, groups, kind="mean", window=0, lib=None):
+    """Coarse chunk scan, candidate expansion and token-level Refine for groups
+    ``groups``. Returns a dict with chunks/chunk_score [ng, nsel] (selected
+    chunks ascending), cand [ng, cw] (ascending keys, -1 padded) and
+    refine/refine_score [ng, g, k]."""
+    lib = lib or load()
+    Q, K, W = _u16(Q), _u16(K), _f32(W)
+    q_len, H, d = Q.shape
+    L = K.shape[0]
+    cend = np.ascontiguousarray(cend, dtype=np.int32)
+    groups = np.ascontiguousarray(groups, dtype=np.int64)
+    ng = groups.size
+    out = dict(
+        chunks=np.empty((ng, nsel), np.int64), chunk_score=np.empty((ng, nsel), np.float64),
+        cand=np.empty((ng, cw), np.int64),
+        refine=np.empty((ng, g, k), np.int64), refine_score=np.empty((ng, g, k), np.float64),
+    )
+    _check(lib.orc_chunk_groups(
+        _p(Q), _p(W), _p(K), L, q_len, H, d, g, PROXY[kind], window, _p(cend), cend.size, nsel, cw, k,
+        _p(groups), ng, _p(out["chunks"]), _p(out["chunk_score"]), _p(out["cand"]),
+        _p(out["refine"]), _p(out["refine_score"])), "chunk_groups")
     return out
 
 

@@ -436,3 +436,338 @@ int orc_pivot_groups_ex(const uint16_t *Q, const float *W, const uint16_t *K,
     free(qbar); free(wbar); free(sc); free(csc); free(cidx); free(cur);
     return rc;
 }
+
+/* ------------------------------------------------------------------------
+ * Key-axis coarse stage: hierarchical indexing over contiguous key chunks.
+ *
+ * Sources. "Not All Tokens Deserve Equal Resolution: Score-Adaptive Indexing
+ * for Sparse Attention in Long-Context LLMs" (SCALE), abstract: contiguous
+ * regions of keys are represented by compact summaries, the summary of a
+ * chunk is its mean key, candidates are chosen at chunk level and refined
+ * with the token-level indexer; fixed-size blocks (HISA-64: one summary per
+ * 64 keys) are the baseline, and SCALE re-partitions the keys under the same
+ * chunk budget by splitting high-dispersion regions and merging homogeneous
+ * neighbours. The PIVOT paper names the same token-axis approach (HISA) in
+ * its experimental setup and results.
+ *
+ * Chunks are given by their exclusive ends cend[0..nc): chunk b holds keys
+ * [cend[b-1], cend[b]) (cend[-1] = 0), ascending, cend[nc-1] = L.
+ * ------------------------------------------------------------------------ */
+
+static int valid_chunks(const int32_t *cend, int64_t nc, int64_t L)
+{
+    if (!cend || nc < 1 || cend[nc - 1] != L)
+        return 0;
+    int64_t prev = 0;
+    for (int64_t b = 0; b < nc; ++b) {
+        if (cend[b] <= prev)
+            return 0;
+        prev = cend[b];
+    }
+    return 1;
+}
+
+/*
+ * Mean key of every chunk (the summary; SCALE abstract: the mean key is the
+ * best single representative of a chunk in squared error). Reading of the
+ * unstated precision, the same as for the query proxy: per dimension, an fp32
+ * sum over the chunk's keys in index order, an fp32 division by the number of
+ * keys, bf16 rounding (nearest, ties to even). kbar is [nc][d] bf16.
+ */
+int orc_chunk_means(const uint16_t *K, int64_t L, int d, const int32_t *cend, int64_t nc,
+                    uint16_t *kbar)
+{
+    if (!K || !kbar || d < 1 || L < 1 || !valid_chunks(cend, nc, L))
+        return ORC_EINVAL;
+    for (int64_t b = 0; b < nc; ++b) {
+        int64_t first = b == 0 ? 0 : cend[b - 1];
+        int64_t end = cend[b];
+        float nkeys = (float)(end - first);
+        for (int e = 0; e < d; ++e) {
+            float sum = 0.0f;
+            for (int64_t s = first; s < end; ++s)
+                sum += bf16_to_float(K[s * d + e]);
+            kbar[b * d + e] = float_to_bf16_rne(sum / nkeys);
+        }
+    }
+    return ORC_OK;
+}
+
+/*
+ * Dispersion of keys [a, b): the squared reconstruction error of the chunk by
+ * its (unrounded) mean, sum_s |k_s - mean|^2 = sum_e (sum_s k_se^2 -
+ * (sum_s k_se)^2 / n). Computed in double in a fixed order (per dimension
+ * the sums run over s in index order; the dimensions are then added in
+ * order), so that any implementation taking the same steps gets the same
+ * bits: the chunking below compares these values, and both sides of a
+ * comparison must make the same decision.
+ */
+static double dispersion(const uint16_t *K, int d, int64_t a, int64_t b)
+{
+    double n = (double)(b - a);
+    double total = 0.0;
+    for (int e = 0; e < d; ++e) {
+        double s1 = 0.0, s2 = 0.0;
+        for (int64_t s = a; s < b; ++s) {
+            double x = bf16_to_double(K[s * d + e]);
+            s1 += x;
+            s2 += x * x;
+        }
+        total += s2 - s1 * s1 / n;
+    }
+    return total;
+}
+
+typedef struct {
+    double key;
+    int64_t idx;
+} orc_rank;
+
+/* higher key first, then lower index */
+static int rank_desc(const void *pa, const void *pb)
+{
+    const orc_rank *a = pa, *b = pb;
+    if (a->key > b->key)
+        return -1;
+    if (a->key < b->key)
+        return 1;
+    return a->idx < b->idx ? -1 : (a->idx > b->idx ? 1 : 0);
+}
+
+/* lower key first, then lower index */
+static int rank_asc(const void *pa, const void *pb)
+{
+    const orc_rank *a = pa, *b = pb;
+    if (a->key < b->key)
+        return -1;
+    if (a->key > b->key)
+        return 1;
+    return a->idx < b->idx ? -1 : (a->idx > b->idx ? 1 : 0);
+}
+
+/*
+ * Score-adaptive chunking under a fixed budget (SCALE abstract: split
+ * high-dispersion regions into more chunks, merge homogeneous neighbours,
+ * keep the number of chunks). The abstract gives no procedure; the reading
+ * taken here:
+ *  - start from fixed blocks of `block` keys (block even); blocks are numbered
+ *    0..n-1, n = ceil(L / block), the last one short when block does not
+ *    divide L; only full blocks take part below;
+ *  - a split cuts a full block into its two halves; its gain is the drop in
+ *    dispersion, G = D(block) - D(first half) - D(second half);
+ *  - a merge joins the aligned pair of full blocks 2j, 2j+1 into one chunk;
+ *    its loss is M = D(pair) - D(2j) - D(2j+1);
+ *  - greedy: splits are taken in order of gain (highest first), merges in
+ *    order of loss (lowest first), ties to the lower block or pair number;
+ *    a block whose pair is merged cannot be split, and a pair with a split
+ *    block cannot be merged (such candidates are passed over); one split and
+ *    one merge are made together while the gain exceeds the loss (the total
+ *    dispersion falls with every step), and the first step where it does
+ *    not ends the procedure.
+ * Every split adds a chunk and every merge removes one, so there are n chunks,
+ * of block/2, block or 2*block keys (the last chunk may be short).
+ * cend gets the n chunk ends in key order.
+ */
+int orc_chunk_adaptive(const uint16_t *K, int64_t L, int d, int64_t block, int32_t *cend)
+{
+    if (!K || !cend || L < 1 || d < 1 || block < 2 || block % 2 || L > 2147483647LL)
+        return ORC_EINVAL;
+    int64_t n = (L + block - 1) / block;
+    int64_t nfull = L / block;
+    int64_t npair = nfull / 2;
+    orc_rank *gain = malloc(sizeof(orc_rank) * (size_t)(nfull > 0 ? nfull : 1));
+    orc_rank *loss = malloc(sizeof(orc_rank) * (size_t)(npair > 0 ? npair : 1));
+    char *split = calloc((size_t)(n > 0 ? n : 1), 1);
+    char *merged = calloc((size_t)(npair > 0 ? npair : 1), 1);
+    if (!gain || !loss || !split || !merged) {
+        free(gain); free(loss); free(split); free(merged);
+        return ORC_EINVAL;
+    }
+    int64_t h = block / 2;
+    for (int64_t b = 0; b < nfull; ++b) {
+        int64_t a = b * block;
+        gain[b].key = dispersion(K, d, a, a + block) - dispersion(K, d, a, a + h) -
+                      dispersion(K, d, a + h, a + block);
+        gain[b].idx = b;
+    }
+    for (int64_t j = 0; j < npair; ++j) {
+        int64_t a = 2 * j * block;
+        loss[j].key = dispersion(K, d, a, a + 2 * block) - dispersion(K, d, a, a + block) -
+                      dispersion(K, d, a + block, a + 2 * block);
+        loss[j].idx = j;
+    }
+    qsort(gain, (size_t)nfull, sizeof(orc_rank), rank_desc);
+    qsort(loss, (size_t)npair, sizeof(orc_rank), rank_asc);
+    int64_t ia = 0, ib = 0;
+    for (;;) {
+        /* next split candidate: a block whose pair is not merged */
+        while (ia < nfull && gain[ia].idx / 2 < npair && merged[gain[ia].idx / 2])
+            ++ia;
+        /* next merge candidate: a pair with no split block and not holding
+         * the split candidate */
+        while (ib < npair) {
+            int64_t j = loss[ib].idx;
+            int conflict = split[2 * j] || split[2 * j + 1] ||
+                           (ia < nfull && gain[ia].idx / 2 == j);
+            if (!conflict)
+                break;
+            ++ib;
+        }
+        if (ia >= nfull || ib >= npair || !(gain[ia].key > loss[ib].key))
+            break;
+        split[gain[ia].idx] = 1;
+        merged[loss[ib].idx] = 1;
+        ++ia;
+        ++ib;
+    }
+    int64_t out = 0;
+    for (int64_t b = 0; b < n; ++b) {
+        int64_t a = b * block;
+        if (b % 2 == 0 && b / 2 < npair && merged[b / 2]) {
+            cend[out++] = (int32_t)(a + 2 * block);
+            ++b;
+        } else if (split[b]) {
+            cend[out++] = (int32_t)(a + h);
+            cend[out++] = (int32_t)(a + block);
+        } else {
+            cend[out++] = (int32_t)(a + block < L ? a + block : L);
+        }
+    }
+    free(gain); free(loss); free(split); free(merged);
+    return out == n ? ORC_OK : ORC_EINVAL;
+}
+
+/*
+ * Chunk-level candidates and token-level refinement for selected groups of
+ * one sequence (positions as in orc_dense_rows; groups and proxies as in
+ * orc_pivot_groups_ex; g = 1 makes the proxy the query itself, i.e. plain
+ * per-query hierarchical indexing):
+ *  1. summaries kbar = orc_chunk_means;
+ *  2. the chunks complete at the group's last position t_last, those with
+ *     cend[b] <= t_last + 1, are scored by the proxy with the index score of
+ *     Eq. (1), the summary standing in for the key;
+ *  3. the top-nsel of them (ranking as everywhere) are the selected chunks,
+ *     written in ascending chunk order, -1 padded ([ngroups][nsel]);
+ *  4. the candidate list: the keys of the selected chunks in index order,
+ *     then the keys after the last complete chunk up to t_last (the chunk in
+ *     progress has no summary yet, and the reading taken is that its keys are
+ *     always kept), then -1 up to width cw ([ngroups][cw]; an error if the
+ *     list does not fit);
+ *  5. Refine: member i scores the candidates at or before pos(i) with its own
+ *     query and weights and keeps its top-k ([ngroups][g][k]).
+ * Score outputs may be NULL.
+ */
+int orc_chunk_groups(const uint16_t *Q, const float *W, const uint16_t *K,
+                     int64_t L, int64_t q_len, int H, int d, int64_t g, int proxy, int64_t window,
+                     const int32_t *cend, int64_t nc, int64_t nsel, int64_t cw, int64_t k,
+                     const int64_t *groups, int64_t ngroups,
+                     int64_t *chunk_out, double *chunk_score, int64_t *cand_out,
+                     int64_t *refine_out, double *refine_score)
+{
+    if (!Q || !W || !K || !groups || !chunk_out || !cand_out || !refine_out ||
+        L < 1 || q_len < 1 || q_len > L || g < 1 || nsel < 1 || cw < 1 || k < 1 ||
+        !valid_chunks(cend, nc, L))
+        return ORC_EINVAL;
+    int64_t ngroups_total = (q_len + g - 1) / g;
+    uint16_t *kbar = malloc(sizeof(uint16_t) * (size_t)nc * (size_t)d);
+    uint16_t *qbar = malloc(sizeof(uint16_t) * (size_t)H * (size_t)d);
+    float *wbar = malloc(sizeof(float) * (size_t)H);
+    double *csc = malloc(sizeof(double) * (size_t)nc);
+    int64_t *sel = malloc(sizeof(int64_t) * (size_t)nsel);
+    double *tsc = malloc(sizeof(double) * (size_t)cw);
+    int64_t *tix = malloc(sizeof(int64_t) * (size_t)cw);
+    if (!kbar || !qbar || !wbar || !csc || !sel || !tsc || !tix) {
+        free(kbar); free(qbar); free(wbar); free(csc); free(sel); free(tsc); free(tix);
+        return ORC_EINVAL;
+    }
+    int rc = orc_chunk_means(K, L, d, cend, nc, kbar);
+    for (int64_t gi = 0; gi < ngroups && rc == ORC_OK; ++gi) {
+        int64_t m = groups[gi];
+        if (m < 0 || m >= ngroups_total) {
+            rc = ORC_EINVAL;
+            break;
+        }
+        int64_t r0 = m * g;
+        int64_t r1 = r0 + g < q_len ? r0 + g : q_len;
+        int64_t t_last = (L - q_len) + r1 - 1;  /* the group's last position */
+        /* chunks complete at t_last form a prefix 0..ncomp-1 */
+        int64_t ncomp = 0;
+        while (ncomp < nc && cend[ncomp] <= t_last + 1)
+            ++ncomp;
+
+        rc = orc_proxy_ex(Q, W, q_len, H, d, g, m, proxy, window, qbar, wbar);
+        if (rc != ORC_OK)
+            break;
+        rc = orc_scores(qbar, wbar, kbar, H, d, ncomp, csc, NULL);
+        if (rc != ORC_OK)
+            break;
+        rc = orc_select(csc, NULL, ncomp, nsel, sel, NULL);
+        if (rc != ORC_OK)
+            break;
+        /* selected chunks in ascending order, -1 last */
+        int64_t nsc = ncomp < nsel ? ncomp : nsel;
+        for (int64_t x = 1; x < nsc; ++x)
+            for (int64_t y = x; y > 0 && sel[y - 1] > sel[y]; --y) {
+                int64_t t = sel[y];
+                sel[y] = sel[y - 1];
+                sel[y - 1] = t;
+            }
+        int64_t *crow = chunk_out + gi * nsel;
+        for (int64_t x = 0; x < nsel; ++x) {
+            crow[x] = x < nsc ? sel[x] : -1;
+            if (chunk_score)
+                chunk_score[gi * nsel + x] = x < nsc ? csc[sel[x]] : -INFINITY;
+        }
+        /* expansion into keys */
+        int64_t *trow = cand_out + gi * cw;
+        int64_t nt = 0;
+        for (int64_t x = 0; x < nsc && rc == ORC_OK; ++x) {
+            int64_t b = sel[x];
+            for (int64_t s = (b == 0 ? 0 : cend[b - 1]); s < cend[b]; ++s) {
+                if (nt == cw) {
+                    rc = ORC_EINVAL;
+                    break;
+                }
+                trow[nt++] = s;
+            }
+        }
+        for (int64_t s = (ncomp == 0 ? 0 : cend[ncomp - 1]); s <= t_last && rc == ORC_OK; ++s) {
+            if (nt == cw) {
+                rc = ORC_EINVAL;
+                break;
+            }
+            trow[nt++] = s;
+        }
+        if (rc != ORC_OK)
+            break;
+        for (int64_t x = nt; x < cw; ++x)
+            trow[x] = -1;
+
+        /* token-level refinement of each member */
+        for (int64_t i = 0; i < g && rc == ORC_OK; ++i) {
+            int64_t *orow = refine_out + (gi * g + i) * k;
+            double *srow = refine_score ? refine_score + (gi * g + i) * k : NULL;
+            int64_t r = r0 + i;
+            if (r >= r1) {
+                for (int64_t x = 0; x < k; ++x) {
+                    orow[x] = -1;
+                    if (srow)
+                        srow[x] = -INFINITY;
+                }
+                continue;
+            }
+            int64_t pos = L - q_len + r;
+            int64_t nv = 0;
+            for (int64_t x = 0; x < nt && rc == ORC_OK; ++x) {
+                if (trow[x] > pos)
+                    continue;
+                rc = orc_scores(Q + r * H * d, W + r * H, K + trow[x] * d, H, d, 1, tsc + nv, NULL);
+                tix[nv++] = trow[x];
+            }
+            if (rc == ORC_OK)
+                rc = orc_select(tsc, tix, nv, k, orow, srow);
+        }
+    }
+    free(kbar); free(qbar); free(wbar); free(csc); free(sel); free(tsc); free(tix);
+    return rc;
+}

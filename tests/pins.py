@@ -370,6 +370,206 @@ def pin_proxy_strategies(lib):
         assert np.array_equal(o1["reuse"][0], ref[0][0])
 
 
+# ------------------------------------------------------- key-chunk pins
+CHUNK_GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "chunk_example.txt")
+
+
+def parse_chunk_golden(path=CHUNK_GOLDEN):
+    g = dict(CK={}, CQ={}, CW={}, MEAN={}, SEL={}, CAND={}, REF={}, CEND=None)
+    with open(path) as f:
+        for line in f:
+            line = line.split("#", 1)[0].strip()
+            if not line:
+                continue
+            head, vals = line.split(":", 1)
+            h = head.split()
+            tag, keys = h[0], tuple(int(x) for x in h[1:])
+            v = [float(x) for x in vals.split()]
+            if tag == "CEND":
+                g[tag] = [int(x) for x in v]
+            elif tag in ("CK", "CQ", "CW", "MEAN"):
+                g[tag][keys[0]] = v
+            else:
+                g[tag][keys] = [int(x) for x in v]
+    L = len(g["CK"])
+    K = bf16_bits(np.array([g["CK"][s] for s in range(L)], np.float32))
+    Q = bf16_bits(np.array([[g["CQ"][t]] for t in range(L)], np.float32))
+    W = np.array([g["CW"][t] for t in range(L)], np.float32)
+    g["arrays"] = (Q, W, K)
+    return g
+
+
+def chunk_dispersion(Kf):
+    """Squared reconstruction error of a chunk by its mean (numpy, fp64)."""
+    return float(((Kf - Kf.mean(axis=0)) ** 2).sum())
+
+
+def pin_golden_chunks(lib):
+    g = parse_chunk_golden()
+    Q, W, K = g["arrays"]
+    L = K.shape[0]
+    cend = oracle.fixed_chunks(L, 2)
+    assert cend.tolist() == g["CEND"]
+    kb = oracle.chunk_means(K, cend, lib=lib)
+    for b, want in g["MEAN"].items():
+        assert bits_to_f64(kb[b]).tolist() == want, (b, bits_to_f64(kb[b]))
+    cw, k = 8, 2
+    for gs, nsel in ((1, 2), (1, 1), (2, 1)):
+        ng = -(-L // gs)
+        o = oracle.chunk_groups(Q, W, K, gs, cend, nsel, cw, k, list(range(ng)), lib=lib)
+        for m in range(ng):
+            assert o["chunks"][m].tolist() == g["SEL"][(gs, nsel, m)], (gs, nsel, m, o["chunks"][m])
+            want = g["CAND"][(gs, nsel, m)]
+            assert o["cand"][m].tolist() == want + [-1] * (cw - len(want)), (gs, nsel, m, o["cand"][m])
+            for i in range(gs):
+                r = m * gs + i
+                if r < L:
+                    assert o["refine"][m, i].tolist() == g["REF"][(gs, nsel, r)], (gs, nsel, r)
+
+
+def pin_chunk_means_closed_forms(lib):
+    """Chunks of equal keys average to that key; three keys x-u, x, x+u average
+    to x (the fp32 sum 3x is exact); a short last chunk divides by its own
+    size; one-key chunks are the keys."""
+    rng = np.random.default_rng(31)
+    d = 6
+    base = bf16_bits(rng.standard_normal((4, d)))
+    K = np.empty((11, d), np.uint16)
+    K[0:4] = base[0]
+    K[4:8] = base[1]
+    x = bits_to_f64(bf16_bits(np.full(d, 1.5)))
+    K[8:11] = bf16_bits(np.stack([x - 0.25, x, x + 0.25]))
+    kb = oracle.chunk_means(K, oracle.fixed_chunks(11, 4), lib=lib)
+    assert np.array_equal(kb[0], base[0]) and np.array_equal(kb[1], base[1])
+    assert np.array_equal(bits_to_f64(kb[2]), x)
+    Kr = bf16_bits(rng.standard_normal((9, d)))
+    assert np.array_equal(oracle.chunk_means(Kr, oracle.fixed_chunks(9, 1), lib=lib), Kr)
+    # uneven chunks [0,2) [2,3) [3,9): the middle one is its key
+    kb2 = oracle.chunk_means(Kr, np.array([2, 3, 9], np.int32), lib=lib)
+    assert np.array_equal(kb2[1], Kr[2])
+    m01 = (bits_to_f64(Kr[0]) + bits_to_f64(Kr[1])) / 2  # exact for two bf16 values
+    assert np.array_equal(bits_to_f64(kb2[0]), bits_to_f64(bf16_bits(m01)))
+
+
+def pin_chunk_reductions(lib):
+    """One key per chunk makes the coarse stage the token scan: with nsel = c
+    the candidates are PIVOT's top-c set and Refine is PIVOT-Refine. A budget
+    of every chunk makes the candidates the whole prefix: Refine is dense."""
+    rng = np.random.default_rng(32)
+    L, H, d, k = 40, 3, 8, 5
+    Q, W, K = rand_inputs(rng, L, H, d)
+    for g, c in ((1, 7), (4, 9)):
+        ng = -(-L // g)
+        o = oracle.chunk_groups(Q, W, K, g, oracle.fixed_chunks(L, 1), c, c, k, list(range(ng)), lib=lib)
+        p = oracle.pivot_groups(Q, W, K, g, c, k, list(range(ng)), lib=lib)
+        assert np.array_equal(o["refine"], p["refine"])
+        for m in range(ng):
+            assert sorted(o["cand"][m][o["cand"][m] >= 0].tolist()) == sorted(
+                p["cand"][m][p["cand"][m] >= 0].tolist())
+    dense, _ = oracle.dense_rows(Q, W, K, k, list(range(L)), lib=lib)
+    for g, blk in ((1, 4), (3, 3), (5, 6)):
+        cend = oracle.fixed_chunks(L, blk)
+        ng = -(-L // g)
+        o = oracle.chunk_groups(Q, W, K, g, cend, cend.size, L + blk, k, list(range(ng)), lib=lib)
+        for m in range(ng):
+            for i in range(g):
+                r = m * g + i
+                if r < L:
+                    assert np.array_equal(o["refine"][m, i], dense[r]), (g, blk, r)
+            t_last = min(m * g + g, L) - 1
+            assert o["cand"][m].tolist() == list(range(t_last + 1)) + [-1] * (L + blk - t_last - 1)
+
+
+def pin_chunk_selection(lib):
+    """The selected chunks are the top-nsel complete chunks by the proxy's
+    score of their summaries (lexsort), the list holds exactly their keys and
+    the tail keys in ascending order, and Refine keeps the top-k of the
+    member's own scores over the causal part of that list."""
+    rng = np.random.default_rng(33)
+    L, H, d, k, g, nsel, blk = 45, 2, 8, 4, 3, 3, 4
+    Q, W, K = rand_inputs(rng, L, H, d)
+    cend = np.array([3, 4, 8, 10, 16, 17, 20, 28, 30, 31, 36, 40, 45], np.int32)
+    starts = np.concatenate([[0], cend[:-1]])
+    kb = oracle.chunk_means(K, cend, lib=lib)
+    ng = -(-L // g)
+    cw = nsel * 8 + 8
+    o = oracle.chunk_groups(Q, W, K, g, cend, nsel, cw, k, list(range(ng)), lib=lib)
+    for m in range(ng):
+        t_last = min(m * g + g, L) - 1
+        ncomp = int(np.sum(cend <= t_last + 1))
+        qb, wb = oracle.proxy(Q, W, g, m, lib=lib)
+        sc, _ = oracle.scores(qb, wb, kb, n=ncomp, lib=lib)
+        order = np.lexsort((np.arange(ncomp), -sc))
+        want = sorted(order[:nsel].tolist())
+        assert o["chunks"][m].tolist() == want + [-1] * (nsel - len(want)), m
+        keys = [s for b in want for s in range(starts[b], cend[b])]
+        tail0 = cend[ncomp - 1] if ncomp else 0
+        keys += list(range(tail0, t_last + 1))
+        assert o["cand"][m].tolist() == keys + [-1] * (cw - len(keys)), m
+        for i in range(g):
+            r = m * g + i
+            if r >= L:
+                assert np.all(o["refine"][m, i] == -1)
+                continue
+            mine = [s for s in keys if s <= r]
+            ss = np.array([oracle.scores(Q[r], W[r], K[s:s + 1], lib=lib)[0][0] for s in mine])
+            top = np.lexsort((np.array(mine), -ss))[:k]
+            got = o["refine"][m, i]
+            assert got[got >= 0].tolist() == [mine[j] for j in top], (m, i)
+
+
+def pin_adaptive_chunks(lib):
+    """Split/merge chunking: no change on keys with no dispersion; a
+    constructed case with two worthwhile split/merge steps; ties between
+    equal gains go to the lower block; on random keys a partition of n chunks
+    of half, one or two blocks whose total dispersion is at most that of the
+    fixed blocks, with as many splits as merges, merges aligned to pairs."""
+    d, blk = 2, 4
+    K = bf16_bits(np.full((32, d), 0.75))
+    assert oracle.adaptive_chunks(K, blk, lib=lib).tolist() == oracle.fixed_chunks(32, blk).tolist()
+
+    def build(blocks):
+        return bf16_bits(np.array([row for b in blocks for row in b], np.float32))
+
+    const = lambda v: [[v, v]] * 4
+    halves = lambda a, b: [a, a, b, b]
+    K2 = build([const(1), const(1), halves([0, 0], [4, 4]), const(3),
+                const(-1), const(-1), halves([1, 0], [-1, 0]), const(5)])
+    assert oracle.adaptive_chunks(K2, blk, lib=lib).tolist() == [8, 10, 12, 16, 24, 26, 28, 32]
+    K3 = build([const(1), const(1), halves([0, 0], [4, 4]), const(100),
+                const(0), const(10), halves([0, 0], [4, 4]), const(-100)])
+    assert oracle.adaptive_chunks(K3, blk, lib=lib).tolist() == [8, 10, 12, 16, 20, 24, 28, 32]
+
+    rng = np.random.default_rng(34)
+    for L, blk in ((256, 8), (203, 8), (96, 4)):
+        scale = np.repeat(rng.uniform(0.05, 2.0, -(-L // blk)), blk)[:L, None]
+        Kr = bf16_bits(rng.standard_normal((L, 6)) * scale)
+        Kf = bits_to_f64(Kr)
+        cend = oracle.adaptive_chunks(Kr, blk, lib=lib)
+        n = -(-L // blk)
+        assert cend.size == n and cend[-1] == L and np.all(np.diff(cend) > 0)
+        starts = np.concatenate([[0], cend[:-1]])
+        sizes = cend - starts
+        nsplit = nmerge = 0
+        for a, e, sz in zip(starts, cend, sizes):
+            if sz == blk // 2:
+                nsplit += 1
+                assert a % (blk // 2) == 0
+            elif sz == 2 * blk:
+                nmerge += 1
+                assert a % (2 * blk) == 0
+            else:
+                assert sz == blk or e == L, (a, e)
+        assert nsplit == 2 * nmerge  # a split block appears as two half chunks
+        fixed = oracle.fixed_chunks(L, blk)
+        fstarts = np.concatenate([[0], fixed[:-1]])
+        tot = sum(chunk_dispersion(Kf[a:e]) for a, e in zip(starts, cend))
+        tot_fixed = sum(chunk_dispersion(Kf[a:e]) for a, e in zip(fstarts, fixed))
+        assert tot <= tot_fixed + 1e-9 * tot_fixed
+        if L == 256:
+            assert nmerge > 0  # the uneven scales make some steps worthwhile
+
+
 ALL_PINS = [
     pin_golden_scores,
     pin_golden_topk,
@@ -384,4 +584,9 @@ ALL_PINS = [
     pin_candidate_injection,
     pin_short_last_group,
     pin_proxy_strategies,
+    pin_golden_chunks,
+    pin_chunk_means_closed_forms,
+    pin_chunk_reductions,
+    pin_chunk_selection,
+    pin_adaptive_chunks,
 ]

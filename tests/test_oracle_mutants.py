@@ -42,6 +42,32 @@ MUTANTS = {
     "refine_not_causal": ("if (cand[x] >= 0 && cand[x] <= pos)", "if (cand[x] >= 0 && cand[x] <= t_last)"),
     "scan_stops_early": ("int64_t t_last = L - q_len + r1 - 1;", "int64_t t_last = L - q_len + r1 - 2;"),
     "scan_starts_group": ("int64_t t_last = L - q_len + r1 - 1;", "int64_t t_last = L - q_len + r0;"),
+    "chunk_mean_not_divided": ("float_to_bf16_rne(sum / nkeys);", "float_to_bf16_rne(sum);"),
+    "chunk_mean_first_chunk_size": ("float nkeys = (float)(end - first);", "float nkeys = (float)cend[0];"),
+    "chunk_mean_skips_first_key": ("for (int64_t s = first; s < end; ++s)", "for (int64_t s = first + 1; s < end; ++s)"),
+    "chunk_in_progress_scored": ("cend[ncomp] <= t_last + 1)", "(ncomp == 0 ? 0 : cend[ncomp - 1]) <= t_last)"),
+    "chunk_complete_strict": ("cend[ncomp] <= t_last + 1)", "cend[ncomp] < t_last + 1)"),
+    "tail_dropped": ("s <= t_last && rc == ORC_OK; ++s) {", "s < 0 && rc == ORC_OK; ++s) {"),
+    "tail_starts_late": ("for (int64_t s = (ncomp == 0 ? 0 : cend[ncomp - 1]); s <=",
+                         "for (int64_t s = (ncomp == 0 ? 0 : cend[ncomp - 1]) + 1; s <="),
+    "chunk_refine_not_causal": ("if (trow[x] > pos)", "if (trow[x] > t_last)"),
+    "chunks_in_rank_order": ("for (int64_t x = 1; x < nsc; ++x)", "for (int64_t x = 1; x < 0; ++x)"),
+    "chunk_expansion_past_end": ("s < cend[b]; ++s) {", "s <= cend[b] && s < L; ++s) {"),
+    "dispersion_no_mean_term": ("total += s2 - s1 * s1 / n;", "total += s2;"),
+    "split_lowest_gain_first": ("qsort(gain, (size_t)nfull, sizeof(orc_rank), rank_desc);",
+                                "qsort(gain, (size_t)nfull, sizeof(orc_rank), rank_asc);"),
+    "merge_highest_loss_first": ("qsort(loss, (size_t)npair, sizeof(orc_rank), rank_asc);",
+                                 "qsort(loss, (size_t)npair, sizeof(orc_rank), rank_desc);"),
+    "gain_ties_to_higher_block": ("a->key < b->key)\n        return 1;\n    return a->idx < b->idx ? -1 : (a->idx > b->idx ? 1 : 0);",
+                                  "a->key < b->key)\n        return 1;\n    return a->idx > b->idx ? -1 : (a->idx < b->idx ? 1 : 0);"),
+    "chunk_group_ends_early": ("int64_t t_last = (L - q_len) + r1 - 1;", "int64_t t_last = (L - q_len) + r1 - 2;"),
+    "chunk_group_at_first_member": ("int64_t t_last = (L - q_len) + r1 - 1;", "int64_t t_last = (L - q_len) + r0;"),
+    "greedy_accepts_equal": ("!(gain[ia].key > loss[ib].key)", "!(gain[ia].key >= loss[ib].key)"),
+    "greedy_one_step": ("        ++ia;\n        ++ib;\n", "        ++ia;\n        ++ib;\n        break;\n"),
+    "merge_ignores_split_blocks": ("int conflict = split[2 * j] || split[2 * j + 1] ||", "int conflict = 0 ||"),
+    "split_ignores_merged_pair": ("while (ia < nfull && gain[ia].idx / 2 < npair && merged[gain[ia].idx / 2])",
+                                  "while (ia < nfull && 0)"),
+    "split_point_off": ("cend[out++] = (int32_t)(a + h);", "cend[out++] = (int32_t)(a + h + 1);"),
 }
 
 
