@@ -208,6 +208,86 @@ int indexer_pivot_refine_varlen(const void *Q, const float *W, const void *K,
                                 int32_t *out_idx, float *out_score, int32_t *out_cand,
                                 void *ws, size_t ws_bytes, hipStream_t stream);
 
+/* ------------------------------------------------------------------------
+ * Key-axis coarse stage: hierarchical indexing over chunks of keys.
+ *
+ * "Not All Tokens Deserve Equal Resolution: Score-Adaptive Indexing for
+ * Sparse Attention in Long-Context LLMs" (SCALE), abstract: contiguous runs
+ * of keys ("chunks") are represented by their mean key; a query scores the
+ * summaries, keeps the best chunks and refines their keys with the
+ * token-level indexer. Fixed blocks of 64 keys are the HISA-64 baseline;
+ * SCALE re-partitions the keys under the same number of chunks.
+ *
+ * A partition of each request's L keys is given by its chunk ends
+ *     cend [B][nc]  int32: chunk b holds keys [cend[b-1], cend[b]) (cend[-1] =
+ *                   0); strictly ascending, cend[nc-1] = L.
+ * The summaries are
+ *     Kbar [B][nc][d_I]  bf16: per dimension, the fp32 sum of the chunk's keys
+ *                   in index order divided (IEEE fp32) by the chunk's size,
+ *                   rounded to bf16 nearest-even (a stated reading: the paper
+ *                   gives no precision).
+ * Uniform batches only (B requests of L keys, the last q_len positions queried).
+ * ------------------------------------------------------------------------ */
+
+/* Fixed blocks: cend[b] = min((b + 1) * block, L) for b < nc = ceil(L / block),
+ * for each of the B requests. cend: [B][nc] device memory. */
+int indexer_chunks_fixed(int B, int64_t L, int block, int32_t *cend, hipStream_t stream);
+
+/* Score-adaptive chunks (the reading taken of SCALE's rule; the abstract gives
+ * no procedure): start from fixed blocks of `block` keys (block even,
+ * n = ceil(L / block) blocks, at most 4096 per request). The split gain of a
+ * full block is the drop of the squared reconstruction error by the mean,
+ * D(block) - D(first half) - D(second half); the merge loss of an aligned pair
+ * of full blocks (2j, 2j+1) is D(pair) - D(2j) - D(2j+1). Splits are taken in
+ * order of gain (highest first), merges in order of loss (lowest first), ties
+ * to the lower number, a split and a merge together while the gain exceeds
+ * the loss; a block of a merged pair is not split and a pair holding a split
+ * block is not merged (such candidates are passed over). The partition keeps
+ * n chunks of block/2, block or 2*block keys (the last one may be short).
+ * D is evaluated in double precision in a fixed order (per dimension the sums
+ * of x and x*x over the keys in index order, then sum over dimensions of
+ * sum(x^2) - sum(x)^2 / n in dimension order), so the decisions are
+ * reproducible. K: [B][L][d_I] bf16; cend: [B][n] int32. ws: scratch of
+ * indexer_chunks_adaptive_workspace_bytes(B, L, block) bytes. */
+size_t indexer_chunks_adaptive_workspace_bytes(int B, int64_t L, int block);
+int indexer_chunks_adaptive(const void *K, int B, int64_t L, int d_I, int block, int32_t *cend,
+                            void *ws, size_t ws_bytes, hipStream_t stream);
+
+/* Summaries of chunks first .. nc-1 of every request (first > 0 refreshes only
+ * the chunks that changed, e.g. after keys were appended to the last one).
+ * K: [B][L][d_I] bf16; cend: [B][nc]; Kbar: [B][nc][d_I] bf16 (rows below
+ * `first` are left untouched). */
+int indexer_chunk_means(const void *K, int B, int64_t L, int d_I, const int32_t *cend, int64_t nc,
+                        int64_t first, void *Kbar, hipStream_t stream);
+
+/* Chunk-level candidates and token-level Refine. For each group of g query
+ * rows (as for PIVOT: contiguous, the last one may be shorter; proxy by
+ * opts->proxy and opts->window; g = 1 makes the proxy the row itself):
+ *  1. the chunks complete at the group's last position t_last, those with
+ *     cend <= t_last + 1, are scored by the proxy with I(t,s), the summary in
+ *     place of the key; the nsel best are kept (ranking as above);
+ *  2. the candidate list holds the keys of those chunks in index order, then
+ *     the keys after the last complete chunk up to t_last (the chunk in
+ *     progress has no summary yet and its keys are always kept), then -1, in
+ *     a row of cw = (nsel + 1) * max_chunk entries;
+ *  3. every member re-scores the candidates at or before its own position and
+ *     keeps its top-k (out_idx, out_score as for the other entry points).
+ * max_chunk: the largest chunk size in cend (block for fixed blocks, 2*block
+ * for adaptive ones); a larger chunk makes the list exceed cw and is
+ * truncated. Requires cw >= k. opts->guard must be 0.
+ *   Kbar     [B][nc][d_I]     summaries (indexer_chunk_means)
+ *   out_chunks [B][G][nsel]   int32, may be NULL: selected chunks, ascending, -1 after
+ *   out_cand [B][G][cw]       int32, may be NULL: the candidate lists
+ * ws: indexer_chunk_refine_workspace_bytes(...) bytes. */
+size_t indexer_chunk_refine_workspace_bytes(int B, int64_t L, int64_t q_len, int H_I, int d_I, int g,
+                                            int64_t nc, int nsel, int max_chunk, int k);
+int indexer_chunk_refine(const void *Q, const float *W, const void *K, const void *Kbar,
+                         const int32_t *cend, int64_t nc, int B, int64_t L, int64_t q_len,
+                         int H_I, int d_I, int g, int nsel, int max_chunk, int k,
+                         const dsaidx_pivot_opts *opts, int32_t *out_idx, float *out_score,
+                         int32_t *out_chunks, int32_t *out_cand,
+                         void *ws, size_t ws_bytes, hipStream_t stream);
+
 /* Message of the last non-OK return on the calling thread ("" if none). */
 const char *indexer_last_error(void);
 

@@ -5,9 +5,12 @@ This module only marshals arguments: the functions named like the C entry
 points (``indexer_dense``, ``indexer_pivot_reuse``, ``indexer_pivot_refine``,
 their ``*_varlen`` forms for batches of requests of different lengths,
 ``indexer_workspace_bytes``, ``indexer_varlen_workspace_bytes``,
+the key-chunk coarse stage ``indexer_chunks_fixed``, ``indexer_chunks_adaptive``,
+``indexer_chunk_means``, ``indexer_chunk_refine`` with their workspace queries,
 ``indexer_last_error``, ``indexer_version``) take raw device pointers and
 sizes, exactly as the C functions do. ``dense``, ``pivot_reuse``,
-``pivot_refine`` and their ``*_varlen`` forms take torch tensors on the GPU,
+``pivot_refine``, their ``*_varlen`` forms, ``chunks_fixed``,
+``chunks_adaptive``, ``chunk_means`` and ``chunk_refine`` take torch tensors on the GPU,
 allocate the outputs and the workspace with torch (device memory and the
 current stream are the only things torch provides) and call the same entry
 points. Every step of the computation runs in the library's HIP kernels;
@@ -25,7 +28,9 @@ DENSE, REUSE, REFINE = 0, 1, 2
 STATUS = {0: "OK", 1: "EINVAL", 2: "EUNSUPPORTED", 3: "EWORKSPACE", 4: "EHIP"}
 EXPORTS = ("indexer_workspace_bytes", "indexer_dense", "indexer_pivot_reuse",
            "indexer_pivot_refine", "indexer_varlen_workspace_bytes", "indexer_dense_varlen",
-           "indexer_pivot_reuse_varlen", "indexer_pivot_refine_varlen", "indexer_last_error",
+           "indexer_pivot_reuse_varlen", "indexer_pivot_refine_varlen", "indexer_chunks_fixed",
+           "indexer_chunks_adaptive_workspace_bytes", "indexer_chunks_adaptive", "indexer_chunk_means",
+           "indexer_chunk_refine_workspace_bytes", "indexer_chunk_refine", "indexer_last_error",
            "indexer_version")
 
 
@@ -62,6 +67,19 @@ def load(path: str = LIB_PATH):
     for f in (lib.indexer_pivot_reuse_varlen, lib.indexer_pivot_refine_varlen):
         f.argtypes = [P, P, P, i32, P, P, i32, i32, i32, i32, i32, P, P, P, P, P, sz, P]
         f.restype = i32
+    lib.indexer_chunks_fixed.argtypes = [i32, i64, i32, P, P]
+    lib.indexer_chunks_fixed.restype = i32
+    lib.indexer_chunks_adaptive_workspace_bytes.argtypes = [i32, i64, i32]
+    lib.indexer_chunks_adaptive_workspace_bytes.restype = sz
+    lib.indexer_chunks_adaptive.argtypes = [P, i32, i64, i32, i32, P, P, sz, P]
+    lib.indexer_chunks_adaptive.restype = i32
+    lib.indexer_chunk_means.argtypes = [P, i32, i64, i32, P, i64, i64, P, P]
+    lib.indexer_chunk_means.restype = i32
+    lib.indexer_chunk_refine_workspace_bytes.argtypes = [i32, i64, i64, i32, i32, i32, i64, i32, i32, i32]
+    lib.indexer_chunk_refine_workspace_bytes.restype = sz
+    lib.indexer_chunk_refine.argtypes = [P, P, P, P, P, i64, i32, i64, i64, i32, i32, i32, i32, i32, i32, P,
+                                         P, P, P, P, P, sz, P]
+    lib.indexer_chunk_refine.restype = i32
     lib.indexer_last_error.argtypes = []
     lib.indexer_last_error.restype = ctypes.c_char_p
     lib.indexer_version.argtypes = []
@@ -119,6 +137,33 @@ def indexer_pivot_refine_varlen(Q, W, K, B, L, q_len, H_I, d_I, g, c, k, opts, o
                                 out_cand, ws, ws_bytes, stream):
     return load().indexer_pivot_refine_varlen(Q, W, K, B, L, q_len, H_I, d_I, g, c, k, opts, out_idx,
                                               out_score, out_cand, ws, ws_bytes, stream)
+
+
+def indexer_chunks_fixed(B, L, block, cend, stream):
+    return load().indexer_chunks_fixed(B, L, block, cend, stream)
+
+
+def indexer_chunks_adaptive_workspace_bytes(B, L, block):
+    return load().indexer_chunks_adaptive_workspace_bytes(B, L, block)
+
+
+def indexer_chunks_adaptive(K, B, L, d_I, block, cend, ws, ws_bytes, stream):
+    return load().indexer_chunks_adaptive(K, B, L, d_I, block, cend, ws, ws_bytes, stream)
+
+
+def indexer_chunk_means(K, B, L, d_I, cend, nc, first, Kbar, stream):
+    return load().indexer_chunk_means(K, B, L, d_I, cend, nc, first, Kbar, stream)
+
+
+def indexer_chunk_refine_workspace_bytes(B, L, q_len, H_I, d_I, g, nc, nsel, max_chunk, k):
+    return load().indexer_chunk_refine_workspace_bytes(B, L, q_len, H_I, d_I, g, nc, nsel, max_chunk, k)
+
+
+def indexer_chunk_refine(Q, W, K, Kbar, cend, nc, B, L, q_len, H_I, d_I, g, nsel, max_chunk, k, opts,
+                         out_idx, out_score, out_chunks, out_cand, ws, ws_bytes, stream):
+    return load().indexer_chunk_refine(Q, W, K, Kbar, cend, nc, B, L, q_len, H_I, d_I, g, nsel, max_chunk,
+                                       k, opts, out_idx, out_score, out_chunks, out_cand, ws, ws_bytes,
+                                       stream)
 
 
 def indexer_last_error():
@@ -283,3 +328,77 @@ def pivot_refine_varlen(Q, W, K, L, q_len, g, c, k, guard=0, proxy="mean", windo
     """PIVOT-Refine over packed requests: (idx, score or None, cand [sum G, c] or None)."""
     return _run_varlen(REFINE, Q, W, K, L, q_len, k, g=g, c=c, guard=guard, proxy=proxy,
                        window=window, scores=scores, cand=cand, ws=ws)
+
+
+# ------------------------------------------------- key chunks (coarse stage)
+def _stream(dev):
+    import torch
+    return ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+
+
+def chunks_fixed(B, L, block, device="cuda"):
+    """Chunk ends of fixed blocks: int32 [B, ceil(L / block)]."""
+    import torch
+    dev = torch.device(device)
+    cend = torch.empty((B, -(-L // block)), dtype=torch.int32, device=dev)
+    _check(indexer_chunks_fixed(B, L, block, _ptr(cend), _stream(dev)))
+    return cend
+
+
+def chunks_adaptive(K, block, ws=None):
+    """Score-adaptive chunk ends of K [B, L, d] (split/merge under the
+    fixed-block budget): int32 [B, ceil(L / block)]."""
+    import torch
+    if K.dtype != torch.bfloat16 or K.dim() != 3 or not K.is_cuda or not K.is_contiguous():
+        raise ValueError("K must be a contiguous bf16 GPU tensor [B, L, d]")
+    B, L, d = K.shape
+    dev = K.device
+    need = indexer_chunks_adaptive_workspace_bytes(B, L, block)
+    wsb = (ws or _default_ws).get(need, dev)
+    cend = torch.empty((B, -(-L // block)), dtype=torch.int32, device=dev)
+    _check(indexer_chunks_adaptive(_ptr(K), B, L, d, block, _ptr(cend), _ptr(wsb), wsb.numel(),
+                                   _stream(dev)))
+    return cend
+
+
+def chunk_means(K, cend, first=0, out=None):
+    """Mean-key summaries bf16 [B, nc, d] of the chunks of K [B, L, d]."""
+    import torch
+    B, L, d = K.shape
+    nc = cend.shape[1]
+    if cend.dtype != torch.int32 or tuple(cend.shape) != (B, nc) or not cend.is_contiguous():
+        raise ValueError("cend must be contiguous int32 [B, nc]")
+    Kbar = out if out is not None else torch.empty((B, nc, d), dtype=torch.bfloat16, device=K.device)
+    _check(indexer_chunk_means(_ptr(K), B, L, d, _ptr(cend), nc, first, _ptr(Kbar), _stream(K.device)))
+    return Kbar
+
+
+def chunk_refine(Q, W, K, Kbar, cend, g, nsel, max_chunk, k, proxy="mean", window=0, scores=True,
+                 chunks=False, cand=False, ws=None):
+    """Chunk-level candidates and token-level Refine: (idx [B, q_len, k], score or
+    None, selected chunks [B, G, nsel] or None, candidate lists [B, G, cw] or
+    None), cw = (nsel + 1) * max_chunk."""
+    import torch
+    B, L, q_len, H, d = _shapes(Q, W, K)
+    nc = cend.shape[1]
+    if tuple(Kbar.shape) != (B, nc, d) or Kbar.dtype != torch.bfloat16 or not Kbar.is_contiguous():
+        raise ValueError("Kbar must be contiguous bf16 [B, nc, d]")
+    if cend.dtype != torch.int32 or tuple(cend.shape) != (B, nc) or not cend.is_contiguous():
+        raise ValueError("cend must be contiguous int32 [B, nc]")
+    if proxy not in PROXY:
+        raise ValueError(f"proxy must be one of {sorted(PROXY)}")
+    dev = Q.device
+    need = indexer_chunk_refine_workspace_bytes(B, L, q_len, H, d, g, nc, nsel, max_chunk, k)
+    wsb = (ws or _default_ws).get(need, dev)
+    G = (q_len + g - 1) // g
+    cw = (nsel + 1) * max_chunk
+    out_idx = torch.empty((B, q_len, k), dtype=torch.int32, device=dev)
+    out_score = torch.empty((B, q_len, k), dtype=torch.float32, device=dev) if scores else None
+    out_chunks = torch.empty((B, G, nsel), dtype=torch.int32, device=dev) if chunks else None
+    out_cand = torch.empty((B, G, cw), dtype=torch.int32, device=dev) if cand else None
+    opts = ctypes.byref(PivotOpts(0, PROXY[proxy], int(window)))
+    _check(indexer_chunk_refine(_ptr(Q), _ptr(W), _ptr(K), _ptr(Kbar), _ptr(cend), nc, B, L, q_len, H, d,
+                                g, nsel, max_chunk, k, opts, _ptr(out_idx), _ptr(out_score),
+                                _ptr(out_chunks), _ptr(out_cand), _ptr(wsb), wsb.numel(),
+                                _stream(dev)))
+    return out_idx, out_score, out_chunks, out_cand

@@ -377,6 +377,9 @@ struct Pass {
     const ReqDesc *req;  // device descriptors (varlen) or nullptr
     int64_t c;
     int guard_rows;      // dense pass over the rows of guarded groups
+    const int32_t *glim = nullptr;    // chunk summaries: last complete chunk per group
+    int64_t krows = 0;                // summaries per request
+    const int32_t *cand_n = nullptr;  // keys per candidate list
 };
 
 // Score + select `nrows` rows per request with the split-key kernels.
@@ -402,9 +405,12 @@ int run_split(int mode, const Pass &ps, const uint16_t *Q, const float *W, const
     sp.guard_rows = ps.guard_rows;
     sp.nrows = nrows;
     sp.rowlen = rowlen;
-    const int64_t npos_max = (mode == kRefine) ? std::min<int64_t>(ps.c, b.L) : b.L;
+    const int64_t npos_max = (mode == kRefine) ? std::min<int64_t>(ps.c, b.L) : (ps.glim ? ps.krows : b.L);
     sp.chunk = split_chunk((int64_t)b.B * nrows, npos_max, mode == kRefine);
     sp.scores = scores;
+    sp.glim = ps.glim;
+    sp.krows = ps.krows;
+    sp.cand_n = ps.cand_n;
     dim3 grid((unsigned)ceil_div(npos_max, sp.chunk), (unsigned)nrows, (unsigned)b.B);
     hipError_t e = launch_split_score(H, D, sp, grid, stream);
     if (e != hipSuccess)
@@ -431,6 +437,8 @@ int run_split(int mode, const Pass &ps, const uint16_t *Q, const float *W, const
     ss.o1_members = o1_members;
     ss.o2_idx = o2;
     ss.o2_score = s2;
+    ss.glim = ps.glim;
+    ss.cand_n = ps.cand_n;
     e = launch_split_select(ss, stream);
     if (e != hipSuccess)
         return hip_fail(e, "split select launch");
@@ -453,6 +461,9 @@ ScanParams scan_base(const Pass &ps, int mode, const uint16_t *Q, const float *W
     p.G = ceil_div(b.q_len, p.g);
     p.m0 = (mode == kDense && !ps.guard_rows) ? 0 : b.m0;
     p.guard_rows = ps.guard_rows;
+    p.glim = ps.glim;
+    p.krows = ps.krows;
+    p.cand_n = ps.cand_n;
     return p;
 }
 
@@ -671,6 +682,225 @@ size_t workspace_for(int mode, const Batch &b, int H, int D, int64_t c, int64_t 
     return total;
 }
 
+// ------------------------------------------------------------ key chunks
+// Workspace of indexer_chunk_refine: proxies, chunk limits, list lengths,
+// selected chunks and candidate lists (unless the caller takes them), and
+// one region shared by the coarse scan and Refine.
+struct ChunkPlan {
+    bool split_scan = false, split_refine = false;
+    int nw_refine = 4;
+    int cap_scan = 0, cap_refine = 0;
+    int64_t G = 0, cw = 0;
+    size_t off_proxy_q = 0, off_proxy_w = 0, off_glim = 0, off_cn = 0, off_chunks = 0, off_cand = 0;
+    size_t off_work = 0, total = 0;
+};
+
+constexpr int64_t kMaxCandWidth = (int64_t)1 << 22;
+
+int make_chunk_plan(const Batch &b, int H, int D, int64_t nc, int64_t nsel, int64_t max_chunk, int64_t k,
+                    bool have_chunks, bool have_cand, ChunkPlan &pl)
+{
+    int s = check_common(H, D, k);
+    if (s != DSAIDX_OK)
+        return s;
+    if (b.g < 1)
+        return fail(DSAIDX_EINVAL, "g=%lld must be >= 1", (long long)b.g);
+    if (nc < 1 || nc > b.L)
+        return fail(DSAIDX_EINVAL, "nc=%lld must be in [1, L=%lld]", (long long)nc, (long long)b.L);
+    if (nsel < 1 || nsel > kMaxSel)
+        return fail(DSAIDX_EINVAL, "nsel=%lld must be in [1, 2^20]", (long long)nsel);
+    if (max_chunk < 1 || max_chunk > b.L)
+        return fail(DSAIDX_EINVAL, "max_chunk=%lld must be in [1, L=%lld]", (long long)max_chunk, (long long)b.L);
+    pl = ChunkPlan{};
+    pl.cw = (nsel + 1) * max_chunk;
+    if (pl.cw > kMaxCandWidth)
+        return fail(DSAIDX_EINVAL, "(nsel + 1) * max_chunk = %lld exceeds 2^22", (long long)pl.cw);
+    if (pl.cw < k)
+        return fail(DSAIDX_EINVAL, "(nsel + 1) * max_chunk = %lld must be >= k=%lld", (long long)pl.cw,
+                    (long long)k);
+    pl.G = ceil_div(b.q_len, b.g);
+    const int64_t groups = (int64_t)b.B * pl.G;
+    size_t off = 0;
+    pl.off_proxy_q = off;
+    off += align_up((size_t)groups * H * D * sizeof(uint16_t));
+    pl.off_proxy_w = off;
+    off += align_up((size_t)groups * H * sizeof(float));
+    pl.off_glim = off;
+    off += align_up((size_t)groups * sizeof(int32_t));
+    pl.off_cn = off;
+    off += align_up((size_t)groups * sizeof(int32_t));
+    if (!have_chunks) {
+        pl.off_chunks = off;
+        off += align_up((size_t)groups * nsel * sizeof(int32_t));
+    }
+    if (!have_cand) {
+        pl.off_cand = off;
+        off += align_up((size_t)groups * pl.cw * sizeof(int32_t));
+    }
+    pl.split_scan = pl.G <= kSplitRowsMax;
+    pl.cap_scan = scan_cap(nsel, nc);
+    size_t work = pl.split_scan ? (size_t)b.B * pl.G * score_row(nc) * sizeof(float)
+                                : scan_bytes(H, D, 8, pl.cap_scan);
+    pl.split_refine = b.q_len <= kSplitRowsMax;
+    pl.nw_refine = b.g <= 4 ? 4 : 8;
+    pl.cap_refine = (int)ceil_div(pl.cw + 128, 64) * 64;
+    work = std::max(work, pl.split_refine ? (size_t)b.B * b.q_len * score_row(pl.cw) * sizeof(float)
+                                          : scan_bytes(H, D, pl.nw_refine, pl.cap_refine));
+    pl.off_work = off;
+    off += align_up(work);
+    pl.total = off;
+    return DSAIDX_OK;
+}
+
+int chunk_batch(int B, int64_t L, int64_t q_len, int g, const dsaidx_pivot_opts *opts, Batch &b)
+{
+    if (g < 1)
+        return fail(DSAIDX_EINVAL, "g=%d must be >= 1", g);
+    int s = uniform_batch(B, L, q_len, g, b);
+    if (s != DSAIDX_OK)
+        return s;
+    if (opts) {
+        if (opts->proxy != DSAIDX_PROXY_MEAN && opts->proxy != DSAIDX_PROXY_FIRST && opts->proxy != DSAIDX_PROXY_LAST)
+            return fail(DSAIDX_EINVAL, "unknown proxy strategy %d", opts->proxy);
+        if (opts->window < 0)
+            return fail(DSAIDX_EINVAL, "window=%d must be >= 0", opts->window);
+        if (opts->guard != 0)
+            return fail(DSAIDX_EINVAL, "the chunk path has no guard (opts->guard must be 0)");
+        b.proxy = opts->proxy;
+        b.window = opts->window;
+    }
+    return DSAIDX_OK;
+}
+
+int run_chunk_refine(const Batch &b, const void *Qv, const float *W, const void *Kv, const void *Kbarv,
+                     const int32_t *cend, int64_t nc, int H, int D, int64_t nsel, int64_t max_chunk, int64_t k,
+                     int32_t *out_idx, float *out_score, int32_t *out_chunks, int32_t *out_cand, void *ws,
+                     size_t ws_bytes, hipStream_t stream)
+{
+    ChunkPlan pl;
+    int s = make_chunk_plan(b, H, D, nc, nsel, max_chunk, k, out_chunks != nullptr, out_cand != nullptr, pl);
+    if (s != DSAIDX_OK)
+        return s;
+    s = check_ptrs(Qv, W, Kv, out_idx, out_score, out_cand, ws, pl.total);
+    if (s != DSAIDX_OK)
+        return s;
+    if (!Kbarv || !cend)
+        return fail(DSAIDX_EINVAL, "Kbar and cend must not be NULL");
+    if (!aligned(Kbarv, 16) || !aligned(cend, 4) || (out_chunks && !aligned(out_chunks, 4)))
+        return fail(DSAIDX_EINVAL, "Kbar must be 16-byte aligned, cend and out_chunks 4-byte aligned");
+    if (ws_bytes < pl.total)
+        return fail(DSAIDX_EWORKSPACE, "workspace of %zu bytes is below the %zu needed", ws_bytes, pl.total);
+    const uint16_t *Q = static_cast<const uint16_t *>(Qv);
+    const uint16_t *K = static_cast<const uint16_t *>(Kv);
+    const uint16_t *Kbar = static_cast<const uint16_t *>(Kbarv);
+    unsigned char *wsb = static_cast<unsigned char *>(ws);
+    uint16_t *Qp = reinterpret_cast<uint16_t *>(wsb + pl.off_proxy_q);
+    float *Wp = reinterpret_cast<float *>(wsb + pl.off_proxy_w);
+    int32_t *glim = reinterpret_cast<int32_t *>(wsb + pl.off_glim);
+    int32_t *cn = reinterpret_cast<int32_t *>(wsb + pl.off_cn);
+    int32_t *chunks = out_chunks ? out_chunks : reinterpret_cast<int32_t *>(wsb + pl.off_chunks);
+    int32_t *cand = out_cand ? out_cand : reinterpret_cast<int32_t *>(wsb + pl.off_cand);
+    float *work = reinterpret_cast<float *>(wsb + pl.off_work);
+
+    // 1. proxies
+    PoolParams pp{};
+    pp.Q = Q;
+    pp.W = W;
+    pp.B = b.B;
+    pp.L = b.L;
+    pp.q_len = b.q_len;
+    pp.g = b.g;
+    pp.m0 = 0;
+    pp.gmax = pl.G;
+    pp.proxy = b.proxy;
+    pp.window = b.window;
+    pp.Qp = Qp;
+    pp.Wp = Wp;
+    hipError_t e = launch_pool(H, D, pp, stream);
+    if (e != hipSuccess)
+        return hip_fail(e, "pool launch");
+
+    // 2. chunks complete at each group's last position
+    e = launch_chunk_limits(b.B, b.L, b.q_len, b.g, cend, nc, glim, stream);
+    if (e != hipSuccess)
+        return hip_fail(e, "chunk limit launch");
+
+    // 3. coarse scan of the summaries: top-nsel chunks per group
+    Pass ps{&b, nullptr, 0, 0};
+    ps.glim = glim;
+    ps.krows = nc;
+    if (pl.split_scan) {
+        s = run_split(kProxy, ps, Qp, Wp, Kbar, nullptr, pl.G, score_row(nc), H, D, (int)nsel, 0, chunks, nullptr, 0,
+                      nullptr, nullptr, work, stream);
+        if (s != DSAIDX_OK)
+            return s;
+    } else {
+        ScanParams p = scan_base(ps, kProxy, Qp, Wp, Kbar);
+        p.nblk_per_batch = ceil_div(pl.G, 8);
+        p.nblocks = p.nblk_per_batch * b.B;
+        p.sel = (int)nsel;
+        p.sel2 = 0;
+        p.o1_idx = chunks;
+        p.o1_score = nullptr;
+        p.o1_members = 0;
+        p.slots = reinterpret_cast<Entry *>(work);
+        p.cap = pl.cap_scan;
+        e = launch_scan_select(H, D, 8, kProxy, p, scan_grid(H, D, 8, p.nblocks), stream);
+        if (e != hipSuccess)
+            return hip_fail(e, "coarse scan launch");
+    }
+
+    // 4. candidate lists
+    ChunkExpandParams xp{};
+    xp.chunks = chunks;
+    xp.cend = cend;
+    xp.glim = glim;
+    xp.L = b.L;
+    xp.q_len = b.q_len;
+    xp.g = b.g;
+    xp.nc = nc;
+    xp.nsel = (int)nsel;
+    xp.cw = pl.cw;
+    xp.cand = cand;
+    xp.cand_n = cn;
+    e = launch_chunk_expand(xp, (int64_t)b.B * pl.G, stream);
+    if (e != hipSuccess)
+        return hip_fail(e, "expansion launch");
+
+    // 5. Refine on the lists
+    Pass pr{&b, nullptr, pl.cw, 0};
+    pr.cand_n = cn;
+    if (pl.split_refine)
+        return run_split(kRefine, pr, Q, W, K, cand, b.q_len, score_row(pl.cw), H, D, (int)k, 0, out_idx, out_score, 0,
+                         nullptr, nullptr, work, stream);
+    ScanParams p = scan_base(pr, kRefine, Q, W, K);
+    p.cand = cand;
+    p.member_chunks = ceil_div(b.g, pl.nw_refine);
+    p.nblk_per_batch = pl.G * p.member_chunks;
+    p.nblocks = p.nblk_per_batch * b.B;
+    p.sel = (int)k;
+    p.sel2 = 0;
+    p.o1_idx = out_idx;
+    p.o1_score = out_score;
+    p.slots = reinterpret_cast<Entry *>(work);
+    p.cap = pl.cap_refine;
+    e = launch_scan_select(H, D, pl.nw_refine, kRefine, p, scan_grid(H, D, pl.nw_refine, p.nblocks), stream);
+    if (e != hipSuccess)
+        return hip_fail(e, "refine launch");
+    return DSAIDX_OK;
+}
+
+int check_chunk_sizes(int B, int64_t L, int block)
+{
+    if (B < 1 || B > 65535)
+        return fail(DSAIDX_EINVAL, "B=%d must be in [1, 65535]", B);
+    if (L < 1 || L >= (int64_t)INT32_MAX)
+        return fail(DSAIDX_EINVAL, "L=%lld must be in [1, 2^31-1)", (long long)L);
+    if (block < 1)
+        return fail(DSAIDX_EINVAL, "block=%d must be >= 1", block);
+    return DSAIDX_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -781,8 +1011,108 @@ int indexer_pivot_refine_varlen(const void *Q, const float *W, const void *K, in
     return run_pivot(DSAIDX_REFINE, b, Q, W, K, H_I, d_I, c, k, out_idx, out_score, out_cand, ws, ws_bytes, stream);
 }
 
+int indexer_chunks_fixed(int B, int64_t L, int block, int32_t *cend, hipStream_t stream)
+{
+    int s = check_chunk_sizes(B, L, block);
+    if (s != DSAIDX_OK)
+        return s;
+    if (!cend || !aligned(cend, 4))
+        return fail(DSAIDX_EINVAL, "cend must be a non-NULL 4-byte aligned pointer");
+    hipError_t e = launch_chunk_fixed(B, L, block, ceil_div(L, block), cend, stream);
+    return e == hipSuccess ? DSAIDX_OK : hip_fail(e, "chunk launch");
+}
+
+size_t indexer_chunks_adaptive_workspace_bytes(int B, int64_t L, int block)
+{
+    if (check_chunk_sizes(B, L, block) != DSAIDX_OK)
+        return 0;
+    const int64_t nfull = L / block;
+    return align_up((size_t)B * nfull * sizeof(double)) + align_up((size_t)B * (nfull / 2) * sizeof(double));
+}
+
+int indexer_chunks_adaptive(const void *K, int B, int64_t L, int d_I, int block, int32_t *cend, void *ws,
+                            size_t ws_bytes, hipStream_t stream)
+{
+    int s = check_chunk_sizes(B, L, block);
+    if (s != DSAIDX_OK)
+        return s;
+    if (block < 2 || block % 2)
+        return fail(DSAIDX_EINVAL, "block=%d must be even", block);
+    if (d_I != 128 && d_I != 32)
+        return fail(DSAIDX_EUNSUPPORTED, "d_I=%d has no kernel; supported: 32, 128", d_I);
+    const int64_t n = ceil_div(L, block);
+    if (n > kAdaptBlocksMax)
+        return fail(DSAIDX_EUNSUPPORTED, "%lld blocks per request exceed the %d the adaptive partition supports",
+                    (long long)n, kAdaptBlocksMax);
+    if (!K || !cend || !aligned(K, 16) || !aligned(cend, 4))
+        return fail(DSAIDX_EINVAL, "K (16-byte aligned) and cend (4-byte aligned) must not be NULL");
+    const size_t need = indexer_chunks_adaptive_workspace_bytes(B, L, block);
+    if (need > 0 && (!ws || !aligned(ws, 16)))
+        return fail(DSAIDX_EINVAL, "ws must be a non-NULL 16-byte aligned pointer (%zu bytes needed)", need);
+    if (ws_bytes < need)
+        return fail(DSAIDX_EWORKSPACE, "workspace of %zu bytes is below the %zu needed", ws_bytes, need);
+    ChunkAdaptParams p{};
+    p.K = static_cast<const uint16_t *>(K);
+    p.L = L;
+    p.block = block;
+    p.n = n;
+    p.nfull = L / block;
+    p.npair = p.nfull / 2;
+    p.gain = static_cast<double *>(ws);
+    p.loss = reinterpret_cast<double *>(static_cast<unsigned char *>(ws) +
+                                        align_up((size_t)B * p.nfull * sizeof(double)));
+    p.cend = cend;
+    hipError_t e = launch_chunk_adaptive(d_I, B, p, stream);
+    return e == hipSuccess ? DSAIDX_OK : hip_fail(e, "adaptive chunk launch");
+}
+
+int indexer_chunk_means(const void *K, int B, int64_t L, int d_I, const int32_t *cend, int64_t nc, int64_t first,
+                        void *Kbar, hipStream_t stream)
+{
+    int s = check_chunk_sizes(B, L, 1);
+    if (s != DSAIDX_OK)
+        return s;
+    if (d_I != 128 && d_I != 32)
+        return fail(DSAIDX_EUNSUPPORTED, "d_I=%d has no kernel; supported: 32, 128", d_I);
+    if (nc < 1 || nc > L || first < 0 || first > nc)
+        return fail(DSAIDX_EINVAL, "need 1 <= nc <= L and 0 <= first <= nc (nc=%lld, first=%lld)", (long long)nc,
+                    (long long)first);
+    if (!K || !cend || !Kbar || !aligned(K, 16) || !aligned(Kbar, 16) || !aligned(cend, 4))
+        return fail(DSAIDX_EINVAL, "K, Kbar (16-byte aligned) and cend (4-byte aligned) must not be NULL");
+    if (first == nc)
+        return DSAIDX_OK;
+    hipError_t e = launch_chunk_means(d_I, static_cast<const uint16_t *>(K), B, L, cend, nc, first,
+                                      static_cast<uint16_t *>(Kbar), stream);
+    return e == hipSuccess ? DSAIDX_OK : hip_fail(e, "summary launch");
+}
+
+size_t indexer_chunk_refine_workspace_bytes(int B, int64_t L, int64_t q_len, int H_I, int d_I, int g, int64_t nc,
+                                            int nsel, int max_chunk, int k)
+{
+    Batch b;
+    if (chunk_batch(B, L, q_len, g, nullptr, b) != DSAIDX_OK)
+        return 0;
+    ChunkPlan pl;
+    if (make_chunk_plan(b, H_I, d_I, nc, nsel, max_chunk, k, false, false, pl) != DSAIDX_OK)
+        return 0;
+    return pl.total;
+}
+
+int indexer_chunk_refine(const void *Q, const float *W, const void *K, const void *Kbar, const int32_t *cend,
+                         int64_t nc, int B, int64_t L, int64_t q_len, int H_I, int d_I, int g, int nsel,
+                         int max_chunk, int k, const dsaidx_pivot_opts *opts, int32_t *out_idx, float *out_score,
+                         int32_t *out_chunks, int32_t *out_cand, void *ws, size_t ws_bytes, hipStream_t stream)
+{
+    Batch b;
+    int s = chunk_batch(B, L, q_len, g, opts, b);
+    if (s != DSAIDX_OK)
+        return s;
+    return run_chunk_refine(b, Q, W, K, Kbar, cend, nc, H_I, d_I, nsel, max_chunk, k, out_idx, out_score,
+                            out_chunks, out_cand, ws, ws_bytes, stream);
+}
+
 const char *indexer_last_error(void) { return g_last_error.c_str(); }
 
-const char *indexer_version(void) { return "dsaidx 0.2.0 gfx950"; }
+const char *indexer_version(void) { return "dsaidx 0.3.0 gfx950"; }
 
 }  // extern "C"

@@ -90,6 +90,11 @@ struct ScanParams {
     float *o2_score;
     Entry *slots;            // per (workgroup, wave) candidate buffers
     int cap;                 // entries per buffer
+    // key-chunk coarse stage (kProxy): K holds krows chunk summaries per
+    // request and group row m scans summaries 0..glim[m] (nullptr: token keys)
+    const int32_t *glim;
+    int64_t krows;
+    const int32_t *cand_n;   // kRefine: keys in each group's list (nullptr: min(c, t_last + 1))
 };
 
 struct PoolParams {
@@ -121,6 +126,9 @@ struct SplitScoreParams {
     int64_t rowlen;       // positions per score row (L, or c for kRefine)
     int64_t chunk;        // positions per workgroup
     float *scores;        // [B][nrows][rowlen]
+    const int32_t *glim;  // as in ScanParams
+    int64_t krows;
+    const int32_t *cand_n;
 };
 
 struct SplitSelectParams {
@@ -138,6 +146,32 @@ struct SplitSelectParams {
     int o1_members;
     int32_t *o2_idx;
     float *o2_score;
+    const int32_t *glim;  // as in ScanParams
+    const int32_t *cand_n;
+};
+
+// Key chunks (chunks.hip).
+struct ChunkExpandParams {
+    const int32_t *chunks;  // selected chunks [B][G][nsel], ascending, -1 after the last
+    const int32_t *cend;    // chunk ends [B][nc]
+    const int32_t *glim;    // last complete chunk of each group [B][G]
+    int64_t L, q_len, g, nc;
+    int nsel;
+    int64_t cw;             // candidate row width
+    int32_t *cand;          // [B][G][cw]
+    int32_t *cand_n;        // [B][G]
+};
+
+// Adaptive chunking: at most this many blocks per request (its sort runs in LDS).
+constexpr int kAdaptBlocksMax = 4096;
+
+struct ChunkAdaptParams {
+    const uint16_t *K;      // [B][L][D]
+    int64_t L, block;
+    int64_t n, nfull, npair;  // blocks, full blocks, aligned pairs of full blocks
+    double *gain;           // [B][nfull] split gains
+    double *loss;           // [B][npair] merge losses
+    int32_t *cend;          // [B][n]
 };
 
 constexpr int kSplitWaves = 4;
@@ -161,5 +195,12 @@ hipError_t launch_scan_select(int H, int D, int NW, int mode, const ScanParams &
 hipError_t launch_pool(int H, int D, const PoolParams &prm, hipStream_t stream);
 hipError_t launch_split_score(int H, int D, const SplitScoreParams &prm, dim3 grid, hipStream_t stream);
 hipError_t launch_split_select(const SplitSelectParams &prm, hipStream_t stream);
+hipError_t launch_chunk_fixed(int B, int64_t L, int64_t block, int64_t nc, int32_t *cend, hipStream_t stream);
+hipError_t launch_chunk_means(int D, const uint16_t *K, int B, int64_t L, const int32_t *cend, int64_t nc,
+                              int64_t first, uint16_t *Kbar, hipStream_t stream);
+hipError_t launch_chunk_limits(int B, int64_t L, int64_t q_len, int64_t g, const int32_t *cend, int64_t nc,
+                               int32_t *glim, hipStream_t stream);
+hipError_t launch_chunk_expand(const ChunkExpandParams &prm, int64_t groups, hipStream_t stream);
+hipError_t launch_chunk_adaptive(int D, int B, const ChunkAdaptParams &prm, hipStream_t stream);
 
 }  // namespace dsaidx

@@ -287,6 +287,14 @@ __device__ __forceinline__ void plan_block(const ScanParams &p, int64_t j, int w
         wr.lim = (int)(off + r1 - 1);
         const int64_t r1last = ((mlast + 1) * p.g < rq.q_len) ? (mlast + 1) * p.g : rq.q_len;
         bk.nkeys = rb >= 0 ? (int)(off + r1last) : 0;
+        if (p.glim) {
+            // chunk summaries: the chunks complete at the group's last
+            // position (a non-decreasing limit over the groups)
+            bk.Kb = p.K + (int64_t)bi * p.krows * D;
+            bk.L = (int)p.krows;
+            wr.lim = wr.valid ? p.glim[grow] : -1;
+            bk.nkeys = rb >= 0 ? p.glim[rq.g_off + mlast] + 1 : 0;
+        }
         // output 1: candidate rows [groups][sel] or the member rows
         if (p.o1_members) {
             const int64_t row = rq.q_off + r0;
@@ -322,7 +330,7 @@ __device__ __forceinline__ void plan_block(const ScanParams &p, int64_t j, int w
         wr.fan1 = 1;
         const int64_t t_last = off + r1 - 1;
         bk.list = p.cand + (rq.g_off + m) * p.c;
-        bk.nkeys = live ? (int)((p.c < t_last + 1) ? p.c : t_last + 1) : 0;
+        bk.nkeys = live ? (p.cand_n ? p.cand_n[rq.g_off + m] : (int)((p.c < t_last + 1) ? p.c : t_last + 1)) : 0;
     }
 }
 
@@ -535,7 +543,7 @@ void scan_select_kernel(ScanParams p)
             bool ok;
             if (MODE == kRefine) {
                 key = lb[nt * 32 + col];
-                ok = lane < 32 && col < nkeys - p0 && key <= lim;
+                ok = lane < 32 && col < nkeys - p0 && key >= 0 && key <= lim;
             } else {
                 key = p0 + col;
                 ok = lane < 32 && col <= last - p0;

@@ -64,6 +64,11 @@ __device__ __forceinline__ SplitRow split_row(const SplitScoreParams &p, int H, 
         s.q = p.Q + grow * H * D;
         s.w = p.W + grow * H;
         s.lim = (int)(off + r1 - 1);
+        if (p.glim) {  // chunk summaries complete at the group's last position
+            s.lim = p.glim[grow];
+            s.Kb = p.K + (int64_t)bi * p.krows * D;
+            s.L = (int)p.krows;
+        }
         s.npos = s.lim + 1;
     } else if (p.mode == kDense) {
         if (r >= dense_rows(rq, p.g, p.guard_rows))
@@ -85,7 +90,7 @@ __device__ __forceinline__ SplitRow split_row(const SplitScoreParams &p, int H, 
         const int64_t r1 = ((m + 1) * p.g < rq.q_len) ? (m + 1) * p.g : rq.q_len;
         const int64_t t_last = off + r1 - 1;
         s.list = p.cand + (rq.g_off + m) * p.c;
-        s.npos = (int)((p.c < t_last + 1) ? p.c : t_last + 1);
+        s.npos = p.cand_n ? p.cand_n[rq.g_off + m] : (int)((p.c < t_last + 1) ? p.c : t_last + 1);
     }
     return s;
 }
@@ -765,7 +770,7 @@ __device__ __forceinline__ void select_row(const SelRow &s, const SelOut *outs, 
     if (vlist && n > kCandCap) {
         int v = 0;
         for (int i = threadIdx.x; i < s.npos; i += kSelectThreads)
-            v += vlist[i] <= s.lim ? 1 : 0;
+            v += (vlist[i] >= 0 && vlist[i] <= s.lim) ? 1 : 0;
         n = wave_totals(wave_sum(v), 0u, 0u, sm).total;
         vlist = nullptr;
     }
@@ -799,7 +804,7 @@ __device__ __forceinline__ void select_row(const SelRow &s, const SelOut *outs, 
                 for (int x = 0; x < 4; ++x) {
                     const int px = p + x;
                     const int e = x == 0 ? lv[q].x : x == 1 ? lv[q].y : x == 2 ? lv[q].z : lv[q].w;
-                    if (px < g.b1 && (vlist == nullptr || e <= s.lim)) {
+                    if (px < g.b1 && (vlist == nullptr || (e >= 0 && e <= s.lim))) {
                         const float f = f4(v[q], x);
                         if (p + 3 >= g.b1)
                             sm.cs[px] = f;
@@ -869,11 +874,11 @@ __device__ __forceinline__ bool select_geometry(const SplitSelectParams &p, int 
             return false;
         const int64_t r0 = m * p.g;
         const int64_t r1 = (r0 + p.g < rq.q_len) ? r0 + p.g : rq.q_len;
-        s.list = nullptr;
-        s.lim = (int)(off + r1 - 1);
-        s.npos = s.lim + 1;
         const int64_t mrow = rq.q_off + r0;
         const int64_t grow = rq.g_off + m;
+        s.list = nullptr;
+        s.lim = p.glim ? p.glim[grow] : (int)(off + r1 - 1);
+        s.npos = s.lim + 1;
         if (p.o1_members) {
             o1 = p.o1_idx + mrow * p.sel;
             s1 = p.o1_score ? p.o1_score + mrow * p.sel : nullptr;
@@ -904,7 +909,7 @@ __device__ __forceinline__ bool select_geometry(const SplitSelectParams &p, int 
             const int64_t r1 = ((m + 1) * p.g < rq.q_len) ? (m + 1) * p.g : rq.q_len;
             const int64_t t_last = off + r1 - 1;
             s.list = p.cand + (rq.g_off + m) * p.c;
-            s.npos = (int)((p.c < t_last + 1) ? p.c : t_last + 1);
+            s.npos = p.cand_n ? p.cand_n[rq.g_off + m] : (int)((p.c < t_last + 1) ? p.c : t_last + 1);
         }
         const int64_t row = rq.q_off + rr;
         o1 = p.o1_idx + row * p.sel;

@@ -145,3 +145,47 @@ def test_varlen_rejects_bad_arguments():
     rc = dsa.indexer_pivot_refine_varlen(fake(), fake(), fake(), 2, L, q, 64, 128, 4, 128, 64, bad,
                                          fake(), None, None, fake(), 1 << 40, None)
     assert rc == EINVAL and "proxy" in dsa.indexer_last_error()
+
+
+def chunk_ws(B=1, L=8192, q_len=8192, H=64, d=128, g=1, nc=128, nsel=16, max_chunk=64, k=256):
+    return dsa.indexer_chunk_refine_workspace_bytes(B, L, q_len, H, d, g, nc, nsel, max_chunk, k)
+
+
+def test_chunk_workspace_sizes():
+    assert chunk_ws() > 0
+    assert chunk_ws(g=4) > 0 and chunk_ws(q_len=2, g=2) > 0
+    assert chunk_ws(nsel=3, max_chunk=32, k=256) == 0    # (nsel + 1) * max_chunk < k
+    assert chunk_ws(nc=0) == 0 and chunk_ws(nc=8193) == 0
+    assert chunk_ws(g=0) == 0 and chunk_ws(max_chunk=0) == 0
+    assert chunk_ws(H=8, d=128) == 0
+    assert dsa.indexer_chunks_adaptive_workspace_bytes(2, 8192, 64) >= 2 * 128 * 8
+    assert dsa.indexer_chunks_adaptive_workspace_bytes(0, 8192, 64) == 0
+
+
+def test_chunk_entry_points_reject_bad_arguments():
+    assert dsa.indexer_chunks_fixed(0, 100, 8, fake(), None) == EINVAL
+    assert dsa.indexer_chunks_fixed(1, 100, 0, fake(), None) == EINVAL
+    assert dsa.indexer_chunks_fixed(1, 100, 8, None, None) == EINVAL
+    big = 1 << 40
+    # adaptive: odd block, too many blocks, unsupported d
+    assert dsa.indexer_chunks_adaptive(fake(), 1, 1000, 128, 7, fake(), fake(), big, None) == EINVAL
+    rc = dsa.indexer_chunks_adaptive(fake(), 1, 4097 * 64, 128, 64, fake(), fake(), big, None)
+    assert rc == EUNSUPPORTED and "4096" in dsa.indexer_last_error()
+    assert dsa.indexer_chunks_adaptive(fake(), 1, 1000, 64, 8, fake(), fake(), big, None) == EUNSUPPORTED
+    assert dsa.indexer_chunks_adaptive(fake(), 1, 1000, 128, 8, fake(), fake(), 8, None) == EWORKSPACE
+    # summaries
+    assert dsa.indexer_chunk_means(fake(), 1, 100, 128, fake(), 0, 0, fake(), None) == EINVAL
+    assert dsa.indexer_chunk_means(fake(), 1, 100, 128, fake(), 10, 11, fake(), None) == EINVAL
+    assert dsa.indexer_chunk_means(fake(), 1, 100, 128, fake(), 10, 10, fake(), None) == OK  # nothing to do
+    # refine
+    def refine(opts=None, nc=128, nsel=16, max_chunk=64, k=256, Kbar=fake(), ws_bytes=big):
+        return dsa.indexer_chunk_refine(fake(), fake(), fake(), Kbar, fake(), nc, 1, 8192, 8192, 64, 128, 1,
+                                        nsel, max_chunk, k, opts, fake(), None, None, None, fake(), ws_bytes,
+                                        None)
+    assert refine(opts=ctypes.byref(dsa.PivotOpts(64, 0, 0))) == EINVAL
+    assert "guard" in dsa.indexer_last_error()
+    assert refine(opts=ctypes.byref(dsa.PivotOpts(0, 5, 0))) == EINVAL
+    assert refine(nsel=2, max_chunk=32) == EINVAL and ">= k" in dsa.indexer_last_error()
+    assert refine(nc=9000) == EINVAL
+    assert refine(Kbar=None) == EINVAL
+    assert refine(ws_bytes=64) == EWORKSPACE
