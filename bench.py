@@ -7,10 +7,14 @@ re-score, top-k). Inputs are resident in HBM before timing starts. The line
 printed at the end reports scored (query, key) pairs per second for the whole
 step, top-k rows per second, the dense kernel against the bf16 MFMA roofline,
 recall of Reuse/Refine against dense, a decode step (32 requests x 65536
-cached keys, 2 new rows each, Refine) against the HBM roofline, and the CPU
-oracle timed on a bounded sample of the same workload.
+cached keys, 2 new rows each, Refine) against the HBM roofline, the key-chunk
+coarse stage (fixed and score-adaptive partitions of 64-key blocks, chunk scan
+and Refine, on keys with local structure) with its recall against dense, and
+the CPU oracle timed on a bounded sample of the same workload.
 
-usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--sweep]
+usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+                       [--sweep | --chunk-sweep | --chunk-only PARTITION,G,NSEL]
+                       [--no-decode] [--no-chunks]
 """
 from __future__ import annotations
 
@@ -231,6 +235,83 @@ def sweep(dsa, torch, Q, W, K, k, steps=2):
                 del f_idx
 
 
+# ------------------------------------------------------------ key chunks
+CHUNK_BLOCK = 64
+CHUNK_CONFIGS = (("fixed", 1, 64), ("adaptive", 1, 64), ("fixed", 4, 64), ("adaptive", 4, 64))
+CHUNK_SWEEP = tuple((p, g, n) for p in ("fixed", "adaptive") for g in (1, 4, 16) for n in (32, 48, 64, 96, 128))
+
+
+def chunk_pairs(torch, cend, cand, L, q_len, g, nsel):
+    """Scored pairs of a chunk call: the coarse scan (each group against the
+    summaries of its complete chunks) plus Refine (each member against its
+    causal candidates)."""
+    G = cand.shape[1]
+    m = torch.arange(G, device=cand.device)
+    t_last = L - q_len + torch.clamp((m + 1) * g, max=q_len) - 1
+    ncomp = torch.searchsorted(cend[0].to(torch.int64), t_last + 1, right=True)
+    coarse = int(ncomp.sum())
+    refine = 0
+    for o in range(g):
+        r = m * g + (g - 1 - o)
+        live = r < q_len
+        pos = L - q_len + r
+        ok = (cand[0] >= 0) & (cand[0] <= pos[:, None]) & live[:, None]
+        refine += int(ok.sum())
+    return coarse, refine
+
+
+def bench_chunks(dsa, synth, torch, w, Q, W, configs=CHUNK_CONFIGS, steps=3):
+    """The key-chunk path at the workload's size on keys with local structure
+    (synth.keys_local): index build (fixed or adaptive partition, summaries)
+    and chunk scan + Refine, against the dense indexer on the same keys."""
+    dev = Q.device
+    L, d, k, H = w.L, w.d, w.k, w.H
+    q_len = Q.shape[1]
+    K = synth.keys_local(L, d, w.rank, w.seed, dev)[None]
+    ws = dsa.Workspace()
+
+    def timed(fn, n=steps):
+        out = fn()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(n):
+            out = fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return out, e0.elapsed_time(e1) / n
+
+    (d_idx, _), d_ms = timed(lambda: dsa.dense(Q, W, K, k, scores=False, ws=ws), 1)
+    parts = {"fixed": timed(lambda: dsa.chunks_fixed(1, L, CHUNK_BLOCK, dev)),
+             "adaptive": timed(lambda: dsa.chunks_adaptive(K, CHUNK_BLOCK, ws=ws))}
+    means = {p: timed(lambda: dsa.chunk_means(K, parts[p][0])) for p in parts}
+    (p_idx, _, _), p_ms = timed(lambda: dsa.pivot_refine(Q, W, K, 4, 4096, k, scores=False, ws=ws))
+    res = {"keys": "synth.keys_local", "block": CHUNK_BLOCK, "dense_ms": d_ms,
+           "pivot_refine_g4_c4096": {"ms": p_ms, "speedup_vs_dense": d_ms / p_ms,
+                                     "recall_vs_dense": recall(p_idx, d_idx)},
+           "index_build_ms": {p: parts[p][1] + means[p][1] for p in parts},
+           "partition_ms": {p: parts[p][1] for p in parts},
+           "summary_ms": {p: means[p][1] for p in parts}, "runs": []}
+    del p_idx
+    flop_per_pair = 2 * H * d
+    for part, g, nsel in configs:
+        cend, Kbar = parts[part][0], means[part][0]
+        mc = 2 * CHUNK_BLOCK if part == "adaptive" else CHUNK_BLOCK
+        (idx, _, _, cand), ms = timed(lambda: dsa.chunk_refine(Q, W, K, Kbar, cend, g, nsel, mc, k,
+                                                               scores=False, cand=True, ws=ws))
+        coarse, refine = chunk_pairs(torch, cend, cand, L, q_len, g, nsel)
+        print(f"[bench] chunks {part} g={g} nsel={nsel}: {ms:.2f} ms", file=sys.stderr, flush=True)
+        res["runs"].append({"partition": part, "g": g, "nsel": nsel, "max_chunk": mc, "ms": ms,
+                            "speedup_vs_dense": d_ms / ms, "recall_vs_dense": recall(idx, d_idx),
+                            "coarse_pairs": coarse, "refine_pairs": refine,
+                            "mean_candidates": refine / q_len,
+                            "mfma_frac": (coarse + refine) * flop_per_pair / (ms * 1e-3) /
+                            (PEAK_BF16_TFLOPS * 1e12)})
+        del idx, cand
+    return res
+
+
 # --------------------------------------------------------------------- main
 def main():
     ap = argparse.ArgumentParser()
@@ -245,6 +326,12 @@ def main():
                     help="also run one 1 GiB device copy (counter calibration)")
     ap.add_argument("--sweep", action="store_true",
                     help="instead of the step: recall and time of Reuse/Refine over g, c and proxy")
+    ap.add_argument("--no-chunks", action="store_true", help="skip the key-chunk measurement")
+    ap.add_argument("--chunk-sweep", action="store_true",
+                    help="instead of the step: the key-chunk path over partitions, g and nsel")
+    ap.add_argument("--chunk-only", default=None, metavar="PARTITION,G,NSEL",
+                    help="instead of the step: build one partition and run only that chunk call "
+                         "(--steps times; for kernel traces)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the indexer is not "
@@ -270,6 +357,23 @@ def main():
     variants = list(w.variants)
     if args.sweep:
         sweep(dsa, torch, Q, W, K, k)
+        return
+    if args.chunk_only:
+        part, cg, cn = args.chunk_only.split(",")
+        del K
+        Kl = synth.keys_local(L, d, w.rank, w.seed, dev)[None]
+        cend = dsa.chunks_adaptive(Kl, CHUNK_BLOCK) if part == "adaptive" else dsa.chunks_fixed(1, L, CHUNK_BLOCK, dev)
+        Kbar = dsa.chunk_means(Kl, cend)
+        mc = 2 * CHUNK_BLOCK if part == "adaptive" else CHUNK_BLOCK
+        ws = dsa.Workspace()
+        for i in range(args.steps):
+            dsa.chunk_refine(Q, W, Kl, Kbar, cend, int(cg), int(cn), mc, k, scores=False, ws=ws)
+            torch.cuda.synchronize()
+            print(f"[bench] chunk call {i} done", file=sys.stderr, flush=True)
+        return
+    if args.chunk_sweep:
+        del K
+        print(json.dumps(bench_chunks(dsa, synth, torch, w, Q, W, configs=CHUNK_SWEEP, steps=2)), flush=True)
         return
 
     def alloc(cand_c=None):
@@ -361,6 +465,11 @@ def main():
         print("[bench] decode step", file=sys.stderr, flush=True)
         decode = bench_decode(dsa, synth, torch)
 
+    chunks = None
+    if not args.no_chunks:
+        print("[bench] key-chunk path", file=sys.stderr, flush=True)
+        chunks = bench_chunks(dsa, synth, torch, w, Q, W)
+
     cpu = None
     if args.cpu_rows > 0:
         print("[bench] cpu baseline", file=sys.stderr, flush=True)
@@ -379,6 +488,7 @@ def main():
         "variants": detail,
         "roofline": roofline,
         "decode": decode,
+        "chunks": chunks,
         "cpu_baseline": cpu,
         "wall_s_timed": wall,
         "kernel_hash": kernel_hash(),

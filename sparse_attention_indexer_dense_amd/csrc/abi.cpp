@@ -46,6 +46,8 @@ int hip_fail(hipError_t e, const char *what)
 
 // Rows per batch item at or below which a stage uses the split-key kernels.
 constexpr int64_t kSplitRowsMax = 64;
+// Rows of one split-score launch (its grid's y dimension).
+constexpr int64_t kGridYMax = 65535;
 // Persistent workgroups of the scan kernels: at most as many as fit at once
 // on the 256 CUs of an MI355X (LDS decides: one 8-wave or two 4-wave
 // workgroups per CU); the workspace holds one set of row buffers per slot.
@@ -368,6 +370,9 @@ int64_t split_chunk(int64_t rows_total, int64_t npos, bool list)
     per_wave = std::max<int64_t>(per_wave, 128);
     if (list)
         per_wave = std::min<int64_t>(per_wave, kSplitSpanMax);
+    // spread the row evenly over the workgroups it needs
+    const int64_t nchunks = ceil_div(npos, per_wave * kSplitWaves);
+    per_wave = ceil_div(ceil_div(ceil_div(npos, nchunks), kSplitWaves), 32) * 32;
     return per_wave * kSplitWaves;
 }
 
@@ -411,10 +416,15 @@ int run_split(int mode, const Pass &ps, const uint16_t *Q, const float *W, const
     sp.glim = ps.glim;
     sp.krows = ps.krows;
     sp.cand_n = ps.cand_n;
-    dim3 grid((unsigned)ceil_div(npos_max, sp.chunk), (unsigned)nrows, (unsigned)b.B);
-    hipError_t e = launch_split_score(H, D, sp, grid, stream);
-    if (e != hipSuccess)
-        return hip_fail(e, "split score launch");
+    hipError_t e = hipSuccess;
+    for (int64_t r0 = 0; r0 < nrows; r0 += kGridYMax) {
+        sp.row0 = r0;
+        dim3 grid((unsigned)ceil_div(npos_max, sp.chunk), (unsigned)std::min<int64_t>(kGridYMax, nrows - r0),
+                  (unsigned)b.B);
+        e = launch_split_score(H, D, sp, grid, stream);
+        if (e != hipSuccess)
+            return hip_fail(e, "split score launch");
+    }
     SplitSelectParams ss{};
     ss.scores = scores;
     ss.cand = cand;
@@ -741,8 +751,10 @@ int make_chunk_plan(const Batch &b, int H, int D, int64_t nc, int64_t nsel, int6
     pl.cap_scan = scan_cap(nsel, nc);
     size_t work = pl.split_scan ? (size_t)b.B * pl.G * score_row(nc) * sizeof(float)
                                 : scan_bytes(H, D, 8, pl.cap_scan);
+    // one row per group: every row has a list of its own, so each one-wave
+    // workgroup streams its own list (several per CU)
     pl.split_refine = b.q_len <= kSplitRowsMax;
-    pl.nw_refine = b.g <= 4 ? 4 : 8;
+    pl.nw_refine = b.g == 1 ? 1 : (b.g <= 4 ? 4 : 8);
     pl.cap_refine = (int)ceil_div(pl.cw + 128, 64) * 64;
     work = std::max(work, pl.split_refine ? (size_t)b.B * b.q_len * score_row(pl.cw) * sizeof(float)
                                           : scan_bytes(H, D, pl.nw_refine, pl.cap_refine));

@@ -125,6 +125,7 @@ struct SplitScoreParams {
     int64_t nrows;        // score rows per batch item (the largest request's count)
     int64_t rowlen;       // positions per score row (L, or c for kRefine)
     int64_t chunk;        // positions per workgroup
+    int64_t row0;         // first row of this launch (grid y covers at most 65535 rows)
     float *scores;        // [B][nrows][rowlen]
     const int32_t *glim;  // as in ScanParams
     int64_t krows;

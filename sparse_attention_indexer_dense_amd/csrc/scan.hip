@@ -35,7 +35,7 @@ namespace dsaidx {
 // 64 for 4-wave ones (two workgroups then share a CU).
 template <int NW>
 struct ScanStage {
-    static constexpr int KEYS = NW >= 8 ? 128 : 64;
+    static constexpr int KEYS = NW >= 8 ? 128 : (NW >= 4 ? 64 : 32);
 };
 
 // LDS histogram increment for use while key DMA is in flight. Written as
@@ -389,7 +389,7 @@ __device__ __forceinline__ void stage_issue(unsigned char *kbuf, int32_t *lbuf, 
 #pragma unroll
         for (int h0 = 0; h0 < STAGE; h0 += kWave) {
             const int pp = t * STAGE + h0 + lane;
-            if (pp < bk.nkeys)
+            if (pp < bk.nkeys && h0 + lane < STAGE)
                 __builtin_amdgcn_global_load_lds(
                     (const __attribute__((address_space(1))) void *)(bk.list + pp),
                     (__attribute__((address_space(3))) void *)(lbuf + h0), 4, 0, 0);
@@ -737,7 +737,7 @@ static hipError_t launch_pool_t(const PoolParams &prm, hipStream_t stream)
 size_t scan_lds_bytes(int H, int D, int NW)
 {
     (void)H;
-    const int stage = NW >= 8 ? ScanStage<8>::KEYS : ScanStage<4>::KEYS;
+    const int stage = NW >= 8 ? ScanStage<8>::KEYS : (NW >= 4 ? ScanStage<4>::KEYS : ScanStage<1>::KEYS);
     return 2 * (size_t)stage * 2 * D + (size_t)NW * kBins1 * 4;
 }
 
@@ -749,10 +749,12 @@ hipError_t launch_scan_select(int H, int D, int NW, int mode, const ScanParams &
         return launch_scan<HH, DD, NN, MM>(prm, grid, stream);
     DSAIDX_SCAN_CASE(64, 128, 8, kDense)
     DSAIDX_SCAN_CASE(64, 128, 8, kProxy)
+    DSAIDX_SCAN_CASE(64, 128, 1, kRefine)
     DSAIDX_SCAN_CASE(64, 128, 4, kRefine)
     DSAIDX_SCAN_CASE(64, 128, 8, kRefine)
     DSAIDX_SCAN_CASE(4, 32, 8, kDense)
     DSAIDX_SCAN_CASE(4, 32, 8, kProxy)
+    DSAIDX_SCAN_CASE(4, 32, 1, kRefine)
     DSAIDX_SCAN_CASE(4, 32, 4, kRefine)
     DSAIDX_SCAN_CASE(4, 32, 8, kRefine)
 #undef DSAIDX_SCAN_CASE

@@ -130,7 +130,7 @@ __global__ __launch_bounds__(kSplitWaves * kWave) void split_score_kernel(SplitS
     __shared__ int32_t lst[kSplitWaves][LIST ? kSplitSpanMax : 0];
 
     const int bi = blockIdx.z;
-    const int64_t r = blockIdx.y;
+    const int64_t r = p.row0 + blockIdx.y;
     const int wave = uniform(threadIdx.x / kWave);  // wave-uniform (SGPR)
     const int lane = threadIdx.x % kWave;
     const int half = lane >> 5;

@@ -37,6 +37,10 @@ STREAM_WEIGHT = 2
 STREAM_KEY_DIRS = 3
 STREAM_KEY_COEF = 4
 STREAM_QUERY_START = 5
+STREAM_LOCAL_COEF = 6
+STREAM_LOCAL_JUMP = 7
+STREAM_LOCAL_OFFSET = 8
+STREAM_LOCAL_SCALE = 9
 
 
 def _sub_seed(seed: int, stream: int, chunk: int) -> int:
@@ -69,6 +73,67 @@ def keys(L, d, rank, seed, device="cpu", coef_var=0.5, out=None):
                             device=device) * math.sqrt(coef_var)
             for r in range(rank):
                 kf = kf + a[:, r:r + 1] * u[r]
+        out[c0:c1] = kf.to(torch.bfloat16)
+    return out
+
+
+def keys_local(L, d, rank, seed, device="cpu", coef_var=0.5, rho_k=0.98, jump=1.0 / 256,
+               segment=1024, noise=(0.25, 1.5), out=None):
+    """Keys [L, d] bf16 with local structure, for the key-chunk coarse stage
+    (whose premise is that neighbouring keys are often alike, with a spread
+    that varies along the sequence):
+
+      k_s = sigma_{s // segment} z_s / sqrt(d) + sum_r (a_{s,r} + o_{s,r}) u_r
+
+    z_s ~ N(0, I_d); u_r ~ N(0, I_d) / sqrt(d) shared; a_{.,r} an AR(1) process
+    along s with coefficient rho_k and stationary variance coef_var / 2;
+    o_{.,r} piecewise constant, a fresh N(0, coef_var / 2) value at every jump
+    (each position starts a new piece with probability `jump`); sigma drawn
+    per segment of `segment` keys from U(noise)."""
+    device = torch.device(device)
+    if out is None:
+        out = torch.empty((L, d), dtype=torch.bfloat16, device=device)
+    u = torch.randn((max(rank, 1), d), generator=_gen(device, seed, STREAM_KEY_DIRS, 0),
+                    device=device) / math.sqrt(d)
+    half = math.sqrt(coef_var / 2)
+    carry = None
+    last_off = None
+    for c0 in range(0, L, KEY_CHUNK):
+        c1 = min(L, c0 + KEY_CHUNK)
+        n = c1 - c0
+        chunk = c0 // KEY_CHUNK
+        z = torch.randn((n, d), generator=_gen(device, seed, STREAM_KEY_NOISE, chunk), device=device)
+        nseg = -(-n // segment)
+        sig = torch.rand((nseg, 1), generator=_gen(device, seed, STREAM_LOCAL_SCALE, chunk),
+                         device=device) * (noise[1] - noise[0]) + noise[0]
+        kf = z / math.sqrt(d) * sig.repeat_interleave(segment, dim=0)[:n]
+        if rank > 0:
+            eps = torch.randn((n, rank), generator=_gen(device, seed, STREAM_LOCAL_COEF, chunk),
+                              device=device)
+            if carry is None:  # stationary start
+                eps[0] = eps[0] / math.sqrt(1 - rho_k * rho_k)
+            a = _ar1_chunk(eps * math.sqrt(1 - rho_k * rho_k), rho_k, carry) * half
+            carry = a[-1] / half
+            jumps = torch.rand((n,), generator=_gen(device, seed, STREAM_LOCAL_JUMP, chunk),
+                               device=device) < jump
+            vals = torch.randn((n, rank), generator=_gen(device, seed, STREAM_LOCAL_OFFSET, chunk),
+                               device=device) * half
+            if last_off is None:
+                jumps[0] = True
+            piece = torch.cumsum(jumps.long(), 0) - 1  # index of the piece's first position
+            starts = torch.nonzero(jumps).flatten()
+            off = vals[starts][piece.clamp(min=0)] if starts.numel() else None
+            if last_off is not None:
+                # positions before the chunk's first jump continue the last piece
+                before = piece < 0
+                if off is None:
+                    off = last_off[None, :].expand(n, rank).clone()
+                else:
+                    off[before] = last_off
+            last_off = off[-1].clone()
+            coef = a + off
+            for r in range(rank):
+                kf = kf + coef[:, r:r + 1] * u[r]
         out[c0:c1] = kf.to(torch.bfloat16)
     return out
 
