@@ -365,6 +365,59 @@ __device__ __forceinline__ int stage_key(const BlockKeys &bk, int t, int wave, i
     return bk.list ? bk.list[pp] : pp;
 }
 
+// Refine: the list entries of this wave's DMA slots of stage t, loaded
+// without branches (a clamped index for slots past the list) so that the
+// compiler can count the loads in flight exactly; ok[j] marks the slots that
+// hold a key.
+template <int D, int NW, int STAGE>
+__device__ __forceinline__ void stage_list_keys(const BlockKeys &bk, int t, int ntiles, int wave, int lane,
+                                                int (&raw)[StageDma<D, NW, STAGE>::PER_WAVE],
+                                                bool (&ok)[StageDma<D, NW, STAGE>::PER_WAVE])
+{
+    using SD = StageDma<D, NW, STAGE>;
+#pragma unroll
+    for (int j = 0; j < SD::PER_WAVE; ++j) {
+        const int i = wave + NW * j;
+        const int pp = t * STAGE + i * SD::RPI + lane / SD::CHUNKS;
+        ok[j] = (SD::PER_STAGE % NW == 0 || i < SD::PER_STAGE) && t < ntiles && pp < bk.nkeys;
+        raw[j] = bk.list[ok[j] ? pp : 0];
+    }
+}
+
+// Refine: DMA of stage t's keys (no branches: a slot without a key fetches
+// row 0, which the filter never admits) and of its list entries.
+template <int D, int NW, int STAGE>
+__device__ __forceinline__ void stage_issue_list(unsigned char *kbuf, int32_t *lbuf, const BlockKeys &bk, int L,
+                                                 int t, const int (&raw)[StageDma<D, NW, STAGE>::PER_WAVE],
+                                                 const bool (&ok)[StageDma<D, NW, STAGE>::PER_WAVE], int wave,
+                                                 int lane)
+{
+    using SD = StageDma<D, NW, STAGE>;
+#pragma unroll
+    for (int j = 0; j < SD::PER_WAVE; ++j) {
+        const int i = wave + NW * j;
+        // every wave owns PER_WAVE slots when NW divides the stage's DMA count
+        if (SD::PER_STAGE % NW == 0 || i < SD::PER_STAGE) {
+            const int n = i * SD::RPI + lane / SD::CHUNKS;
+            const int c = (lane % SD::CHUNKS) ^ (n & (SD::CHUNKS - 1));
+            const int key = (ok[j] && raw[j] >= 0 && raw[j] < L) ? raw[j] : 0;
+            __builtin_amdgcn_global_load_lds(
+                (const __attribute__((address_space(1))) void *)(bk.Kb + (int64_t)key * D + c * 8),
+                (__attribute__((address_space(3))) void *)(kbuf + i * 1024), 16, 0, 0);
+        }
+    }
+    if (wave == NW - 1) {
+#pragma unroll
+        for (int h0 = 0; h0 < STAGE; h0 += kWave) {
+            const int pp = t * STAGE + h0 + lane;
+            if (h0 + lane < STAGE)
+                __builtin_amdgcn_global_load_lds(
+                    (const __attribute__((address_space(1))) void *)(bk.list + (pp < bk.nkeys ? pp : 0)),
+                    (__attribute__((address_space(3))) void *)(lbuf + h0), 4, 0, 0);
+        }
+    }
+}
+
 template <int D, int NW, int STAGE>
 __device__ __forceinline__ void stage_issue(unsigned char *kbuf, int32_t *lbuf, const BlockKeys &bk, int L,
                                             int t, const int (&keys)[StageDma<D, NW, STAGE>::PER_WAVE],
@@ -617,29 +670,40 @@ void scan_select_kernel(ScanParams p)
 
         // key indices of this wave's DMA slots, one stage ahead
         int keys[SD::PER_WAVE];
+        bool kok[SD::PER_WAVE];
         auto fetch_keys = [&](int t) {
+            if (MODE == kRefine) {
+                stage_list_keys<D, NW, STAGE>(bk, t, ntiles, wave, lane, keys, kok);
+            } else {
 #pragma unroll
-            for (int jj = 0; jj < SD::PER_WAVE; ++jj)
-                keys[jj] = (t < ntiles) ? stage_key<D, NW, STAGE>(bk, t, wave, lane, jj) : -1;
+                for (int jj = 0; jj < SD::PER_WAVE; ++jj)
+                    keys[jj] = (t < ntiles) ? stage_key<D, NW, STAGE>(bk, t, wave, lane, jj) : -1;
+            }
+        };
+        auto issue = [&](unsigned char *kb, int32_t *lb, int t) {
+            if (MODE == kRefine)
+                stage_issue_list<D, NW, STAGE>(kb, lb, bk, bk.L, t, keys, kok, wave, lane);
+            else
+                stage_issue<D, NW, STAGE>(kb, lb, bk, bk.L, t, keys, wave, lane);
         };
 
         fetch_keys(0);
         if (ntiles > 0)
-            stage_issue<D, NW, STAGE>(kA, lA, bk, bk.L, 0, keys, wave, lane);
+            issue(kA, lA, 0);
         fetch_keys(1);
         __syncthreads();
         // two stages per trip so that each LDS buffer is a distinct object at
         // every access (the DMA into one overlaps the MFMA reads of the other)
         for (int t = 0; t < ntiles; t += 2) {
             if (t + 1 < ntiles)
-                stage_issue<D, NW, STAGE>(kB, lB, bk, bk.L, t + 1, keys, wave, lane);
+                issue(kB, lB, t + 1);
             fetch_keys(t + 2);
             compute(kA, lA, t);
             __syncthreads();
             if (t + 1 >= ntiles)
                 break;
             if (t + 2 < ntiles)
-                stage_issue<D, NW, STAGE>(kA, lA, bk, bk.L, t + 2, keys, wave, lane);
+                issue(kA, lA, t + 2);
             fetch_keys(t + 3);
             compute(kB, lB, t + 1);
             __syncthreads();
