@@ -594,14 +594,16 @@ void scan_select_kernel(ScanParams p)
             const int p0 = t * STAGE + nt * 32;
             int key;
             bool ok;
+            // bitwise ands: the lane-varying conditions need no branch or exec
+            // mask change
             if (MODE == kRefine) {
                 key = lb[nt * 32 + col];
-                ok = lane < 32 && col < nkeys - p0 && key >= 0 && key <= lim;
+                ok = (lane < 32) & (col < nkeys - p0) & (key >= 0) & (key <= lim);
             } else {
                 key = p0 + col;
-                ok = lane < 32 && col <= last - p0;
+                ok = (lane < 32) & (col <= last - p0);
             }
-            const bool adm = ok && total > st.theta;
+            const bool adm = ok & (total > st.theta);
             const uint64_t m = ballot(adm);
             if (m) {
                 if (adm) {
