@@ -319,7 +319,7 @@ def main():
     ap.add_argument("--steps", type=int, default=5)
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--workload", default="pivot128k")
-    ap.add_argument("--cpu-rows", type=int, default=48,
+    ap.add_argument("--cpu-rows", type=int, default=512,
                     help="rows of the oracle CPU baseline (0 disables it)")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
