@@ -288,6 +288,19 @@ int indexer_chunk_refine(const void *Q, const float *W, const void *K, const voi
                          int32_t *out_chunks, int32_t *out_cand,
                          void *ws, size_t ws_bytes, hipStream_t stream);
 
+/* Rows of a selection in ranking order. The entry points above write each
+ * output row in ascending index order (the order in which a sparse attention
+ * gathers keys best); this call rewrites `rows` rows of k (index, score) pairs
+ * in place so that each runs in ranking order instead: score descending,
+ * equal scores by ascending index, the -1 padding (score -inf) last ("each
+ * query keeps the k highest-scoring keys": PIVOT, motivation paragraph; the
+ * tie rule is the reading stated at the top of this header).
+ *   idx   [rows][k] int32, score [rows][k] fp32 (both required; e.g. out_idx
+ *         and out_score of any entry point above, rows = B * q_len)
+ *   k     1 .. 8192
+ * A -0 score is written back as +0. Errors as above (EINVAL before launch). */
+int indexer_sort_rows(int32_t *idx, float *score, int64_t rows, int k, hipStream_t stream);
+
 /* Message of the last non-OK return on the calling thread ("" if none). */
 const char *indexer_last_error(void);
 

@@ -7,6 +7,7 @@ their ``*_varlen`` forms for batches of requests of different lengths,
 ``indexer_workspace_bytes``, ``indexer_varlen_workspace_bytes``,
 the key-chunk coarse stage ``indexer_chunks_fixed``, ``indexer_chunks_adaptive``,
 ``indexer_chunk_means``, ``indexer_chunk_refine`` with their workspace queries,
+``indexer_sort_rows``,
 ``indexer_last_error``, ``indexer_version``) take raw device pointers and
 sizes, exactly as the C functions do. ``dense``, ``pivot_reuse``,
 ``pivot_refine``, their ``*_varlen`` forms, ``chunks_fixed``,
@@ -30,8 +31,8 @@ EXPORTS = ("indexer_workspace_bytes", "indexer_dense", "indexer_pivot_reuse",
            "indexer_pivot_refine", "indexer_varlen_workspace_bytes", "indexer_dense_varlen",
            "indexer_pivot_reuse_varlen", "indexer_pivot_refine_varlen", "indexer_chunks_fixed",
            "indexer_chunks_adaptive_workspace_bytes", "indexer_chunks_adaptive", "indexer_chunk_means",
-           "indexer_chunk_refine_workspace_bytes", "indexer_chunk_refine", "indexer_last_error",
-           "indexer_version")
+           "indexer_chunk_refine_workspace_bytes", "indexer_chunk_refine", "indexer_sort_rows",
+           "indexer_last_error", "indexer_version")
 
 
 class IndexerError(RuntimeError):
@@ -80,6 +81,8 @@ def load(path: str = LIB_PATH):
     lib.indexer_chunk_refine.argtypes = [P, P, P, P, P, i64, i32, i64, i64, i32, i32, i32, i32, i32, i32, P,
                                          P, P, P, P, P, sz, P]
     lib.indexer_chunk_refine.restype = i32
+    lib.indexer_sort_rows.argtypes = [P, P, i64, i32, P]
+    lib.indexer_sort_rows.restype = i32
     lib.indexer_last_error.argtypes = []
     lib.indexer_last_error.restype = ctypes.c_char_p
     lib.indexer_version.argtypes = []
@@ -164,6 +167,10 @@ def indexer_chunk_refine(Q, W, K, Kbar, cend, nc, B, L, q_len, H_I, d_I, g, nsel
     return load().indexer_chunk_refine(Q, W, K, Kbar, cend, nc, B, L, q_len, H_I, d_I, g, nsel, max_chunk,
                                        k, opts, out_idx, out_score, out_chunks, out_cand, ws, ws_bytes,
                                        stream)
+
+
+def indexer_sort_rows(idx, score, rows, k, stream):
+    return load().indexer_sort_rows(idx, score, rows, k, stream)
 
 
 def indexer_last_error():
@@ -402,3 +409,18 @@ def chunk_refine(Q, W, K, Kbar, cend, g, nsel, max_chunk, k, proxy="mean", windo
                                 _ptr(out_chunks), _ptr(out_cand), _ptr(wsb), wsb.numel(),
                                 _stream(dev)))
     return out_idx, out_score, out_chunks, out_cand
+
+
+def sort_rows(idx, score):
+    """Reorder output rows (idx int32 [..., k], score fp32 [..., k], both on the
+    GPU) in place into ranking order: score descending, ties by ascending index,
+    -1 padding last. Returns (idx, score)."""
+    import torch
+    if idx.dtype != torch.int32 or score.dtype != torch.float32 or idx.shape != score.shape:
+        raise ValueError("idx (int32) and score (fp32) of one shape are required")
+    if not (idx.is_cuda and score.is_cuda and idx.is_contiguous() and score.is_contiguous()):
+        raise ValueError("idx and score must be contiguous GPU tensors")
+    k = idx.shape[-1]
+    rows = idx.numel() // k if k else 0
+    _check(indexer_sort_rows(_ptr(idx), _ptr(score), rows, k, _stream(idx.device)))
+    return idx, score

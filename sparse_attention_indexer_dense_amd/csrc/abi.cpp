@@ -1123,6 +1123,20 @@ int indexer_chunk_refine(const void *Q, const float *W, const void *K, const voi
                             out_chunks, out_cand, ws, ws_bytes, stream);
 }
 
+int indexer_sort_rows(int32_t *idx, float *score, int64_t rows, int k, hipStream_t stream)
+{
+    if (rows < 0 || rows >= ((int64_t)1 << 40))
+        return fail(DSAIDX_EINVAL, "rows=%lld must be in [0, 2^40)", (long long)rows);
+    if (k < 1 || k > kSortRowMax)
+        return fail(DSAIDX_EINVAL, "k=%d must be in [1, %d]", k, kSortRowMax);
+    if (!idx || !score || !aligned(idx, 4) || !aligned(score, 4))
+        return fail(DSAIDX_EINVAL, "idx and score must be non-NULL 4-byte aligned pointers");
+    if (rows == 0)
+        return DSAIDX_OK;
+    hipError_t e = launch_sort_rows(idx, score, rows, k, stream);
+    return e == hipSuccess ? DSAIDX_OK : hip_fail(e, "sort launch");
+}
+
 const char *indexer_last_error(void) { return g_last_error.c_str(); }
 
 const char *indexer_version(void) { return "dsaidx 0.3.0 gfx950"; }

@@ -203,5 +203,8 @@ hipError_t launch_chunk_limits(int B, int64_t L, int64_t q_len, int64_t g, const
                                int32_t *glim, hipStream_t stream);
 hipError_t launch_chunk_expand(const ChunkExpandParams &prm, int64_t groups, hipStream_t stream);
 hipError_t launch_chunk_adaptive(int D, int B, const ChunkAdaptParams &prm, hipStream_t stream);
+// Rows of k (index, score) pairs reordered in place into ranking order (sort.hip).
+constexpr int kSortRowMax = 8192;
+hipError_t launch_sort_rows(int32_t *idx, float *score, int64_t rows, int k, hipStream_t stream);
 
 }  // namespace dsaidx

@@ -189,3 +189,12 @@ def test_chunk_entry_points_reject_bad_arguments():
     assert refine(nc=9000) == EINVAL
     assert refine(Kbar=None) == EINVAL
     assert refine(ws_bytes=64) == EWORKSPACE
+
+
+def test_sort_rows_rejects_bad_arguments():
+    assert dsa.indexer_sort_rows(fake(), fake(), 10, 0, None) == EINVAL
+    assert dsa.indexer_sort_rows(fake(), fake(), 10, 8193, None) == EINVAL
+    assert dsa.indexer_sort_rows(None, fake(), 10, 64, None) == EINVAL
+    assert dsa.indexer_sort_rows(fake(), None, 10, 64, None) == EINVAL
+    assert dsa.indexer_sort_rows(fake(), fake(), -1, 64, None) == EINVAL
+    assert dsa.indexer_sort_rows(fake(), fake(), 0, 64, None) == OK  # nothing to do
