@@ -316,8 +316,8 @@ def bench_chunks(dsa, synth, torch, w, Q, W, configs=CHUNK_CONFIGS, steps=3):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=5)
-    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="pivot128k")
     ap.add_argument("--cpu-rows", type=int, default=512,
                     help="rows of the oracle CPU baseline (0 disables it)")
@@ -412,10 +412,13 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     per_variant = {v: 0.0 for v in variants}
+    samples = {v: [] for v in variants}
     step_ms = 0.0
     for s in range(args.steps):
         for i, v in enumerate(variants):
-            per_variant[v] += ev[s][i].elapsed_time(ev[s][i + 1]) / args.steps
+            t = ev[s][i].elapsed_time(ev[s][i + 1])
+            per_variant[v] += t / args.steps
+            samples[v].append(t)
         step_ms += ev[s][0].elapsed_time(ev[s][-1]) / args.steps
 
     # work accounting (outside the timed region)
@@ -431,7 +434,7 @@ def main():
     detail = {}
     for v in variants:
         ms = per_variant[v]
-        detail[v] = {"ms": ms, "scored_pairs": pairs[v],
+        detail[v] = {"ms": ms, "median_ms": sorted(samples[v])[len(samples[v]) // 2], "scored_pairs": pairs[v],
                      "pairs_per_s": pairs[v] / (ms * 1e-3),
                      "dense_equiv_pairs_per_s": pd / (ms * 1e-3),
                      "queries_per_s": B * q_len / (ms * 1e-3),
