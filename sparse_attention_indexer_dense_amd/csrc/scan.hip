@@ -351,18 +351,47 @@ struct StageDma {
     static constexpr int PER_WAVE = (PER_STAGE + NW - 1) / NW;  // per wave
 };
 
-// Key index of the row this lane fetches for its DMA slot j of stage t (-1: none).
+// Prefix scans (dense rows, proxies): DMA of stage t's keys, rows
+// t*STAGE .. t*STAGE+STAGE-1. A full stage's rows are contiguous: slot j of
+// lane l fetches the 16 bytes at stage base + j * NW*RPI*ROWB + loff, where
+// loff (this lane's row-in-slot and swizzled chunk, the same for every j
+// because NW*RPI is a multiple of CHUNKS) is fixed for the whole kernel. No
+// index arithmetic, bounds checks or branches per DMA. The last, partial
+// stage of a row block fetches row 0 for slots past the prefix (the causal
+// mask never admits them).
 template <int D, int NW, int STAGE>
-__device__ __forceinline__ int stage_key(const BlockKeys &bk, int t, int wave, int lane, int j)
+__device__ __forceinline__ void stage_issue_prefix(unsigned char *kbuf, const BlockKeys &bk, int t, uint32_t loff,
+                                                   int wave, int lane)
 {
     using SD = StageDma<D, NW, STAGE>;
-    const int i = wave + NW * j;
-    if (i >= SD::PER_STAGE)
-        return -1;
-    const int pp = t * STAGE + i * SD::RPI + lane / SD::CHUNKS;
-    if (pp >= bk.nkeys)
-        return -1;
-    return bk.list ? bk.list[pp] : pp;
+    static_assert((NW * SD::RPI) % SD::CHUNKS == 0, "slot offsets must not change the swizzle");
+    const int row0 = t * STAGE;
+    const unsigned char *kb = reinterpret_cast<const unsigned char *>(bk.Kb);
+    if (row0 + STAGE <= bk.nkeys) {
+#pragma unroll
+        for (int j = 0; j < SD::PER_WAVE; ++j) {
+            const int i = wave + NW * j;
+            if (SD::PER_STAGE % NW == 0 || i < SD::PER_STAGE) {
+                const unsigned char *sb = kb + ((int64_t)row0 * SD::ROWB + j * NW * SD::RPI * SD::ROWB);
+                __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void *)(sb + loff),
+                                                 (__attribute__((address_space(3))) void *)(kbuf + i * 1024), 16,
+                                                 0, 0);
+            }
+        }
+    } else {
+#pragma unroll
+        for (int j = 0; j < SD::PER_WAVE; ++j) {
+            const int i = wave + NW * j;
+            if (SD::PER_STAGE % NW == 0 || i < SD::PER_STAGE) {
+                const int n = i * SD::RPI + lane / SD::CHUNKS;
+                const int row = (row0 + n < bk.nkeys) ? row0 + n : 0;
+                const int c = (lane % SD::CHUNKS) ^ (n & (SD::CHUNKS - 1));
+                __builtin_amdgcn_global_load_lds(
+                    (const __attribute__((address_space(1))) void *)(kb + (int64_t)row * SD::ROWB + c * 16),
+                    (__attribute__((address_space(3))) void *)(kbuf + i * 1024), 16, 0, 0);
+            }
+        }
+    }
 }
 
 // Refine: the list entries of this wave's DMA slots of stage t, loaded
@@ -418,38 +447,6 @@ __device__ __forceinline__ void stage_issue_list(unsigned char *kbuf, int32_t *l
     }
 }
 
-template <int D, int NW, int STAGE>
-__device__ __forceinline__ void stage_issue(unsigned char *kbuf, int32_t *lbuf, const BlockKeys &bk, int L,
-                                            int t, const int (&keys)[StageDma<D, NW, STAGE>::PER_WAVE],
-                                            int wave, int lane)
-{
-    using SD = StageDma<D, NW, STAGE>;
-#pragma unroll
-    for (int j = 0; j < SD::PER_WAVE; ++j) {
-        const int i = wave + NW * j;
-        if (i < SD::PER_STAGE) {
-            const int n = i * SD::RPI + lane / SD::CHUNKS;
-            const int c = (lane % SD::CHUNKS) ^ (n & (SD::CHUNKS - 1));
-            const int key = keys[j];
-            if (key >= 0 && key < L) {
-                __builtin_amdgcn_global_load_lds(
-                    (const __attribute__((address_space(1))) void *)(bk.Kb + (int64_t)key * D + c * 8),
-                    (__attribute__((address_space(3))) void *)(kbuf + i * 1024), 16, 0, 0);
-            }
-        }
-    }
-    if (bk.list && wave == NW - 1) {
-#pragma unroll
-        for (int h0 = 0; h0 < STAGE; h0 += kWave) {
-            const int pp = t * STAGE + h0 + lane;
-            if (pp < bk.nkeys && h0 + lane < STAGE)
-                __builtin_amdgcn_global_load_lds(
-                    (const __attribute__((address_space(1))) void *)(bk.list + pp),
-                    (__attribute__((address_space(3))) void *)(lbuf + h0), 4, 0, 0);
-        }
-    }
-}
-
 // Two waves per SIMD: one 8-wave workgroup, or two 4-wave workgroups, per CU.
 template <int H, int D, int NW, int MODE>
 __global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(2, 2)))
@@ -475,6 +472,14 @@ void scan_select_kernel(ScanParams p)
     const int col = lane & 31;
     uint32_t *h = hist_all + wave * kBins1;
     Entry *buf = p.slots + ((int64_t)blockIdx.x * NW + wave) * p.cap;
+
+    // this lane's byte offset within slot 0 of a stage of contiguous keys
+    // (row within the slot, XOR-swizzled chunk)
+    uint32_t loff;
+    {
+        const int n = wave * SD::RPI + lane / SD::CHUNKS;
+        loff = (uint32_t)(n * SD::ROWB + (((lane % SD::CHUNKS) ^ (n & (SD::CHUNKS - 1))) * 16));
+    }
 
     // lane-constant LDS byte offsets of this lane's B-fragment chunks in a stage
     uint32_t koff[KS];
@@ -674,19 +679,14 @@ void scan_select_kernel(ScanParams p)
         int keys[SD::PER_WAVE];
         bool kok[SD::PER_WAVE];
         auto fetch_keys = [&](int t) {
-            if (MODE == kRefine) {
+            if constexpr (MODE == kRefine)
                 stage_list_keys<D, NW, STAGE>(bk, t, ntiles, wave, lane, keys, kok);
-            } else {
-#pragma unroll
-                for (int jj = 0; jj < SD::PER_WAVE; ++jj)
-                    keys[jj] = (t < ntiles) ? stage_key<D, NW, STAGE>(bk, t, wave, lane, jj) : -1;
-            }
         };
         auto issue = [&](unsigned char *kb, int32_t *lb, int t) {
-            if (MODE == kRefine)
+            if constexpr (MODE == kRefine)
                 stage_issue_list<D, NW, STAGE>(kb, lb, bk, bk.L, t, keys, kok, wave, lane);
             else
-                stage_issue<D, NW, STAGE>(kb, lb, bk, bk.L, t, keys, wave, lane);
+                stage_issue_prefix<D, NW, STAGE>(kb, bk, t, loff, wave, lane);
         };
 
         fetch_keys(0);
