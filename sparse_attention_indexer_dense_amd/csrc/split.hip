@@ -740,6 +740,100 @@ __device__ __forceinline__ int count_pack(const float *sc, int b, int e, uint32_
     return t.total;
 }
 
+// A row of at most kRegRow scores is read from global memory once: wave w
+// holds its contiguous segment in registers, one score per lane per step of
+// 64 positions, and the sample, the count and the pack all work on those
+// registers. The sample is every kSampleEvery-th step of each wave (at most
+// 8192 scores, packed into LDS); its order statistic gives the key theta as
+// in sample_theta. Counting and packing compare floats with the float of
+// theta, which orders finite scores exactly as their keys do once a theta of
+// +0 is lowered to -0 (both zeros then pass, as their keys do). Padding
+// positions hold -inf and never pass, because theta is the key of a finite
+// sampled score (a row holding -inf takes the exact path instead). Returns the
+// number of scores >= theta; if it is at most kCandCap they are packed into
+// cs/cp in index order, with [lo, hi] their key range.
+constexpr int kRegDw = 64;                         // steps per lane held in registers
+constexpr int kRegRow = kSelectThreads * kRegDw;   // longest row held whole
+constexpr int kSampleEvery = 8;
+
+__device__ __forceinline__ int reg_stage(const float *sc, int n, int sel, SelShared &sm, uint32_t &lo, uint32_t &hi)
+{
+    const int wave = uniform(threadIdx.x / kWave), lane = lane_id();
+    const int S = (n + kSelWaves * kWave - 1) / (kSelWaves * kWave) * kWave;  // positions per wave
+    const int b0 = wave * S;
+    const int len = uniform(max(0, min(S, n - b0)));  // this wave's positions
+    float v[kRegDw];
+#pragma unroll
+    for (int q = 0; q < kRegDw; ++q) {
+        const int o = q * kWave + lane;
+        v[q] = o < len ? sc[b0 + o] : -__builtin_inff();
+    }
+    // the sample: wave totals give each wave its slice of cs
+    int nsw = 0;
+    uint32_t slo = 0xFFFFFFFFu, shi = 0u;
+#pragma unroll
+    for (int q = 0; q < kRegDw; q += kSampleEvery) {
+        const int r = min(max(len - q * kWave, 0), kWave);
+        nsw += r;
+        if (lane < r) {
+            const uint32_t k = score_key(v[q]);
+            slo = min(slo, k);
+            shi = max(shi, k);
+        }
+    }
+    const WaveTotals st = wave_totals(nsw, wave_min(slo), wave_max(shi), sm);
+    {
+        int off = st.off;
+#pragma unroll
+        for (int q = 0; q < kRegDw; q += kSampleEvery) {
+            const int r = min(max(len - q * kWave, 0), kWave);
+            if (lane < r)
+                sm.cs[off + lane] = v[q];
+            off += r;
+        }
+    }
+    lds_sync();
+    const int ns = st.total;
+    const float expect = (float)sel * (float)ns / (float)n;
+    int rk = (int)ceilf(expect + 4.f * sqrtf(expect)) + 8;
+    rk = rk < ns ? rk : ns;
+    const Cut c = block_radix_cut(ns, rk, st.lo, st.hi, [&](int i) { return score_key(sm.cs[i]); }, sm);
+    lds_sync();
+    uint32_t theta = c.req > 0 ? c.keq : (uint32_t)(c.kgt + 1);
+    if (theta == 0x80000000u)  // +0: lower to -0
+        theta = 0x7FFFFFFFu;
+    const float thf = key_score(theta);
+    if (!(thf > -__builtin_inff()))
+        return -1;
+
+    int cnt = 0;
+    float fm = -__builtin_inff();
+#pragma unroll
+    for (int q = 0; q < kRegDw; ++q) {
+        cnt += __popcll(ballot(v[q] >= thf));
+        fm = fmaxf(fm, v[q]);
+    }
+    const WaveTotals t = wave_totals(cnt, 0u, wave_max(score_key(fm)), sm);
+    if (t.total > kCandCap)
+        return t.total;
+    int slot0 = t.off;
+#pragma unroll
+    for (int q = 0; q < kRegDw; ++q) {
+        const bool in = v[q] >= thf;
+        const uint64_t m = ballot(in);
+        if (in) {
+            const int o = slot0 + prefix_count(m);
+            sm.cs[o] = v[q];
+            sm.cp[o] = b0 + q * kWave + lane;
+        }
+        slot0 += __popcll(m);
+    }
+    lds_sync();
+    lo = theta;
+    hi = t.hi;
+    return t.total;
+}
+
 // Key range of positions [0, n) of a row (for the exact path over the row).
 __device__ __forceinline__ void row_range(const float *sc, int n, SelShared &sm, uint32_t &lo, uint32_t &hi)
 {
@@ -819,6 +913,12 @@ __device__ __forceinline__ void select_row(const SelRow &s, const SelOut *outs, 
         n = m = t.total;
         lo = t.lo;
         hi = t.hi;
+    } else if (n <= kRegRow) {
+        m = reg_stage(sc, n, selmax, sm, lo, hi);
+        if (m < selmax || m > kCandCap)
+            staged = false;
+        else
+            identity = false;
     } else {
         const uint32_t theta = sample_theta(sc, n, selmax, sm);
         uint32_t km;
