@@ -89,6 +89,16 @@ __device__ __forceinline__ float half_wave_sum(float v)
     return __uint_as_float(p[0]) + __uint_as_float(p[1]);
 }
 
+// Two such sums at once: lane l < 32 gets a[l] + a[l+32], lane l >= 32 gets
+// b[l-32] + b[l] (the lower half's value first in both, as above). The swap
+// exchanges the upper half of its first operand with the lower half of its
+// second, leaving (a[l], b[l-32]) and (a[l+32], b[l]) per lane.
+__device__ __forceinline__ float half_wave_sum2(float a, float b)
+{
+    auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+    return __uint_as_float(p[0]) + __uint_as_float(p[1]);
+}
+
 // Wave-wide sum of an int (all lanes get it).
 __device__ __forceinline__ int wave_sum(int v)
 {

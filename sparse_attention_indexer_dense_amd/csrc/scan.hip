@@ -556,7 +556,8 @@ void scan_select_kernel(ScanParams p)
                         acc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[mb][k0 + ks], kf[ks], acc[mb], 0, 0, 0);
             }
         };
-        // epilogue: ReLU, head weights, head sum (one partial sum per head block)
+        // epilogue: ReLU, head weights, and the sum over this lane's heads (the
+        // other half-wave's heads are added when two tiles are combined)
         auto epilogue = [&](const f32x16 (&acc)[MB]) {
             float part[MB];
 #pragma unroll
@@ -570,7 +571,7 @@ void scan_select_kernel(ScanParams p)
 #pragma unroll
             for (int mb = 1; mb < MB; ++mb)
                 s += part[mb];
-            return half_wave_sum(s) + 0.0f;
+            return s;
         };
         // raise the threshold bin while the bins above it hold >= sel entries:
         // a step or two by walking, a longer jump by searching all bins at once
@@ -594,19 +595,23 @@ void scan_select_kernel(ScanParams p)
             st.count_ge = cg;
             st.theta = fmaxf(st.theta_exact, bin1_floor(st.b));
         };
-        // causal mask and threshold filter of tile nt (lanes 0..31 own the 32 keys)
-        auto filter = [&](float total, const int32_t *lb, int t, int nt) {
-            const int p0 = t * STAGE + nt * 32;
+        // causal mask and threshold filter of the tile pair pr of stage t: lane
+        // l owns key position t*STAGE + 64*pr + l (tile 2pr in lanes 0..31,
+        // tile 2pr+1 in lanes 32..63). A stage of one tile pairs it with
+        // nothing: its upper lanes are masked.
+        auto filter = [&](float total, const int32_t *lb, int t, int pr) {
+            const int p0 = t * STAGE + pr * 64;
+            const bool in_stage = STAGE >= 64 || lane < STAGE;
             int key;
             bool ok;
             // bitwise ands: the lane-varying conditions need no branch or exec
             // mask change
             if (MODE == kRefine) {
-                key = lb[nt * 32 + col];
-                ok = (lane < 32) & (col < nkeys - p0) & (key >= 0) & (key <= lim);
+                key = lb[STAGE >= 64 ? pr * 64 + lane : (in_stage ? lane : 0)];
+                ok = in_stage & (lane < nkeys - p0) & (key >= 0) & (key <= lim);
             } else {
-                key = p0 + col;
-                ok = (lane < 32) & (col <= last - p0);
+                key = p0 + lane;
+                ok = in_stage & (lane <= last - p0);
             }
             const bool adm = ok & (total > st.theta);
             const uint64_t m = ballot(adm);
@@ -648,18 +653,19 @@ void scan_select_kernel(ScanParams p)
                 return;
             f32x16 a0[MB], a1[MB];
             mfma_tile(kb, 0, a0);
+            float s0 = 0.f;  // lane partial of the pair's first tile
 #pragma unroll
             for (int nt = 0; nt < TILES; ++nt) {
                 if (nt >= ntl)
                     break;
-                float total;
+                float s;
                 if (nt + 1 < ntl) {
                     if (nt & 1) {
                         mfma_tile(kb, nt + 1, a0);
-                        total = epilogue(a1);
+                        s = epilogue(a1);
                     } else {
                         mfma_tile(kb, nt + 1, a1);
-                        total = epilogue(a0);
+                        s = epilogue(a0);
                     }
                     // interleave: one MFMA per four VALU ops
 #pragma unroll
@@ -668,9 +674,17 @@ void scan_select_kernel(ScanParams p)
                         __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
                     }
                 } else {
-                    total = (nt & 1) ? epilogue(a1) : epilogue(a0);
+                    s = (nt & 1) ? epilogue(a1) : epilogue(a0);
                 }
-                filter(total, lb, t, nt);
+                // one filter per tile pair, all 64 lanes holding a key; a
+                // pair missing its second tile adds nothing for it (its
+                // lanes are past the stage's last key)
+                if (nt & 1)
+                    filter(half_wave_sum2(s0, s) + 0.0f, lb, t, nt >> 1);
+                else if (nt + 1 >= ntl)
+                    filter(half_wave_sum2(s, 0.f) + 0.0f, lb, t, nt >> 1);
+                else
+                    s0 = s;
             }
             stage_end();
         };
