@@ -771,8 +771,11 @@ __global__ __launch_bounds__(256) void pool_kernel(PoolParams p)
     const float n = (float)(r1 - r0);
     const uint16_t *Qb = p.Q + rq.q_off * H * D;
     const float *Wb = p.W + rq.q_off * H;
-    for (int x = threadIdx.x * 8; x < H * D; x += blockDim.x * 8) {
+    // a few groups spread each proxy over gridDim.z workgroups; the member
+    // loads are unrolled so that several are in flight at once
+    for (int x = (blockIdx.z * blockDim.x + threadIdx.x) * 8; x < H * D; x += gridDim.z * blockDim.x * 8) {
         float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll 4
         for (int64_t r = r0; r < r1; ++r) {
             u32x4 v = *reinterpret_cast<const u32x4 *>(Qb + r * H * D + x);
 #pragma unroll
@@ -790,11 +793,14 @@ __global__ __launch_bounds__(256) void pool_kernel(PoolParams p)
         }
         *reinterpret_cast<u32x4 *>(p.Qp + grp * H * D + x) = o;
     }
-    for (int jh = threadIdx.x; jh < H; jh += blockDim.x) {
-        float acc = 0.f;
-        for (int64_t r = r0; r < r1; ++r)
-            acc += Wb[r * H + jh];
-        p.Wp[grp * H + jh] = __fdiv_rn(acc, n);
+    if (blockIdx.z == 0) {
+        for (int jh = threadIdx.x; jh < H; jh += blockDim.x) {
+            float acc = 0.f;
+#pragma unroll 4
+            for (int64_t r = r0; r < r1; ++r)
+                acc += Wb[r * H + jh];
+            p.Wp[grp * H + jh] = __fdiv_rn(acc, n);
+        }
     }
 }
 
@@ -809,8 +815,12 @@ static hipError_t launch_scan(const ScanParams &prm, int grid, hipStream_t strea
 template <int H, int D>
 static hipError_t launch_pool_t(const PoolParams &prm, hipStream_t stream)
 {
-    // one workgroup per (group, request); gmax = the largest request's groups
-    hipLaunchKernelGGL((pool_kernel<H, D>), dim3((unsigned)prm.gmax, (unsigned)prm.B), dim3(256), 0, stream, prm);
+    // one workgroup per (group, request) and, when there are few groups (a
+    // decode step), one per 2048 proxy elements; gmax = the largest request's
+    // groups
+    const unsigned zc = (prm.gmax * prm.B <= 1024) ? (unsigned)((H * D / 8 + 255) / 256) : 1u;
+    hipLaunchKernelGGL((pool_kernel<H, D>), dim3((unsigned)prm.gmax, (unsigned)prm.B, zc), dim3(256), 0, stream,
+                       prm);
     return hipGetLastError();
 }
 
