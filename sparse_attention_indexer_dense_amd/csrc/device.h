@@ -99,6 +99,20 @@ __device__ __forceinline__ float half_wave_sum2(float a, float b)
     return __uint_as_float(p[0]) + __uint_as_float(p[1]);
 }
 
+// Issue priority of the calling wave, 0 (lowest) to 3, from a value the
+// compiler knows once loops are unrolled (s_setprio takes an immediate).
+__device__ __forceinline__ void wave_priority(int p)
+{
+    if (p >= 3)
+        __builtin_amdgcn_s_setprio(3);
+    else if (p == 2)
+        __builtin_amdgcn_s_setprio(2);
+    else if (p == 1)
+        __builtin_amdgcn_s_setprio(1);
+    else
+        __builtin_amdgcn_s_setprio(0);
+}
+
 // Wave-wide sum of an int (all lanes get it).
 __device__ __forceinline__ int wave_sum(int v)
 {

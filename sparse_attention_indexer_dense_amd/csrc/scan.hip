@@ -642,7 +642,12 @@ void scan_select_kernel(ScanParams p)
 
         // the active tiles of a stage, software-pipelined: the MFMAs of tile
         // nt+1 are issued next to the epilogue of tile nt so that the matrix
-        // pipe and the VALU work at the same time
+        // pipe and the VALU work at the same time. The two waves sharing a
+        // SIMD start a stage together; the issue arbiter favours the older
+        // one, which then waits at the stage barrier while the other finishes
+        // alone. Each wave therefore raises its priority by the tiles it has
+        // left, so that the one behind is served first and both finish
+        // together.
         auto compute = [&](const unsigned char *kb, const int32_t *lb, int t) {
             if (!wr.valid)
                 return;
@@ -658,6 +663,7 @@ void scan_select_kernel(ScanParams p)
             for (int nt = 0; nt < TILES; ++nt) {
                 if (nt >= ntl)
                     break;
+                wave_priority(TILES - 1 - nt);
                 float s;
                 if (nt + 1 < ntl) {
                     if (nt & 1) {
@@ -686,6 +692,7 @@ void scan_select_kernel(ScanParams p)
                 else
                     s0 = s;
             }
+            wave_priority(0);
             stage_end();
         };
 
