@@ -2,14 +2,15 @@
 // and the group-proxy pooling kernel.
 //
 // One workgroup owns NW rows (one per wave) that share a stream of key tiles.
-// Per 64-key stage, the keys are staged in LDS once for all NW rows. Each wave
-// computes, for its row and 32 keys at a time, the 64-head score tile
+// Per stage (128 keys for 8-wave workgroups, 64 or 32 for the smaller Refine
+// ones), the keys are staged in LDS once for all NW rows. Each wave computes,
+// for its row and 32 keys at a time, the 64-head score tile
 // S[j][s] = q_j . k_s with bf16 MFMA 32x32x16 (fp32 accumulate), then the
 // epilogue I(s) = sum_j w_j * max(0, S[j][s]) in registers (Eq. (1) of the
 // PIVOT paper, arXiv 2607.24593, as described in its observation-O3
-// paragraph), the causal mask, and a threshold filter: a key is kept only if
-// its score beats a running threshold below which it provably cannot reach
-// the row's top-sel. Kept (score, index) pairs go, in index order, to a
+// paragraph); then, per 64 keys, the causal mask and a threshold filter: a
+// key is kept only if its score beats a running threshold below which it
+// provably cannot reach the row's top-sel. Kept (score, index) pairs go, in index order, to a
 // per-row buffer in the workspace; a per-row LDS histogram of kept scores
 // raises the threshold as keys stream by. After the last tile, an exact
 // three-level radix cut over the buffer yields the top-sel set (ties to the
