@@ -96,7 +96,9 @@ size_t indexer_workspace_bytes(int mode, int B, int64_t L, int64_t q_len,
 /*
  * Dense DSA indexer (PIVOT paper, motivation paragraph and Eq. (1)): for each
  * query row, the top-k keys of its causal prefix.
- * Requires B >= 1, 1 <= q_len <= L, 1 <= k, L < 2^31.
+ * Requires B >= 1, 0 <= q_len <= L, 1 <= k, L < 2^31. A batch without query
+ * rows (q_len = 0) is valid: the other arguments are still checked, nothing
+ * is read, written or enqueued, and the pointers may be NULL.
  */
 int indexer_dense(const void *Q, const float *W, const void *K,
                   int B, int64_t L, int64_t q_len, int H_I, int d_I, int k,
@@ -165,8 +167,12 @@ typedef struct {
  * never slower than the dense indexer).
  *
  *   L, q_len  host arrays of B entries: request b has L[b] keys and its
- *             queries are its last q_len[b] positions (1 <= q_len[b] <= L[b]
- *             < 2^31). The arrays are read during the call only.
+ *             queries are its last q_len[b] positions (0 <= q_len[b] <= L[b]
+ *             < 2^31). The arrays are read during the call only. A request
+ *             with q_len[b] = 0 (L[b] may then be 0 too) has no rows, groups
+ *             or candidate rows and takes no part in the call; if no request
+ *             has queries, nothing is read, written or enqueued and the
+ *             device pointers may be NULL.
  *   Packed layouts (device memory, requests in order, no padding):
  *     Q        [sum q_len][H_I][d_I]  bf16
  *     W        [sum q_len][H_I]       fp32

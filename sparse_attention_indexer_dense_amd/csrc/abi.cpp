@@ -176,12 +176,14 @@ void finish_batch(Batch &b, const int64_t *Ls, const int64_t *qs, int64_t guard)
     }
 }
 
+// A request may be empty (q_len = 0, and then L may be 0 as well): it has no
+// query rows and contributes nothing.
 int check_sizes(int64_t L, int64_t q_len, const char *what, int i)
 {
-    if (L < 1 || L >= (int64_t)INT32_MAX)
-        return fail(DSAIDX_EINVAL, "%s%d: L=%lld must be in [1, 2^31-1)", what, i, (long long)L);
-    if (q_len < 1 || q_len > L)
-        return fail(DSAIDX_EINVAL, "%s%d: q_len=%lld must be in [1, L=%lld]", what, i, (long long)q_len,
+    if (L < 0 || L >= (int64_t)INT32_MAX)
+        return fail(DSAIDX_EINVAL, "%s%d: L=%lld must be in [0, 2^31-1)", what, i, (long long)L);
+    if (q_len < 0 || q_len > L)
+        return fail(DSAIDX_EINVAL, "%s%d: q_len=%lld must be in [0, L=%lld]", what, i, (long long)q_len,
                     (long long)L);
     return DSAIDX_OK;
 }
@@ -527,6 +529,8 @@ int run_pivot(int mode, const Batch &b, const void *Qv, const float *W, const vo
     int s = make_plan(mode, b, H, D, c, k, out_cand != nullptr, pl);
     if (s != DSAIDX_OK)
         return s;
+    if (b.total_q == 0)
+        return DSAIDX_OK;  // no query rows: nothing to read or write
     s = check_ptrs(Qv, W, Kv, out_idx, out_score, out_cand, ws, pl.total);
     if (s != DSAIDX_OK)
         return s;
@@ -658,6 +662,8 @@ int run_dense_call(const Batch &b, const void *Qv, const float *W, const void *K
     int s = make_plan(DSAIDX_DENSE, b, H, D, 0, k, false, pl);
     if (s != DSAIDX_OK)
         return s;
+    if (b.total_q == 0)
+        return DSAIDX_OK;  // no query rows: nothing to read or write
     s = check_ptrs(Qv, W, Kv, out_idx, out_score, nullptr, ws, pl.total);
     if (s != DSAIDX_OK)
         return s;
@@ -768,6 +774,9 @@ int chunk_batch(int B, int64_t L, int64_t q_len, int g, const dsaidx_pivot_opts 
 {
     if (g < 1)
         return fail(DSAIDX_EINVAL, "g=%d must be >= 1", g);
+    if (L < 1 || q_len < 1)
+        return fail(DSAIDX_EINVAL, "the chunk path needs L >= 1 and q_len >= 1 (L=%lld, q_len=%lld)",
+                    (long long)L, (long long)q_len);
     int s = uniform_batch(B, L, q_len, g, b);
     if (s != DSAIDX_OK)
         return s;

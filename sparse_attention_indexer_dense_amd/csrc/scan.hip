@@ -330,7 +330,10 @@ __device__ __forceinline__ void plan_block(const ScanParams &p, int64_t j, int w
         wr.s1 = p.o1_score ? p.o1_score + row * p.sel : nullptr;
         wr.fan1 = 1;
         const int64_t t_last = off + r1 - 1;
-        bk.list = p.cand + (rq.g_off + m) * p.c;
+        // a block without a live group (m < 0 past a request's groups, or an
+        // empty request) reads no keys, but the branch-free list loads still
+        // touch entry 0: point it at the first candidate row, which exists
+        bk.list = p.cand + (live ? (rq.g_off + m) * p.c : 0);
         bk.nkeys = live ? (p.cand_n ? p.cand_n[rq.g_off + m] : (int)((p.c < t_last + 1) ? p.c : t_last + 1)) : 0;
     }
 }

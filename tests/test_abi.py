@@ -73,7 +73,8 @@ def call_dense(B=1, L=1024, q_len=1024, H=64, d=128, k=64, Q=None, W=None, K=Non
 def test_dense_rejects_bad_sizes():
     assert call_dense(B=0) == EINVAL
     assert call_dense(q_len=2000) == EINVAL
-    assert call_dense(q_len=0) == EINVAL
+    assert call_dense(q_len=-1) == EINVAL
+    assert call_dense(L=-1, q_len=0) == EINVAL
     assert call_dense(k=0) == EINVAL
     assert call_dense(H=8, d=64) == EUNSUPPORTED
     assert "no kernel" in dsa.indexer_last_error()
@@ -118,7 +119,8 @@ def test_varlen_workspace_sizes():
     # the guard removes the PIVOT stages when every group is guarded
     assert varlen_ws(dsa.REFINE, [4096], [4096], guard=4096) < varlen_ws(dsa.REFINE, [4096], [4096])
     assert varlen_ws(dsa.DENSE, [100, 50], [100, 60]) == 0   # q_len > L
-    assert varlen_ws(dsa.DENSE, [0], [0]) == 0
+    assert varlen_ws(dsa.DENSE, [0], [1]) == 0   # q_len > L
+    assert varlen_ws(dsa.DENSE, [5], [-1]) == 0
     assert varlen_ws(dsa.REFINE, [100], [100], guard=-1) == 0
     assert varlen_ws(dsa.REFINE, [100], [100], proxy=3) == 0
     assert varlen_ws(dsa.REFINE, [100], [100], window=-2) == 0
@@ -145,6 +147,31 @@ def test_varlen_rejects_bad_arguments():
     rc = dsa.indexer_pivot_refine_varlen(fake(), fake(), fake(), 2, L, q, 64, 128, 4, 128, 64, bad,
                                          fake(), None, None, fake(), 1 << 40, None)
     assert rc == EINVAL and "proxy" in dsa.indexer_last_error()
+
+
+def test_empty_batches_do_nothing():
+    # no query rows: parameters are still checked, nothing is touched, and the
+    # pointers may be NULL
+    N = None
+    assert dsa.indexer_dense(N, N, N, 2, 1024, 0, 64, 128, 64, N, N, N, 0, None) == OK
+    assert dsa.indexer_dense(N, N, N, 2, 0, 0, 64, 128, 64, N, N, N, 0, None) == OK
+    assert dsa.indexer_dense(N, N, N, 2, 1024, 0, 64, 128, 0, N, N, N, 0, None) == EINVAL  # k = 0
+    for fn in (dsa.indexer_pivot_reuse, dsa.indexer_pivot_refine):
+        assert fn(N, N, N, 1, 1024, 0, 64, 128, 4, 512, 256, N, N, N, N, 0, None) == OK
+        assert fn(N, N, N, 1, 1024, 0, 64, 128, 0, 512, 256, N, N, N, N, 0, None) == EINVAL  # g = 0
+    assert dsa.indexer_pivot_refine(N, N, N, 1, 1024, 0, 64, 128, 4, 100, 256, N, N, N, N, 0,
+                                    None) == EINVAL  # c < k
+    arr = ctypes.c_int64 * 3
+    L, q = arr(0, 500, 70), arr(0, 0, 0)
+    assert dsa.indexer_dense_varlen(N, N, N, 3, L, q, 64, 128, 64, N, N, N, 0, None) == OK
+    for fn in (dsa.indexer_pivot_reuse_varlen, dsa.indexer_pivot_refine_varlen):
+        assert fn(N, N, N, 3, L, q, 64, 128, 4, 512, 256, None, N, N, N, N, 0, None) == OK
+    assert varlen_ws(dsa.REFINE, [0, 500, 70], [0, 0, 0]) > 0
+    # a batch with some queries still needs its pointers
+    q = arr(0, 10, 0)
+    assert dsa.indexer_dense_varlen(N, N, N, 3, L, q, 64, 128, 64, N, N, N, 0, None) == EINVAL
+    # the key-chunk path keeps L, q_len >= 1
+    assert chunk_ws(q_len=0) == 0
 
 
 def chunk_ws(B=1, L=8192, q_len=8192, H=64, d=128, g=1, nc=128, nsel=16, max_chunk=64, k=256):

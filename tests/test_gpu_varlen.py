@@ -2,7 +2,8 @@
 every request's rows against the oracle run on that request alone; groups
 never reach into a neighbouring request; the guard scores short groups as
 dense rows. Covers the scan (many rows) and split-key (few rows) paths, short
-last groups, q_len < L, a request shorter than k, and the guard's limits."""
+last groups, q_len < L, a request shorter than k, requests without queries
+(with or without keys), and the guard's limits."""
 import numpy as np
 import pytest
 import torch
@@ -140,3 +141,61 @@ def test_decode_batch_of_lengths():
     d_idx, d_sc = dsa.dense_varlen(Q, W, K, L, q, k)
     res, _, _ = check_varlen("dense", Q, W, K, L, q, 1, 0, k, 0, (d_idx, d_sc, None))
     assert_ok(res)
+
+
+def packed_with_empty(L, q_len, H=4, d=32, seed=0):
+    """As packed(), where a request with q_len = 0 brings only its keys (none
+    if L = 0)."""
+    Qs, Ws, Ks = [], [], []
+    for i, (Lb, qb) in enumerate(zip(L, q_len)):
+        if qb > 0:
+            Q, W, K = packed([Lb], [qb], H, d, seed + i)
+        else:
+            Q = torch.empty((0, H, d), dtype=torch.bfloat16, device=DEV)
+            W = torch.empty((0, H), dtype=torch.float32, device=DEV)
+            K = (synth.decode(1, Lb, 1, H, d, 0.9, 2, seed + i, DEV)[2][0] if Lb > 0
+                 else torch.empty((0, d), dtype=torch.bfloat16, device=DEV))
+        Qs.append(Q)
+        Ws.append(W)
+        Ks.append(K)
+    return torch.cat(Qs).contiguous(), torch.cat(Ws).contiguous(), torch.cat(Ks).contiguous()
+
+
+# requests without queries (with and without keys) among ordinary ones, on
+# the scan path (up to 120 rows per request) and the split-key path
+EMPTY_SCAN = ([0, 3001, 500, 0, 700, 9000], [0, 120, 0, 0, 65, 2])
+EMPTY_SPLIT = ([0, 5000, 300, 9000], [0, 2, 0, 3])
+
+
+@pytest.mark.parametrize("shape", [EMPTY_SCAN, EMPTY_SPLIT], ids=["scan", "split"])
+@pytest.mark.parametrize("variant", ["dense", "reuse", "refine"])
+def test_empty_requests(shape, variant):
+    L, q = shape
+    Q, W, K = packed_with_empty(L, q, seed=11)
+    g, c, k = 4, 128, 64
+    if variant == "dense":
+        idx, sc = dsa.dense_varlen(Q, W, K, L, q, k)
+        out = (idx, sc, None)
+    elif variant == "reuse":
+        out = dsa.pivot_reuse_varlen(Q, W, K, L, q, g, k, c=c, cand=True)
+    else:
+        out = dsa.pivot_refine_varlen(Q, W, K, L, q, g, c, k, cand=True)
+    rd, rc, rr = check_varlen(variant, Q, W, K, L, q, g, c, k, 0, out)
+    assert_ok(rd, rc, rr)
+    assert out[0].shape[0] == sum(q)
+    assert rd.rows + rr.rows == sum(q)
+
+
+def test_all_requests_empty():
+    # no request has queries: the calls return empty outputs and touch nothing
+    L, q = [0, 300, 0], [0, 0, 0]
+    Q = torch.empty((0, 4, 32), dtype=torch.bfloat16, device=DEV)
+    W = torch.empty((0, 4), dtype=torch.float32, device=DEV)
+    K = synth.decode(1, 300, 1, 4, 32, 0.9, 2, 0, DEV)[2][0].contiguous()
+    idx, sc = dsa.dense_varlen(Q, W, K, L, q, 64)
+    assert tuple(idx.shape) == (0, 64)
+    idx, sc, cand = dsa.pivot_refine_varlen(Q, W, K, L, q, 4, 128, 64, cand=True)
+    assert tuple(idx.shape) == (0, 64) and tuple(cand.shape) == (0, 128)
+    idx, sc, cand = dsa.pivot_reuse_varlen(Q, W, K, L, q, 4, 64, c=128, cand=True)
+    assert tuple(idx.shape) == (0, 64) and tuple(cand.shape) == (0, 128)
+    torch.cuda.synchronize()
