@@ -7,8 +7,8 @@
 //   split_score_kernel  - a workgroup owns (batch item, row, span of key
 //                         positions), one round of workgroups for all rows;
 //                         each wave streams its own contiguous part of the
-//                         span in 32-key tiles through a private ring of LDS
-//                         tiles filled by global->LDS DMA (several tiles in
+//                         span in 32-key tiles, loaded straight into
+//                         registers as MFMA B fragments (several tiles in
 //                         flight while one is scored), runs the MFMA score
 //                         tile and the ReLU/weight/head-sum epilogue, and
 //                         stores one fp32 score per position;
@@ -96,38 +96,23 @@ __device__ __forceinline__ SplitRow split_row(const SplitScoreParams &p, int H, 
 }
 
 // ------------------------------------------------------------------ scoring
-// s_waitcnt with only the vector-memory counter constrained to <= n (gfx9
-// encoding: vmcnt bits [3:0] and [15:14]; expcnt and lgkmcnt left at max).
-template <int N>
-__device__ __forceinline__ void wait_vmcnt()
-{
-    static_assert(N >= 0 && N < 64, "vmcnt range");
-    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
-}
-
-// Each wave streams its span of positions through a private ring of RING
-// LDS tiles of 32 keys; tiles t+1 .. t+RING-1 are in flight while tile t is
-// scored. Every tile costs exactly DMA_PER_TILE DMA instructions (lanes
-// without a key fetch row 0 into a slot that is never read) and exactly one
-// score store, so the number of vector-memory operations issued after tile
-// t's DMA is known and the wait for it is exact. The ring fills the LDS:
-// five tiles per wave for a key prefix, four beside the candidate list.
-template <bool LIST, int ROWB>
-struct SplitRing {
-    static constexpr int RING = (LIST || ROWB < 256) ? 4 : 5;
-};
+// Key rows are read once and used by one row's MFMAs only, so they go straight
+// from global memory into registers as B fragments, with no LDS staging. K-step
+// ks of a fragment holds the 16-byte chunk 2*ks + half of its row (half = lane
+// / 32): the 32 rows of a tile are then read 32 contiguous bytes per row per
+// load instruction, and the query fragments use the same chunk order, so
+// every dot product sums the same terms. A ring of kSplitDepth tiles keeps
+// the loads of the next tiles in flight while one tile is scored; the loads
+// are plain vector loads, whose completion the compiler tracks exactly.
+constexpr int kSplitDepth = 4;
 
 template <int H, int D, bool LIST>
 __global__ __launch_bounds__(kSplitWaves * kWave) void split_score_kernel(SplitScoreParams p)
 {
     using S = Shape<H, D>;
-    constexpr int MB = S::MB, KS = S::KS, ROWB = S::ROWB, CHUNKS = S::CHUNKS;
-    constexpr int TILE_BYTES = 32 * ROWB;
-    constexpr int DMA_PER_TILE = TILE_BYTES / 1024;
-    constexpr int RPI = kWave / CHUNKS;  // key rows per DMA instruction
-    constexpr int kRing = SplitRing<LIST, ROWB>::RING;
-    __shared__ __align__(1024) unsigned char ring[kSplitWaves][kRing][TILE_BYTES];
-    __shared__ int32_t lst[kSplitWaves][LIST ? kSplitSpanMax : 0];
+    constexpr int MB = S::MB, KS = S::KS;
+    constexpr int P = kSplitDepth;
+    __shared__ int32_t lst[kSplitWaves][LIST ? kSplitSpanMax : 1];
 
     const int bi = blockIdx.z;
     const int64_t r = p.row0 + blockIdx.y;
@@ -152,26 +137,8 @@ __global__ __launch_bounds__(kSplitWaves * kWave) void split_score_kernel(SplitS
         __builtin_amdgcn_wave_barrier();
     }
 
-    // DMA of tile t into ring slot t % kRing: lane l of instruction i fetches
-    // the chunk that the XOR swizzle puts in slot l of the i-th KiB
-    auto issue = [&](int t) {
-        unsigned char *dst = ring[wave][t % kRing];
-#pragma unroll
-        for (int i = 0; i < DMA_PER_TILE; ++i) {
-            const int n = i * RPI + lane / CHUNKS;
-            const int pos = w0 + t * 32 + n;
-            const int c = (lane % CHUNKS) ^ (n & (CHUNKS - 1));
-            int key = 0;
-            if (t < ntile && pos < w1) {
-                key = LIST ? wl[pos - w0] : pos;
-                key = (key >= 0 && key < sr.L) ? key : 0;
-            }
-            __builtin_amdgcn_global_load_lds(
-                (const __attribute__((address_space(1))) void *)(Kb + (int64_t)key * D + c * 8),
-                (__attribute__((address_space(3))) void *)(dst + i * 1024), 16, 0, 0);
-        }
-    };
-
+    // the query row as MFMA A fragments (chunk order as above) and the
+    // weights per accumulator row
     bf16x8 qa[MB][KS];
     float wv[MB][16];
 #pragma unroll
@@ -181,7 +148,7 @@ __global__ __launch_bounds__(kSplitWaves * kWave) void split_score_kernel(SplitS
         for (int ks = 0; ks < KS; ++ks) {
             u32x4 v = {0u, 0u, 0u, 0u};
             if (head < H)
-                v = *reinterpret_cast<const u32x4 *>(sr.q + (int64_t)head * D + (half * KS + ks) * 8);
+                v = *reinterpret_cast<const u32x4 *>(sr.q + (int64_t)head * D + (2 * ks + half) * 8);
             qa[mb][ks] = __builtin_bit_cast(bf16x8, v);
         }
 #pragma unroll
@@ -190,31 +157,36 @@ __global__ __launch_bounds__(kSplitWaves * kWave) void split_score_kernel(SplitS
             wv[mb][rr] = hr < H ? sr.w[hr] : 0.f;
         }
     }
-    uint32_t koff[KS];
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
-        koff[ks] = (uint32_t)(col * ROWB + (((half * KS + ks) ^ (col & (CHUNKS - 1))) * 16));
 
-    // MFMA score tile t into acc (all K fragments read first)
-    auto mfma_tile = [&](int t, f32x16 (&acc)[MB]) {
-        const unsigned char *src = ring[wave][t % kRing];
+    // B fragments of tile t: key row w0 + 32t + col (through the list for
+    // Refine); a lane without a key (past the span or the list's valid
+    // entries, or beyond the ring's last tile) reads row 0, whose score is
+    // never stored
+    bf16x8 kq[P][KS];
+    auto load_tile = [&](int t, bf16x8 (&kf)[KS]) {
+        const int pos = w0 + t * 32 + col;
+        const bool ok = t < ntile && pos < w1;
+        int key = pos;
+        if (LIST)
+            key = wl[ok ? pos - w0 : 0];
+        key = (ok && key >= 0 && key < sr.L) ? key : 0;
+        const uint16_t *src = Kb + (int64_t)key * D + half * 8;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+            kf[ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(src + ks * 16));
+    };
+    auto mfma_tile = [&](const bf16x8 (&kf)[KS], f32x16 (&acc)[MB]) {
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb)
             acc[mb] = f32x16{};
-        bf16x8 kf[KS];
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks)
-            kf[ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(src + koff[ks]));
-        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
             for (int mb = 0; mb < MB; ++mb)
                 acc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[mb][ks], kf[ks], acc[mb], 0, 0, 0);
     };
-    // epilogue of tile t and its one store instruction: lane 0 always holds a
-    // position of the tile; positions whose key is beyond the row's limit get
-    // a score too, which the selection ignores
+    // epilogue of tile t and its store: positions whose key is beyond the
+    // row's limit get a score too, which the selection ignores
     auto finish = [&](int t, const f32x16 (&acc)[MB]) {
         float part[MB];
 #pragma unroll
@@ -233,48 +205,35 @@ __global__ __launch_bounds__(kSplitWaves * kWave) void split_score_kernel(SplitS
         if (lane < 32 && pos < w1)
             out[pos] = total;
     };
-    // tile t's DMA is complete once at most this many vector-memory
-    // operations are outstanding: the DMA of the kRing - 2 tiles issued after
-    // it, and the stores issued since (tile t - 1's in iteration t, one per
-    // iteration from iteration 1 on, at most kRing - 1)
-    auto wait_tile = [&](int t) {
-        constexpr int B0 = (kRing - 2) * DMA_PER_TILE;
-        const int st = t < 1 ? 0 : (t - 1 < kRing - 1 ? t - 1 : kRing - 1);
-        switch (st) {
-        case 0: wait_vmcnt<B0>(); break;
-        case 1: wait_vmcnt<B0 + 1>(); break;
-        case 2: wait_vmcnt<B0 + 2>(); break;
-        case 3: wait_vmcnt<B0 + 3>(); break;
-        default: wait_vmcnt<B0 + 4>(); break;
-        }
-    };
 
-    // the ring primed with kRing - 1 tiles behind the operand loads (waiting
-    // for tile 0 waits for them as well); the MFMAs of tile t run next to the
-    // epilogue of tile t - 1
-    __builtin_amdgcn_sched_barrier(0);
-    for (int t = 0; t < kRing - 1; ++t)
-        issue(t);
-    f32x16 a0[MB], a1[MB];
-    for (int t = 0; t < ntile; ++t) {
-        __builtin_amdgcn_sched_barrier(0);
-        wait_tile(t);
-        __builtin_amdgcn_sched_barrier(0);
-        issue(t + kRing - 1);
-        if (t == 0) {
-            mfma_tile(0, a0);
-        } else {
-            if (t & 1) {
-                mfma_tile(t, a1);
-                finish(t - 1, a0);
-            } else {
-                mfma_tile(t, a0);
-                finish(t - 1, a1);
-            }
+    // ring slots are compile-time: P tiles per trip; the MFMAs of tile t run
+    // next to the epilogue of tile t - 1
 #pragma unroll
-            for (int q = 0; q < KS * MB; ++q) {
-                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+    for (int u = 0; u < P - 1; ++u)
+        load_tile(u, kq[u]);
+    f32x16 a0[MB], a1[MB];
+    for (int t0 = 0; t0 < ntile; t0 += P) {
+#pragma unroll
+        for (int u = 0; u < P; ++u) {
+            const int t = t0 + u;
+            if (t >= ntile)
+                break;
+            load_tile(t + P - 1, kq[(u + P - 1) % P]);
+            if (t == 0) {
+                mfma_tile(kq[u], a0);
+            } else {
+                if (t & 1) {
+                    mfma_tile(kq[u], a1);
+                    finish(t - 1, a0);
+                } else {
+                    mfma_tile(kq[u], a0);
+                    finish(t - 1, a1);
+                }
+#pragma unroll
+                for (int q = 0; q < KS * MB; ++q) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+                }
             }
         }
     }
@@ -284,8 +243,6 @@ __global__ __launch_bounds__(kSplitWaves * kWave) void split_score_kernel(SplitS
         else
             finish(ntile - 1, a0);
     }
-    // no DMA may still be writing this workgroup's LDS when it exits
-    __builtin_amdgcn_s_waitcnt(0);
 }
 
 // ---------------------------------------------------------------- selection
