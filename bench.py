@@ -107,11 +107,13 @@ def _attach_keys(name, shape):
 
 
 def _oracle_row(args):
+    """One dense row through the oracle: (pairs scored, seconds of this process)."""
     import oracle
     q, w, n, k = args
+    t0 = time.perf_counter()
     sc, _ = oracle.scores(q, w, _KEYS[1], n=n)
     oracle.select(sc, k)
-    return n
+    return n, time.perf_counter() - t0
 
 
 def cpu_baseline(Q, W, K, k, L, q_len, budget_rows, seed=0):
@@ -142,16 +144,22 @@ def cpu_baseline(Q, W, K, k, L, q_len, budget_rows, seed=0):
                                  initargs=(shm.name, Kh.shape)) as ex:
             list(ex.map(_oracle_row, [(Qh[0], Wh[0], 1, k)] * workers))  # start the workers
             t0 = time.perf_counter()
-            pairs = sum(ex.map(_oracle_row, work))
+            done = list(ex.map(_oracle_row, work))
             dt = time.perf_counter() - t0
     finally:
         shm.close()
         shm.unlink()
+    pairs = sum(n for n, _ in done)
+    busy = sum(t for _, t in done)  # seconds the workers spent on the rows
+    full = dense_pairs(L, q_len)
     return {"value": pairs / dt, "unit": "pairs/s", "cores": workers, "kind": "oracle",
             "sample": f"dense rows of the same L={L} sequence: {len(rows)} rows drawn uniformly "
                       f"(seed {seed}), {pairs:.3e} scored pairs, fp64 single-threaded oracle per "
                       f"worker process, {dt:.1f} s wall",
-            "seconds": dt}
+            "seconds": dt,
+            "per_core_pairs_per_s": pairs / busy,
+            "dense_launch_s_extrapolated": {"one_core": full / (pairs / busy),
+                                            f"{workers}_cores": full / (pairs / dt)}}
 
 
 # ------------------------------------------------------------------- decode
