@@ -43,6 +43,10 @@
  *   Scores are computed from the bf16 inputs with fp32 accumulation.
  *   Supported (H_I, d_I): (4, 32) and (64, 128). Other pairs return
  *   DSAIDX_EUNSUPPORTED.
+ *   Sizes: 1 <= B <= 65535, 0 <= q_len <= L < 2^31, 1 <= k <= 2^20. A batch
+ *   without query rows (q_len = 0) is valid: the other arguments are still
+ *   checked, nothing is read, written or enqueued, and the pointers may be
+ *   NULL.
  *
  * Memory ownership. Every pointer is caller-owned device memory (16-byte
  * aligned for Q, K and ws). The library allocates and frees nothing, never
@@ -96,9 +100,7 @@ size_t indexer_workspace_bytes(int mode, int B, int64_t L, int64_t q_len,
 /*
  * Dense DSA indexer (PIVOT paper, motivation paragraph and Eq. (1)): for each
  * query row, the top-k keys of its causal prefix.
- * Requires B >= 1, 0 <= q_len <= L, 1 <= k, L < 2^31. A batch without query
- * rows (q_len = 0) is valid: the other arguments are still checked, nothing
- * is read, written or enqueued, and the pointers may be NULL.
+ * Sizes as in the shared conventions above.
  */
 int indexer_dense(const void *Q, const float *W, const void *K,
                   int B, int64_t L, int64_t q_len, int H_I, int d_I, int k,
@@ -111,7 +113,8 @@ int indexer_dense(const void *Q, const float *W, const void *K,
  * identical, and early members may hold keys beyond their own position, which
  * the downstream attention masks). c is used only to fill out_cand with the
  * proxy's top-c when out_cand is not NULL; otherwise it is ignored.
- * Requires g >= 1 and, when out_cand is not NULL, c >= 1.
+ * Requires g >= 1 and, when out_cand is not NULL, k <= c <= 2^20 (the top-k
+ * is then the first k of the top-c).
  */
 int indexer_pivot_reuse(const void *Q, const float *W, const void *K,
                         int B, int64_t L, int64_t q_len, int H_I, int d_I,
@@ -123,7 +126,7 @@ int indexer_pivot_reuse(const void *Q, const float *W, const void *K,
  * PIVOT-Refine (PIVOT paper, abstract and Method): each member row re-scores
  * the group's top-c candidates that lie at or before its own position, with
  * its own query and weights, and keeps its top-k. out_cand, when not NULL,
- * receives the candidates. Requires g >= 1 and c >= k.
+ * receives the candidates. Requires g >= 1 and k <= c <= 2^20.
  */
 int indexer_pivot_refine(const void *Q, const float *W, const void *K,
                          int B, int64_t L, int64_t q_len, int H_I, int d_I,
