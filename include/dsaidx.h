@@ -235,7 +235,8 @@ int indexer_pivot_refine_varlen(const void *Q, const float *W, const void *K,
  *                   in index order divided (IEEE fp32) by the chunk's size,
  *                   rounded to bf16 nearest-even (a stated reading: the paper
  *                   gives no precision).
- * Uniform batches only (B requests of L keys, the last q_len positions queried).
+ * Uniform batches only (B requests of L keys, the last q_len positions
+ * queried), with L >= 1 and q_len >= 1.
  * ------------------------------------------------------------------------ */
 
 /* Fixed blocks: cend[b] = min((b + 1) * block, L) for b < nc = ceil(L / block),
@@ -313,7 +314,7 @@ int indexer_sort_rows(int32_t *idx, float *score, int64_t rows, int k, hipStream
 /* Message of the last non-OK return on the calling thread ("" if none). */
 const char *indexer_last_error(void);
 
-/* Library version string, e.g. "dsaidx 0.1.0 gfx950". */
+/* Library version string, e.g. "dsaidx 0.4.0 gfx950". */
 const char *indexer_version(void);
 
 #ifdef __cplusplus

@@ -1148,6 +1148,6 @@ int indexer_sort_rows(int32_t *idx, float *score, int64_t rows, int k, hipStream
 
 const char *indexer_last_error(void) { return g_last_error.c_str(); }
 
-const char *indexer_version(void) { return "dsaidx 0.3.0 gfx950"; }
+const char *indexer_version(void) { return "dsaidx 0.4.0 gfx950"; }
 
 }  // extern "C"
