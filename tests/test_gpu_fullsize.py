@@ -73,7 +73,8 @@ def run_pivot(Q, W, K, g, c, k, variant, groups):
 def test_dense16k():
     w = synth.WORKLOADS["dense16k"]
     Q, W, K = synth.make(w, device=DEV)
-    rows = [(0, r) for r in sample(w.L, 8, 8, 16, 1)]
+    # stratified: the first 64 rows, the last 64 and 128 seeded-random ones
+    rows = [(0, r) for r in sample(w.L, 64, 64, 128, 1)]
     res = run_dense(Q, W, K, w.k, rows)
     assert_ok(res)
     print(res.summary())
@@ -91,7 +92,7 @@ def pivot128k():
 
 def test_pivot128k_dense(pivot128k):
     w, Q, W, K = pivot128k
-    rows = [(0, r) for r in sample(w.L, 1, 2, 5, 2)]
+    rows = [(0, r) for r in sample(w.L, 4, 4, 24, 2)]
     res = run_dense(Q, W, K, w.k, rows)
     assert_ok(res)
     print(res.summary())
@@ -101,7 +102,7 @@ def test_pivot128k_dense(pivot128k):
 def test_pivot128k(pivot128k, variant):
     w, Q, W, K = pivot128k
     G = w.L // w.g
-    groups = [(0, m) for m in sample(G, 1, 1, 2, 3)]
+    groups = [(0, m) for m in sample(G, 2, 2, 12, 3)]
     rc, rr = run_pivot(Q, W, K, w.g, w.c, w.k, variant, groups)
     assert_ok(rc, rr)
     print(variant, rc.summary(), rr.summary())
@@ -110,7 +111,7 @@ def test_pivot128k(pivot128k, variant):
 def test_decode64k():
     w = synth.WORKLOADS["decode64k"]
     Q, W, K = synth.make(w, device=DEV)
-    reqs = [0, 7, 19, 31]
+    reqs = [0, 4, 9, 13, 18, 22, 27, 31]
     res = run_dense(Q, W, K, w.k, [(b, r) for b in reqs for r in range(w.g)])
     assert_ok(res)
     rc, rr = run_pivot(Q, W, K, w.g, w.c, w.k, "refine", [(b, 0) for b in reqs])
@@ -140,7 +141,7 @@ def test_pivot1m_dense(pivot1m):
 def test_pivot1m(pivot1m, variant):
     w, Q, W, K = pivot1m
     G = w.L // w.g
-    groups = [(0, m) for m in sample(G, 1, 0, 1, 5)]
+    groups = [(0, m) for m in sample(G, 1, 1, 2, 5)]
     rc, rr = run_pivot(Q, W, K, w.g, w.c, w.k, variant, groups)
     assert_ok(rc, rr)
     print(variant, rc.summary(), rr.summary())
