@@ -342,8 +342,8 @@ def main():
                          "(--steps times; for kernel traces)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the indexer is not "
-              "sharded across GPUs in this build.", file=sys.stderr)
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the library does not shard the "
+              "indexer across GPUs.", file=sys.stderr)
         sys.exit(2)
 
     import torch
