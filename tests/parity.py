@@ -10,6 +10,7 @@ import numpy as np
 import torch
 
 import oracle
+import oracle_pool
 import sparse_attention_indexer_dense_amd as dsa
 import synth
 from checker import Result, check_row
@@ -39,9 +40,18 @@ class HostView:
         return synth.to_u16(self.Q[b, r0:r1]), self.W[b, r0:r1].detach().cpu().numpy()
 
 
-def check_dense_rows(idx, sc, hv, L, q_len, k, rows, res=None):
-    """Check GPU dense output rows (host arrays idx/sc [B, q_len, k]) for `rows`."""
+def check_dense_rows(idx, sc, hv, L, q_len, k, rows, res=None, pool=None):
+    """Check GPU dense output rows (host arrays idx/sc [B, q_len, k]) for `rows`
+    (in the worker processes of an oracle_pool.OraclePool when one is given)."""
     res = Result() if res is None else res
+    if pool is not None:
+        jobs = []
+        for b, r in rows:
+            q, w = hv.rows(b, r, r + 1)
+            jobs.append((b, r, q[0], w[0], L - q_len + r + 1, np.asarray(idx[b, r]), np.asarray(sc[b, r]), k))
+        for part in pool.map(oracle_pool._dense_job, jobs):
+            merge(res, part)
+        return res
     for b, r in rows:
         pos = L - q_len + r
         q, w = hv.rows(b, r, r + 1)
@@ -62,34 +72,59 @@ def check_dense(Q, W, K, k, rows=None, out=None):
     return res, idx, sc
 
 
-def check_pivot_rows(variant, idx, sc, cand, hv, L, q_len, g, c, k, groups, kind="mean", window=0):
+def check_pivot_rows(variant, idx, sc, cand, hv, L, q_len, g, c, k, groups, kind="mean", window=0,
+                     pool=None):
     """Check PIVOT outputs (host arrays) for `groups` [(b, m)]: candidates vs the
     oracle's proxy scan, Reuse rows vs the proxy top-k (identical within a
-    group), Refine rows vs the oracle re-scoring the GPU's own candidates."""
+    group), Refine rows vs the oracle re-scoring the GPU's own candidates. With
+    an oracle_pool.OraclePool the proxy scans run in its worker processes."""
     res_c, res_r = Result(), Result()
+    scan = cand is not None or variant == "reuse"
+    if pool is not None and scan:
+        jobs = []
+        for b, m in groups:
+            r0, r1 = m * g, min(m * g + g, q_len)
+            Qm, Wm = hv.rows(b, r0, r1)
+            qb, wb = oracle.proxy(Qm, Wm, g, 0, kind=kind, window=window)
+            reuse = ([(r, np.asarray(idx[b, r]), np.asarray(sc[b, r])) for r in range(r0, r1)]
+                     if variant == "reuse" else [])
+            jobs.append((b, m, qb, wb, L - q_len + r1, None if cand is None else np.asarray(cand[b, m]), c,
+                         reuse, k))
+        for rc_, rr_ in pool.map(oracle_pool._proxy_job, jobs):
+            merge(res_c, rc_)
+            merge(res_r, rr_)
+        scan = False  # done
+    refine_jobs = []
     for b, m in groups:
         r0, r1 = m * g, min(m * g + g, q_len)
         t_last = L - q_len + r1 - 1
         Qm, Wm = hv.rows(b, r0, r1)
-        qb, wb = oracle.proxy(Qm, Wm, g, 0, kind=kind, window=window)
         univ = None
-        if cand is not None or variant == "reuse":
+        if scan:
+            qb, wb = oracle.proxy(Qm, Wm, g, 0, kind=kind, window=window)
             ref, mass = oracle.scores(qb, wb, hv.keys(b), n=t_last + 1)
             univ = np.arange(t_last + 1)
-        if cand is not None:
-            check_row(cand[b, m], None, univ, ref, mass, c, res_c, f"cand b{b} m{m}")
+            if cand is not None:
+                check_row(cand[b, m], None, univ, ref, mass, c, res_c, f"cand b{b} m{m}")
         for r in range(r0, r1):
             if variant == "reuse":
-                check_row(idx[b, r], sc[b, r], univ, ref, mass, k, res_r, f"reuse b{b} r{r}")
+                if scan:
+                    check_row(idx[b, r], sc[b, r], univ, ref, mass, k, res_r, f"reuse b{b} r{r}")
                 if not (np.array_equal(idx[b, r], idx[b, r0]) and np.array_equal(sc[b, r], sc[b, r0])):
                     res_r.add(False, False, 0.0, f"reuse b{b} r{r}: differs from the group's first row")
             else:
                 pos = L - q_len + r
                 cm = cand[b, m]
                 cp = cm[(cm >= 0) & (cm <= pos)]
+                if pool is not None:
+                    refine_jobs.append((b, r, Qm[r - r0], Wm[r - r0], np.ascontiguousarray(cp),
+                                        np.asarray(idx[b, r]), np.asarray(sc[b, r]), k))
+                    continue
                 kc = np.ascontiguousarray(hv.keys(b)[cp])
                 ref_i, mass_i = oracle.scores(Qm[r - r0], Wm[r - r0], kc)
                 check_row(idx[b, r], sc[b, r], cp, ref_i, mass_i, k, res_r, f"refine b{b} r{r}")
+    for part in (pool.map(oracle_pool._refine_job, refine_jobs) if refine_jobs else []):
+        merge(res_r, part)
     return res_c, res_r
 
 
