@@ -55,7 +55,7 @@ def test_chunk_refine_fullsize(inputs, partition, g):
 
     G = L // g
     rng = np.random.default_rng(7 + g)
-    groups = sorted(set(range(3)) | {G - 1, G - 2} | set(rng.integers(0, G, 5).tolist()))
+    groups = sorted(set(range(3)) | {G - 1, G - 2} | set(rng.integers(0, G, 64).tolist()))
     chs, cands = rows_of(ch, groups), rows_of(cand, groups)
     members = [m * g + i for m in groups for i in range(g)]
     ids, scs = rows_of(idx, members), rows_of(sc, members)
