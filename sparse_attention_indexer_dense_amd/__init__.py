@@ -51,7 +51,7 @@ def load(path: str = LIB_PATH):
         return _lib
     if not os.path.exists(path):
         raise RuntimeError(
-            f"{path} is missing: build it with `python -c 'import __graft_entry__ as g; g.build()'`")
+            f"{path} is missing: build it with `python -m sparse_attention_indexer_dense_amd.build`")
     lib = ctypes.CDLL(path)
     P, i64, i32, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_size_t
     lib.indexer_workspace_bytes.argtypes = [i32, i32, i64, i64, i32, i32, i32, i32, i32]
