@@ -113,13 +113,45 @@ __device__ __forceinline__ void wave_priority(int p)
         __builtin_amdgcn_s_setprio(0);
 }
 
+// v moved across the lanes of each 16-lane row by a DPP control (gfx9
+// encoding); lanes whose source lies outside the row get `old`.
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t old, uint32_t v)
+{
+    return (uint32_t)__builtin_amdgcn_update_dpp((int)old, (int)v, CTRL, 0xF, 0xF, false);
+}
+
+// Wave-wide reduction by a commutative, associative op; every lane gets the
+// result. Butterflies inside each quad and each row are DPP operands of the
+// op itself; the rows, then the halves, are combined by lane swaps. No LDS
+// round trip. Every lane of the wave must be active.
+template <typename Op>
+__device__ __forceinline__ uint32_t wave_reduce(uint32_t v, Op op)
+{
+    v = op(v, dpp_u32<0xB1>(v, v));   // quad_perm [1,0,3,2]
+    v = op(v, dpp_u32<0x4E>(v, v));   // quad_perm [2,3,0,1]
+    v = op(v, dpp_u32<0x141>(v, v));  // row_half_mirror: the other quad of 8
+    v = op(v, dpp_u32<0x140>(v, v));  // row_mirror: the other 8 of 16
+    const auto p = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+    v = op(p[0], p[1]);               // rows 0+1, rows 2+3
+    const auto q = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+    return op(q[0], q[1]);            // both halves
+}
+
 // Wave-wide sum of an int (all lanes get it).
 __device__ __forceinline__ int wave_sum(int v)
 {
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1)
-        v += __shfl_xor(v, o, kWave);
-    return v;
+    return (int)wave_reduce((uint32_t)v, [](uint32_t a, uint32_t b) { return a + b; });
+}
+
+__device__ __forceinline__ uint32_t wave_min(uint32_t v)
+{
+    return wave_reduce(v, [](uint32_t a, uint32_t b) { return a < b ? a : b; });
+}
+
+__device__ __forceinline__ uint32_t wave_max(uint32_t v)
+{
+    return wave_reduce(v, [](uint32_t a, uint32_t b) { return a > b ? a : b; });
 }
 
 // ---------------------------------------------------------------- radix cut
@@ -133,16 +165,20 @@ struct Cut {
 };
 
 // Inclusive suffix sum over the lanes of a wave: lane l gets sum_{l' >= l} v.
+// Within each row of 16 lanes a shift-and-add ladder (DPP row shifts, zero
+// past the row's end); then each row adds the totals of the rows above it,
+// read from their first lanes. Every lane of the wave must be active.
 __device__ __forceinline__ int wave_suffix_sum(int v)
 {
     const int l = lane_id();
-#pragma unroll
-    for (int o = 1; o < kWave; o <<= 1) {
-        const int u = __shfl_down(v, o, kWave);
-        if (l + o < kWave)
-            v += u;
-    }
-    return v;
+    v += (int)dpp_u32<0x101>(0u, (uint32_t)v);  // row_shl:1
+    v += (int)dpp_u32<0x102>(0u, (uint32_t)v);  // row_shl:2
+    v += (int)dpp_u32<0x104>(0u, (uint32_t)v);  // row_shl:4
+    v += (int)dpp_u32<0x108>(0u, (uint32_t)v);  // row_shl:8
+    const int t1 = __builtin_amdgcn_readlane(v, 16);
+    const int t2 = __builtin_amdgcn_readlane(v, 32);
+    const int t3 = __builtin_amdgcn_readlane(v, 48);
+    return v + (l < 16 ? t1 : 0) + (l < 32 ? t2 : 0) + (l < 48 ? t3 : 0);
 }
 
 // Largest bin x with sum_{y >= x} h[y] >= target (the caller guarantees the
@@ -162,7 +198,7 @@ __device__ __forceinline__ void find_bin(const uint32_t *h, int target, int &x, 
     const int t = wave_suffix_sum(s);
     const uint64_t m = ballot(t >= target);
     const int lc = 63 - __builtin_clzll(m);  // highest lane whose suffix reaches target
-    int run = uniform(__shfl(t, lc, kWave) - __shfl(s, lc, kWave));
+    int run = __builtin_amdgcn_readlane(t, lc) - __builtin_amdgcn_readlane(s, lc);
     int bx = lc * P, ab = run;
     for (int top = P; top > 0; top -= kWave) {
         const int lo = top > kWave ? top - kWave : 0;  // bins [lo, top) of lane lc's range
@@ -173,10 +209,10 @@ __device__ __forceinline__ void find_bin(const uint32_t *h, int target, int &x, 
         if (mm) {
             const int li = 63 - __builtin_clzll(mm);
             bx = lc * P + lo + li;
-            ab = __shfl(sv - v, li, kWave);
+            ab = __builtin_amdgcn_readlane(sv - v, li);
             break;
         }
-        run = uniform(__shfl(sv, 0, kWave));  // all of [lo, top) added
+        run = __builtin_amdgcn_readlane(sv, 0);  // all of [lo, top) added
     }
     x = uniform(bx);
     above = uniform(ab);

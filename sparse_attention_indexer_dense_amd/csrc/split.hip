@@ -292,22 +292,6 @@ struct SelOut {
     int fan;  // rows the selection is written to, sel entries apart
 };
 
-__device__ __forceinline__ uint32_t wave_min(uint32_t v)
-{
-#pragma unroll
-    for (int o = 1; o < kWave; o <<= 1)
-        v = min(v, (uint32_t)__shfl_xor((int)v, o, kWave));
-    return v;
-}
-
-__device__ __forceinline__ uint32_t wave_max(uint32_t v)
-{
-#pragma unroll
-    for (int o = 1; o < kWave; o <<= 1)
-        v = max(v, (uint32_t)__shfl_xor((int)v, o, kWave));
-    return v;
-}
-
 // Per-wave totals gathered over the block: the exclusive prefix of t in wave
 // order, its total, and the key range. t, lo and hi are wave-uniform.
 struct WaveTotals {
@@ -415,7 +399,7 @@ __device__ __forceinline__ Cut block_radix_cut(int m, int sel, uint32_t base, ui
                 int slot0 = 0;
                 if (lane == 0)
                     slot0 = atomicAdd(&sm.nbnd, __popcll(bm));
-                slot0 = __shfl(slot0, 0, kWave);
+                slot0 = __builtin_amdgcn_readlane(slot0, 0);
                 if (hit) {
                     const int sl = slot0 + prefix_count(bm);
                     sm.bkey[sl] = k;
