@@ -251,8 +251,9 @@ __global__ __launch_bounds__(kSplitWaves * kWave) void split_score_kernel(SplitS
 // ascending, so their causal entries come first.
 //
 // A row that fits in LDS is copied there whole. A longer row is reduced first:
-// an exact order statistic of a strided sample gives a lower bound theta that,
-// with high probability, at least `sel` scores of the row reach; the scores
+// the floor of the histogram bin that holds an order statistic of a strided
+// sample is a lower bound theta that, with high probability, at least `sel`
+// scores of the row reach; the scores
 // >= theta are packed into LDS in index order (one read of the row, held in
 // registers between counting and packing). The exact top-`sel` lies among
 // them whenever there are at least `sel`; when there are fewer, or more than
@@ -478,6 +479,28 @@ __device__ __forceinline__ Cut block_radix_cut(int m, int sel, uint32_t base, ui
     return c;  // not reached: the last level has shift 0
 }
 
+// A lower bound for the rk-th largest of the m keys key_at(0..m-1), all in
+// [base, hi]: the floor of the level-1 bin (2048 bins of the top bits of
+// key - base) that holds it, so at least rk of the keys reach it. One
+// histogram pass; the boundary bin is not resolved.
+template <typename KeyAt>
+__device__ __forceinline__ uint32_t rank_bin_floor(int m, int rk, uint32_t base, uint32_t hi, KeyAt key_at,
+                                                   SelShared &sm)
+{
+    const uint32_t span = hi - base;
+    const int nb = span ? 32 - __builtin_clz(span) : 0;
+    const int s1 = nb > 11 ? nb - 11 : 0;
+    for (int i = threadIdx.x; i < kBins1; i += kSelectThreads)
+        sm.h[i] = 0u;
+    lds_sync();
+    for (int i = threadIdx.x; i < m; i += kSelectThreads)
+        atomicAdd(&sm.h[(key_at(i) - base) >> s1], 1u);
+    lds_sync();
+    int b1, a1;
+    block_find_bin(sm.h, rk, sm, b1, a1);
+    return base + ((uint32_t)b1 << s1);
+}
+
 // Writes the entries of a cut over m entries in index order (entry i: score
 // score_at(i), row position pos_at(i)). Wave w takes the w-th contiguous
 // segment; ballots give ranks among equal keys and output slots. The
@@ -577,10 +600,11 @@ __device__ __forceinline__ float f4(const float4 &v, int x)
     return x == 0 ? v.x : (x == 1 ? v.y : (x == 2 ? v.z : v.w));
 }
 
-// Lower bound theta for the top-`sel` of the n scores of a row: an exact
-// order statistic of a sample of contiguous 64-score chunks spread evenly over
-// the row, of rank chosen with slack so that, with high probability, at least
-// sel scores of the row reach it. Whether they do is checked by the caller.
+// Lower bound theta for the top-`sel` of the n scores of a row: the floor of
+// the histogram bin holding an order statistic of a sample of contiguous
+// 64-score chunks spread evenly over the row, of rank chosen with slack so
+// that, with high probability, at least sel scores of the row reach it.
+// Whether they do is checked by the caller.
 __device__ __forceinline__ uint32_t sample_theta(const float *sc, int n, int sel, SelShared &sm)
 {
     constexpr int kPer = kSampleMax / kSelectThreads;
@@ -608,9 +632,7 @@ __device__ __forceinline__ uint32_t sample_theta(const float *sc, int n, int sel
     const float expect = (float)sel * (float)ns / (float)n;
     int r = (int)ceilf(expect + 4.f * sqrtf(expect)) + 8;
     r = r < ns ? r : ns;
-    const Cut c = block_radix_cut(ns, r, st.lo, st.hi, [&](int i) { return score_key(sm.cs[i]); }, sm);
-    lds_sync();
-    return c.req > 0 ? c.keq : (uint32_t)(c.kgt + 1);
+    return rank_bin_floor(ns, r, st.lo, st.hi, [&](int i) { return score_key(sm.cs[i]); }, sm);
 }
 
 // The scores >= theta among positions [b, e) of a row (b a multiple of 4),
@@ -685,14 +707,13 @@ __device__ __forceinline__ int count_pack(const float *sc, int b, int e, uint32_
 // holds its contiguous segment in registers, one score per lane per step of
 // 64 positions, and the sample, the count and the pack all work on those
 // registers. The sample is every kSampleEvery-th step of each wave (at most
-// 8192 scores, packed into LDS); its order statistic gives the key theta as
-// in sample_theta. Counting and packing compare floats with the float of
+// 8192 scores, packed into LDS); it gives the key theta as in sample_theta. Counting and packing compare floats with the float of
 // theta, which orders finite scores exactly as their keys do once a theta of
 // +0 is lowered to -0 (both zeros then pass, as their keys do). Padding
-// positions hold -inf and never pass, because theta is the key of a finite
-// sampled score (a row holding -inf takes the exact path instead). Returns the
-// number of scores >= theta; if it is at most kCandCap they are packed into
-// cs/cp in index order, with [lo, hi] their key range.
+// positions hold -inf and never pass, because theta lies within the key range
+// of finite sampled scores (a row holding -inf takes the exact path instead).
+// Returns the number of scores >= theta; if it is at most kCandCap they are
+// packed into cs/cp in index order, with [lo, hi] their key range.
 constexpr int kRegDw = 64;                         // steps per lane held in registers
 constexpr int kRegRow = kSelectThreads * kRegDw;   // longest row held whole
 constexpr int kSampleEvery = 8;
@@ -738,9 +759,7 @@ __device__ __forceinline__ int reg_stage(const float *sc, int n, int sel, SelSha
     const float expect = (float)sel * (float)ns / (float)n;
     int rk = (int)ceilf(expect + 4.f * sqrtf(expect)) + 8;
     rk = rk < ns ? rk : ns;
-    const Cut c = block_radix_cut(ns, rk, st.lo, st.hi, [&](int i) { return score_key(sm.cs[i]); }, sm);
-    lds_sync();
-    uint32_t theta = c.req > 0 ? c.keq : (uint32_t)(c.kgt + 1);
+    uint32_t theta = rank_bin_floor(ns, rk, st.lo, st.hi, [&](int i) { return score_key(sm.cs[i]); }, sm);
     if (theta == 0x80000000u)  // +0: lower to -0
         theta = 0x7FFFFFFFu;
     const float thf = key_score(theta);
