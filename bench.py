@@ -14,7 +14,8 @@ the CPU oracle timed on a bounded sample of the same workload.
 
 usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
                        [--sweep | --chunk-sweep | --chunk-only PARTITION,G,NSEL]
-                       [--no-decode] [--no-chunks]
+                       [--no-decode] [--no-chunks] [--variants dense,reuse,refine]
+       python bench.py --decode-only [--steps K] [--warmup W]
 """
 from __future__ import annotations
 
@@ -330,6 +331,10 @@ def main():
     ap.add_argument("--cpu-rows", type=int, default=512,
                     help="rows of the oracle CPU baseline (0 disables it)")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--decode-only", action="store_true",
+                    help="instead of the step: only the decode Refine step (--steps timed calls; for traces)")
+    ap.add_argument("--variants", default=None, metavar="dense[,reuse][,refine]",
+                    help="variants run in the step (default: all the workload has; for counter runs)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run one 1 GiB device copy (counter calibration)")
     ap.add_argument("--sweep", action="store_true",
@@ -357,12 +362,21 @@ def main():
         sys.exit(1)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.decode_only:
+        print(json.dumps(bench_decode(dsa, synth, torch, iters=args.steps, warmup=args.warmup)), flush=True)
+        return
     w = synth.WORKLOADS[args.workload]
     print(f"[bench] generating {w.name} inputs", file=sys.stderr, flush=True)
     Q, W, K = synth.make(w, device=dev)
     B, L, q_len, H, d = dsa._shapes(Q, W, K)
     k, g, c = w.k, w.g, w.c
     variants = list(w.variants)
+    if args.variants:
+        want = args.variants.split(",")
+        if "dense" not in want or any(v not in variants for v in want):
+            print(f"--variants must name dense and a subset of {variants}", file=sys.stderr)
+            sys.exit(2)
+        variants = [v for v in variants if v in want]
     if args.sweep:
         sweep(dsa, torch, Q, W, K, k)
         return
