@@ -413,17 +413,21 @@ int run_split(int mode, const Pass &ps, const uint16_t *Q, const float *W, const
     sp.nrows = nrows;
     sp.rowlen = rowlen;
     const int64_t npos_max = (mode == kRefine) ? std::min<int64_t>(ps.c, b.L) : (ps.glim ? ps.krows : b.L);
-    sp.chunk = split_chunk((int64_t)b.B * nrows, npos_max, mode == kRefine);
+    // Refine member rows of one group share its candidate list: with an even
+    // g each wave scores two of them on every gathered key tile
+    const int mr = (mode == kRefine && sp.g % 2 == 0) ? 2 : 1;
+    const int64_t nunits = ceil_div(nrows, mr);  // row units per batch item
+    sp.chunk = split_chunk((int64_t)b.B * nunits, npos_max, mode == kRefine);
     sp.scores = scores;
     sp.glim = ps.glim;
     sp.krows = ps.krows;
     sp.cand_n = ps.cand_n;
     hipError_t e = hipSuccess;
-    for (int64_t r0 = 0; r0 < nrows; r0 += kGridYMax) {
+    for (int64_t r0 = 0; r0 < nrows; r0 += kGridYMax * mr) {
         sp.row0 = r0;
-        dim3 grid((unsigned)ceil_div(npos_max, sp.chunk), (unsigned)std::min<int64_t>(kGridYMax, nrows - r0),
-                  (unsigned)b.B);
-        e = launch_split_score(H, D, sp, grid, stream);
+        dim3 grid((unsigned)ceil_div(npos_max, sp.chunk),
+                  (unsigned)std::min<int64_t>(kGridYMax, ceil_div(nrows - r0, mr)), (unsigned)b.B);
+        e = launch_split_score(H, D, sp, mr, grid, stream);
         if (e != hipSuccess)
             return hip_fail(e, "split score launch");
     }

@@ -194,7 +194,9 @@ hipError_t launch_fill_guarded(const ReqDesc *req, int B, int64_t L, int64_t q_l
 hipError_t launch_scan_select(int H, int D, int NW, int mode, const ScanParams &prm, int grid,
                               hipStream_t stream);
 hipError_t launch_pool(int H, int D, const PoolParams &prm, hipStream_t stream);
-hipError_t launch_split_score(int H, int D, const SplitScoreParams &prm, dim3 grid, hipStream_t stream);
+// mr: score rows per wave (2: Refine member rows paired over their group's
+// candidate list; needs an even g)
+hipError_t launch_split_score(int H, int D, const SplitScoreParams &prm, int mr, dim3 grid, hipStream_t stream);
 hipError_t launch_split_select(const SplitSelectParams &prm, hipStream_t stream);
 hipError_t launch_chunk_fixed(int B, int64_t L, int64_t block, int64_t nc, int32_t *cend, hipStream_t stream);
 hipError_t launch_chunk_means(int D, const uint16_t *K, int B, int64_t L, const int32_t *cend, int64_t nc,

@@ -11,7 +11,9 @@
 //                         registers as MFMA B fragments (several tiles in
 //                         flight while one is scored), runs the MFMA score
 //                         tile and the ReLU/weight/head-sum epilogue, and
-//                         stores one fp32 score per position;
+//                         stores one fp32 score per position (a Refine
+//                         wave scores two member rows of one group on each
+//                         gathered tile when g is even);
 //   split_select_kernel - one workgroup per score row finds the exact top-sel
 //                         (ties to the lower index): a row that fits in LDS
 //                         is staged whole; a longer one is first reduced to
@@ -106,16 +108,17 @@ __device__ __forceinline__ SplitRow split_row(const SplitScoreParams &p, int H, 
 // are plain vector loads, whose completion the compiler tracks exactly.
 constexpr int kSplitDepth = 4;
 
-template <int H, int D, bool LIST>
+template <int H, int D, bool LIST, int MR>
 __global__ __launch_bounds__(kSplitWaves * kWave) void split_score_kernel(SplitScoreParams p)
 {
     using S = Shape<H, D>;
     constexpr int MB = S::MB, KS = S::KS;
-    constexpr int P = kSplitDepth;
+    constexpr int P = MR == 1 ? kSplitDepth : kSplitDepth / 2;  // two rows: twice the work per tile
+    static_assert(MR == 1 || (MR == 2 && LIST), "rows share a wave only over one candidate list");
     __shared__ int32_t lst[kSplitWaves][LIST ? kSplitSpanMax : 1];
 
     const int bi = blockIdx.z;
-    const int64_t r = p.row0 + blockIdx.y;
+    const int64_t r = p.row0 + (int64_t)blockIdx.y * MR;
     const int wave = uniform(threadIdx.x / kWave);  // wave-uniform (SGPR)
     const int lane = threadIdx.x % kWave;
     const int half = lane >> 5;
@@ -128,8 +131,26 @@ __global__ __launch_bounds__(kSplitWaves * kWave) void split_score_kernel(SplitS
     const int w1 = (w0 + span < sr.npos) ? w0 + span : sr.npos;
     const int ntile = (w1 - w0 + 31) / 32;
     const uint16_t *Kb = sr.Kb;
-    float *out = p.scores + ((int64_t)bi * p.nrows + r) * p.rowlen;
+    float *out = p.scores + ((int64_t)bi * p.nrows + r) * p.rowlen;  // row r + m at out + m * rowlen
     int32_t *wl = lst[wave];
+
+    // With MR = 2 the wave also scores row r + 1, the next member of the same
+    // group (rows are paired only when g is even, so a pair never straddles
+    // two groups): both rows use every gathered key tile. A second row past
+    // the request's end scores row r's query and stores nothing.
+    const uint16_t *qrow[MR];
+    const float *wrow[MR];
+    bool live[MR];
+    qrow[0] = sr.q;
+    wrow[0] = sr.w;
+    live[0] = true;
+#pragma unroll
+    for (int m = 1; m < MR; ++m) {
+        const SplitRow s2 = split_row(p, H, D, bi, r + m);
+        live[m] = s2.npos > 0;
+        qrow[m] = live[m] ? s2.q : sr.q;
+        wrow[m] = live[m] ? s2.w : sr.w;
+    }
 
     if (LIST) {
         for (int x = lane; x < w1 - w0; x += kWave)
@@ -137,24 +158,27 @@ __global__ __launch_bounds__(kSplitWaves * kWave) void split_score_kernel(SplitS
         __builtin_amdgcn_wave_barrier();
     }
 
-    // the query row as MFMA A fragments (chunk order as above) and the
+    // the query rows as MFMA A fragments (chunk order as above) and the
     // weights per accumulator row
-    bf16x8 qa[MB][KS];
-    float wv[MB][16];
+    bf16x8 qa[MR][MB][KS];
+    float wv[MR][MB][16];
 #pragma unroll
-    for (int mb = 0; mb < MB; ++mb) {
-        const int head = mb * 32 + col;
+    for (int m = 0; m < MR; ++m) {
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-            u32x4 v = {0u, 0u, 0u, 0u};
-            if (head < H)
-                v = *reinterpret_cast<const u32x4 *>(sr.q + (int64_t)head * D + (2 * ks + half) * 8);
-            qa[mb][ks] = __builtin_bit_cast(bf16x8, v);
-        }
+        for (int mb = 0; mb < MB; ++mb) {
+            const int head = mb * 32 + col;
 #pragma unroll
-        for (int rr = 0; rr < 16; ++rr) {
-            const int hr = mb * 32 + 8 * (rr / 4) + 4 * half + (rr % 4);
-            wv[mb][rr] = hr < H ? sr.w[hr] : 0.f;
+            for (int ks = 0; ks < KS; ++ks) {
+                u32x4 v = {0u, 0u, 0u, 0u};
+                if (head < H)
+                    v = *reinterpret_cast<const u32x4 *>(qrow[m] + (int64_t)head * D + (2 * ks + half) * 8);
+                qa[m][mb][ks] = __builtin_bit_cast(bf16x8, v);
+            }
+#pragma unroll
+            for (int rr = 0; rr < 16; ++rr) {
+                const int hr = mb * 32 + 8 * (rr / 4) + 4 * half + (rr % 4);
+                wv[m][mb][rr] = hr < H ? wrow[m][hr] : 0.f;
+            }
         }
     }
 
@@ -175,35 +199,51 @@ __global__ __launch_bounds__(kSplitWaves * kWave) void split_score_kernel(SplitS
         for (int ks = 0; ks < KS; ++ks)
             kf[ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(src + ks * 16));
     };
-    auto mfma_tile = [&](const bf16x8 (&kf)[KS], f32x16 (&acc)[MB]) {
+    auto mfma_tile = [&](const bf16x8 (&kf)[KS], f32x16 (&acc)[MR][MB]) {
 #pragma unroll
-        for (int mb = 0; mb < MB; ++mb)
-            acc[mb] = f32x16{};
+        for (int m = 0; m < MR; ++m)
+#pragma unroll
+            for (int mb = 0; mb < MB; ++mb)
+                acc[m][mb] = f32x16{};
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
-            for (int mb = 0; mb < MB; ++mb)
-                acc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[mb][ks], kf[ks], acc[mb], 0, 0, 0);
+            for (int m = 0; m < MR; ++m)
+#pragma unroll
+                for (int mb = 0; mb < MB; ++mb)
+                    acc[m][mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[m][mb][ks], kf[ks], acc[m][mb], 0, 0, 0);
     };
     // epilogue of tile t and its store: positions whose key is beyond the
-    // row's limit get a score too, which the selection ignores
-    auto finish = [&](int t, const f32x16 (&acc)[MB]) {
-        float part[MB];
+    // row's limit get a score too, which the selection ignores. With two
+    // rows one lane swap leaves row r's totals in lanes 0-31 and row r+1's
+    // in lanes 32-63 (the same additions as for one row).
+    auto finish = [&](int t, const f32x16 (&acc)[MR][MB]) {
+        float srow[MR];
 #pragma unroll
-        for (int mb = 0; mb < MB; ++mb) {
-            part[mb] = 0.f;
+        for (int m = 0; m < MR; ++m) {
+            float part[MB];
 #pragma unroll
-            for (int rr = 0; rr < 16; ++rr)
-                part[mb] = fmaf(wv[mb][rr], relu(acc[mb][rr]), part[mb]);
+            for (int mb = 0; mb < MB; ++mb) {
+                part[mb] = 0.f;
+#pragma unroll
+                for (int rr = 0; rr < 16; ++rr)
+                    part[mb] = fmaf(wv[m][mb][rr], relu(acc[m][mb][rr]), part[mb]);
+            }
+            srow[m] = part[0];
+#pragma unroll
+            for (int mb = 1; mb < MB; ++mb)
+                srow[m] += part[mb];
         }
-        float s = part[0];
-#pragma unroll
-        for (int mb = 1; mb < MB; ++mb)
-            s += part[mb];
-        const float total = half_wave_sum(s) + 0.0f;
         const int pos = w0 + t * 32 + col;
-        if (lane < 32 && pos < w1)
-            out[pos] = total;
+        if constexpr (MR == 1) {
+            const float total = half_wave_sum(srow[0]) + 0.0f;
+            if (lane < 32 && pos < w1)
+                out[pos] = total;
+        } else {
+            const float total = half_wave_sum2(srow[0], srow[MR - 1]) + 0.0f;
+            if (pos < w1 && live[half])
+                out[(int64_t)half * p.rowlen + pos] = total;
+        }
     };
 
     // ring slots are compile-time: P tiles per trip; the MFMAs of tile t run
@@ -211,7 +251,7 @@ __global__ __launch_bounds__(kSplitWaves * kWave) void split_score_kernel(SplitS
 #pragma unroll
     for (int u = 0; u < P - 1; ++u)
         load_tile(u, kq[u]);
-    f32x16 a0[MB], a1[MB];
+    f32x16 a0[MR][MB], a1[MR][MB];
     for (int t0 = 0; t0 < ntile; t0 += P) {
 #pragma unroll
         for (int u = 0; u < P; ++u) {
@@ -230,7 +270,7 @@ __global__ __launch_bounds__(kSplitWaves * kWave) void split_score_kernel(SplitS
                     finish(t - 1, a1);
                 }
 #pragma unroll
-                for (int q = 0; q < KS * MB; ++q) {
+                for (int q = 0; q < KS * MB * MR; ++q) {
                     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
                     __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
                 }
@@ -994,23 +1034,28 @@ __global__ __launch_bounds__(kSelectThreads) void split_select_kernel(SplitSelec
 
 // ------------------------------------------------------------- launchers
 template <int H, int D>
-static hipError_t launch_split_score_t(const SplitScoreParams &prm, dim3 grid, hipStream_t stream)
+static hipError_t launch_split_score_t(const SplitScoreParams &prm, int mr, dim3 grid, hipStream_t stream)
 {
-    if (prm.mode == kRefine)
-        hipLaunchKernelGGL((split_score_kernel<H, D, true>), grid, dim3(kSplitWaves * kWave), 0, stream, prm);
+    const dim3 block(kSplitWaves * kWave);
+    if (prm.mode == kRefine && mr == 2)
+        hipLaunchKernelGGL((split_score_kernel<H, D, true, 2>), grid, block, 0, stream, prm);
+    else if (prm.mode == kRefine)
+        hipLaunchKernelGGL((split_score_kernel<H, D, true, 1>), grid, block, 0, stream, prm);
     else
-        hipLaunchKernelGGL((split_score_kernel<H, D, false>), grid, dim3(kSplitWaves * kWave), 0, stream, prm);
+        hipLaunchKernelGGL((split_score_kernel<H, D, false, 1>), grid, block, 0, stream, prm);
     return hipGetLastError();
 }
 
-hipError_t launch_split_score(int H, int D, const SplitScoreParams &prm, dim3 grid, hipStream_t stream)
+hipError_t launch_split_score(int H, int D, const SplitScoreParams &prm, int mr, dim3 grid, hipStream_t stream)
 {
     if (prm.chunk % (32 * kSplitWaves) != 0 || (prm.mode == kRefine && prm.chunk / kSplitWaves > kSplitSpanMax))
         return hipErrorInvalidValue;
+    if (mr != 1 && !(mr == 2 && prm.mode == kRefine && prm.g % 2 == 0))
+        return hipErrorInvalidValue;
     if (H == 64 && D == 128)
-        return launch_split_score_t<64, 128>(prm, grid, stream);
+        return launch_split_score_t<64, 128>(prm, mr, grid, stream);
     if (H == 4 && D == 32)
-        return launch_split_score_t<4, 32>(prm, grid, stream);
+        return launch_split_score_t<4, 32>(prm, mr, grid, stream);
     return hipErrorInvalidValue;
 }
 
