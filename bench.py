@@ -7,14 +7,15 @@ re-score, top-k). Inputs are resident in HBM before timing starts. The line
 printed at the end reports scored (query, key) pairs per second for the whole
 step, top-k rows per second, the dense kernel against the bf16 MFMA roofline,
 recall of Reuse/Refine against dense, a decode step (32 requests x 65536
-cached keys, 2 new rows each, Refine) against the HBM roofline, the key-chunk
+cached keys, 2 new rows each, Refine) against the HBM roofline, the dense
+indexer alone at L = 16384 against the MFMA roofline, the key-chunk
 coarse stage (fixed and score-adaptive partitions of 64-key blocks, chunk scan
 and Refine, on keys with local structure) with its recall against dense, and
 the CPU oracle timed on a bounded sample of the same workload.
 
 usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
                        [--sweep | --chunk-sweep | --chunk-only PARTITION,G,NSEL]
-                       [--no-decode] [--no-chunks] [--variants dense,reuse,refine]
+                       [--no-decode] [--no-chunks] [--no-dense16k] [--variants dense,reuse,refine]
        python bench.py --decode-only [--steps K] [--warmup W]
 """
 from __future__ import annotations
@@ -197,6 +198,34 @@ def bench_decode(dsa, synth, torch, iters=20, warmup=3):
             "hbm_frac": gbs / PEAK_HBM_GBS, "recall_vs_dense": rec}
 
 
+def bench_dense16k(dsa, synth, torch, iters=10, warmup=2):
+    """The dense indexer alone on the L = 16384 prefill sequence (H_I = 64,
+    d_I = 128, k = 2048): kernel time per launch (HIP events) against the bf16
+    MFMA roofline."""
+    w = synth.WORKLOADS["dense16k"]
+    Q, W, K = synth.make(w, device="cuda")
+    ws = dsa.Workspace()
+    out = (torch.empty((1, w.L, w.k), dtype=torch.int32, device="cuda"),
+           torch.empty((1, w.L, w.k), dtype=torch.float32, device="cuda"))
+    for _ in range(warmup):
+        dsa.dense(Q, W, K, w.k, ws=ws, out=out)
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(iters + 1)]
+    ev[0].record()
+    for i in range(iters):
+        dsa.dense(Q, W, K, w.k, ws=ws, out=out)
+        ev[i + 1].record()
+    torch.cuda.synchronize()
+    t = sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(iters))
+    ms = ev[0].elapsed_time(ev[-1]) / iters
+    pairs = dense_pairs(w.L, w.L)
+    flop = pairs * 2 * w.H * w.d
+    return {"workload": "dense16k", "L": w.L, "k": w.k, "ms": ms, "median_ms": t[len(t) // 2],
+            "pairs_per_s": pairs / (ms * 1e-3), "queries_per_s": w.L / (ms * 1e-3),
+            "achieved_TFLOPs": flop / (ms * 1e-3) / 1e12,
+            "mfma_frac": flop / (ms * 1e-3) / (PEAK_BF16_TFLOPS * 1e12)}
+
+
 # -------------------------------------------------------------------- sweep
 SWEEP_G = (2, 4, 8, 16)
 SWEEP_C = (2048, 4096, 8192)
@@ -340,6 +369,7 @@ def main():
     ap.add_argument("--sweep", action="store_true",
                     help="instead of the step: recall and time of Reuse/Refine over g, c and proxy")
     ap.add_argument("--no-chunks", action="store_true", help="skip the key-chunk measurement")
+    ap.add_argument("--no-dense16k", action="store_true", help="skip the L=16384 dense measurement")
     ap.add_argument("--chunk-sweep", action="store_true",
                     help="instead of the step: the key-chunk path over partitions, g and nsel")
     ap.add_argument("--chunk-only", default=None, metavar="PARTITION,G,NSEL",
@@ -490,6 +520,11 @@ def main():
         print("[bench] decode step", file=sys.stderr, flush=True)
         decode = bench_decode(dsa, synth, torch)
 
+    d16 = None
+    if not args.no_dense16k:
+        print("[bench] dense indexer at L=16384", file=sys.stderr, flush=True)
+        d16 = bench_dense16k(dsa, synth, torch)
+
     chunks = None
     if not args.no_chunks:
         print("[bench] key-chunk path", file=sys.stderr, flush=True)
@@ -513,6 +548,7 @@ def main():
         "variants": detail,
         "roofline": roofline,
         "decode": decode,
+        "dense16k": d16,
         "chunks": chunks,
         "cpu_baseline": cpu,
         "wall_s_timed": wall,

@@ -60,6 +60,21 @@ def test_pivot_varlen(shape, variant):
     assert rd.rows == 0 and rr.rows == sum(q)
 
 
+@pytest.mark.parametrize("g", [2, 3, 6])
+def test_refine_split_rows_per_wave(g):
+    # few rows per request (split-key kernels): with an even g a wave scores
+    # two member rows of a group on each gathered tile, with an odd g one;
+    # counts of 1, 3 and 5 rows leave a pair's second row missing or a short
+    # last group
+    L, q = [3000, 9000, 700, 5000], [3, 5, 1, 6]
+    Q, W, K = packed(L, q, seed=11)
+    c, k = 256, 64
+    out = dsa.pivot_refine_varlen(Q, W, K, L, q, g, c, k, cand=True)
+    rd, rc, rr = check_varlen("refine", Q, W, K, L, q, g, c, k, 0, out)
+    assert_ok(rd, rc, rr)
+    assert rr.rows == sum(q)
+
+
 def test_reuse_varlen_without_candidates():
     L, q = SCAN
     Q, W, K = packed(L, q, seed=5)
