@@ -155,6 +155,7 @@ def cpu_baseline(Q, W, K, k, L, q_len, budget_rows, seed=0):
     busy = sum(t for _, t in done)  # seconds the workers spent on the rows
     full = dense_pairs(L, q_len)
     return {"value": pairs / dt, "unit": "pairs/s", "cores": workers, "kind": "oracle",
+            "host_cpu_count": os.cpu_count(),
             "sample": f"dense rows of the same L={L} sequence: {len(rows)} rows drawn uniformly "
                       f"(seed {seed}), {pairs:.3e} scored pairs, fp64 single-threaded oracle per "
                       f"worker process, {dt:.1f} s wall",

@@ -209,7 +209,8 @@ def _check(rc):
 
 
 class Workspace:
-    """Reusable device workspace (grown on demand)."""
+    """Reusable device workspace (grown on demand). Calls that share one
+    workspace must not overlap in time: use one per stream."""
 
     def __init__(self):
         self.buf = None
@@ -222,7 +223,37 @@ class Workspace:
         return self.buf
 
 
-_default_ws = Workspace()
+class _StreamWorkspaces:
+    """The default workspace: one per (device, stream), so that calls issued on
+    different streams never share scratch memory. (A buffer that grows is
+    replaced only for calls on its own stream, where the caching allocator
+    may reuse the old one once that stream passes the calls that used it.)"""
+
+    def __init__(self):
+        self._ws = {}
+
+    def get(self, nbytes, device):
+        import torch
+        device = torch.device(device)
+        stream = torch.cuda.current_stream(device).cuda_stream
+        key = (device.index if device.index is not None else torch.cuda.current_device(), stream)
+        ws = self._ws.get(key)
+        if ws is None:
+            ws = self._ws[key] = Workspace()
+        return ws.get(nbytes, device)
+
+
+_default_ws = _StreamWorkspaces()
+
+
+def _check_out(t, name, shape, dtype, device):
+    """A caller-provided output tensor must match what the kernels write."""
+    if t is None:
+        return
+    if tuple(t.shape) != tuple(shape) or t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype} {tuple(shape)}, got {t.dtype} {tuple(t.shape)}")
+    if t.device != device or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous tensor on {device}")
 
 
 def _run(mode, Q, W, K, k, g=1, c=0, scores=True, cand=False, ws=None, out=None):
@@ -239,6 +270,15 @@ def _run(mode, Q, W, K, k, g=1, c=0, scores=True, cand=False, ws=None, out=None)
         out_cand = torch.empty((B, G, c), dtype=torch.int32, device=dev) if cand else None
     else:
         out_idx, out_score, out_cand = (tuple(out) + (None, None))[:3]
+        if out_idx is None:
+            raise ValueError("out must hold out_idx")
+        G = (q_len + g - 1) // g
+        _check_out(out_idx, "out_idx", (B, q_len, k), torch.int32, dev)
+        _check_out(out_score, "out_score", (B, q_len, k), torch.float32, dev)
+        if mode == DENSE:
+            out_cand = None
+        else:
+            _check_out(out_cand, "out_cand", (B, G, c), torch.int32, dev)
     stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
     if mode == DENSE:
         rc = indexer_dense(_ptr(Q), _ptr(W), _ptr(K), B, L, q_len, H, d, k, _ptr(out_idx),

@@ -188,6 +188,21 @@ def weights(L, H, seed, device="cpu", out=None):
     return out
 
 
+def signed_weights(L, H, seed, device="cpu", out=None):
+    """Head weights [L, H] fp32 of either sign, U(-1, 1) / H. Nothing in the
+    index score makes w non-negative; these exercise negative and cancelling
+    scores."""
+    device = torch.device(device)
+    if out is None:
+        out = torch.empty((L, H), dtype=torch.float32, device=device)
+    for c0 in range(0, L, QUERY_CHUNK):
+        c1 = min(L, c0 + QUERY_CHUNK)
+        u = torch.rand((c1 - c0, H), generator=_gen(device, seed, STREAM_WEIGHT, c0 // QUERY_CHUNK),
+                       device=device)
+        out[c0:c1] = (2.0 * u - 1.0) / H
+    return out
+
+
 def prefill(L, H, d, rho, rank, seed, device="cpu", coef_var=0.5):
     """One prefill sequence: Q [1, L, H, d] bf16, W [1, L, H] fp32, K [1, L, d] bf16."""
     Q = queries(L, H, d, rho, seed, device)

@@ -39,7 +39,7 @@ def rand_inputs(rng, L, H, d, q_len=None, neg_w=False):
 
 
 def parse_golden(path=GOLDEN):
-    g = dict(K={}, Q={}, W={}, I={}, TOPK=[], PROXYQ={}, PROXYW={}, SCAN={}, CAND={},
+    g = dict(K={}, Q={}, W={}, I={}, MASS={}, TOPK=[], PROXYQ={}, PROXYW={}, SCAN={}, CAND={},
              REUSE={}, REFINE={}, ROUND=[], PIVOT=None)
     with open(path) as f:
         for line in f:
@@ -83,7 +83,7 @@ def pin_golden_scores(lib):
     for t in range(L):
         sc, ms = oracle.scores(Q[t], W[t], K, n=t + 1, lib=lib)
         assert np.array_equal(sc, np.array(g["I"][t])), (t, sc, g["I"][t])
-        assert np.all(ms >= np.abs(sc))
+        assert np.array_equal(ms, np.array(g["MASS"][t])), (t, ms, g["MASS"][t])
 
 
 def pin_golden_topk(lib):
@@ -155,6 +155,29 @@ def pin_relu_identities(lib):
         assert np.all(np.abs((a - b) - lin) <= tol)
         assert np.all(np.abs((a + b) - np.abs(dots) @ w) <= tol)
         assert np.all(ma + 1e-12 * ma >= ab * (1 - 1e-12))
+
+
+def pin_exact_dyadic(lib):
+    """Signed dyadic inputs: q and k are multiples of 1/2 in [-2, 2], w multiples
+    of 1/4 in [-1, 1]. Every product and partial sum is then exact in fp64, in
+    any order, so numpy's float64 products give the exact score
+    I = max(0, K q^T) w and the exact tolerance mass A = (|K| |q|^T) |w|, and the
+    oracle must equal both bit for bit (negative and zero weights included)."""
+    rng = np.random.default_rng(19)
+    H, d, L = 5, 12, 40
+    for t in range(3):
+        q = bf16_bits(rng.integers(-4, 5, (H, d)) * 0.5)
+        K = bf16_bits(rng.integers(-4, 5, (L, d)) * 0.5)
+        w = (rng.integers(-4, 5, H) * 0.25).astype(np.float32)
+        w[t] = 0.0
+        qf, Kf = bits_to_f64(q), bits_to_f64(K)
+        sc, ms = oracle.scores(q, w, K, lib=lib)
+        dots = Kf @ qf.T  # [L, H], exact
+        want = np.maximum(dots, 0.0) @ w.astype(np.float64)
+        mass = (np.abs(Kf) @ np.abs(qf).T) @ np.abs(w.astype(np.float64))
+        assert np.array_equal(sc, want), (t, sc - want)
+        assert np.array_equal(ms, mass), (t, ms - mass)
+        assert np.any(sc < 0) and np.any(sc == 0)
 
 
 def pin_homogeneity_and_heads(lib):
@@ -308,14 +331,38 @@ def pin_candidate_injection(lib):
     o = oracle.pivot_groups(Q, W, K, g, c, k, list(range(ng)), lib=lib)
     o2 = oracle.pivot_groups(Q, W, K, g, c, k, list(range(ng)), cand_in=o["cand"], lib=lib)
     assert np.array_equal(o["refine"], o2["refine"])
+    # group 0 ends at position 3: its list holds the 4 keys 0..3, then -1 -1;
+    # group 2 ends at position 11 and holds c = 6 keys
+    assert o["cand"][0].tolist()[4:] == [-1, -1] and np.all(o["cand"][2] >= 0)
+    bad_lists = []
     bad = o["cand"].copy()
     bad[2, 1] = bad[2, 0]  # duplicate
-    try:
-        oracle.pivot_groups(Q, W, K, g, c, k, list(range(ng)), cand_in=bad, lib=lib)
-    except ValueError:
-        pass
-    else:
-        raise AssertionError("a duplicated candidate was accepted")
+    bad_lists.append(("a duplicated candidate", bad))
+    bad = o["cand"].copy()
+    bad[2, 3] = 12  # a key after the group's last position
+    bad_lists.append(("a candidate after the group's last position", bad))
+    bad = o["cand"].copy()
+    bad[0, 2] = 4  # the same, in a group whose list is shorter than c
+    bad_lists.append(("a future candidate in a short list", bad))
+    bad = o["cand"].copy()
+    bad[2, 5] = -1  # a list shorter than min(c, t_last + 1)
+    bad_lists.append(("a short candidate list", bad))
+    bad = o["cand"].copy()
+    bad[0, 3] = -1  # the same where the prefix is shorter than c
+    bad_lists.append(("a short list of a short prefix", bad))
+    bad = o["cand"].copy()
+    bad[0, 5] = 0  # a key in the -1 tail
+    bad_lists.append(("a key in the -1 tail", bad))
+    bad = o["cand"].copy()
+    bad[0, 4] = -2  # a tail entry other than -1
+    bad_lists.append(("a tail entry other than -1", bad))
+    for what, bad in bad_lists:
+        try:
+            oracle.pivot_groups(Q, W, K, g, c, k, list(range(ng)), cand_in=bad, lib=lib)
+        except ValueError:
+            pass
+        else:
+            raise AssertionError(f"{what} was accepted")
 
 
 def pin_short_last_group(lib):
@@ -576,6 +623,7 @@ ALL_PINS = [
     pin_golden_pivot,
     pin_golden_proxy_rounding,
     pin_relu_identities,
+    pin_exact_dyadic,
     pin_homogeneity_and_heads,
     pin_one_hot,
     pin_select_vs_lexsort,

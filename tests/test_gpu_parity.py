@@ -162,3 +162,28 @@ def test_deterministic_repeat():
     b = dsa.pivot_refine(Q, W, K, 4, 128, 64, cand=True)
     for x, y in zip(a, b):
         assert torch.equal(x, y)
+
+
+def test_binding_rejects_mismatched_outputs():
+    # caller-provided outputs are checked before any launch: wrong shape,
+    # dtype or device never reach the kernels
+    import sparse_attention_indexer_dense_amd as dsa
+    Q, W, K = tiny(L=256)
+    k = 16
+    good = torch.empty((1, 256, k), dtype=torch.int32, device=DEV)
+    score = torch.empty((1, 256, k), dtype=torch.float32, device=DEV)
+    bad = [
+        (torch.empty((1, 256, k - 1), dtype=torch.int32, device=DEV), score),
+        (torch.empty((1, 256, k), dtype=torch.int64, device=DEV), score),
+        (torch.empty((1, 256, k), dtype=torch.int32), score),
+        (good, torch.empty((1, 255, k), dtype=torch.float32, device=DEV)),
+        (torch.empty((1, k, 256), dtype=torch.int32, device=DEV).transpose(1, 2), score),
+    ]
+    for out in bad:
+        with pytest.raises(ValueError):
+            dsa.dense(Q, W, K, k, out=out)
+    with pytest.raises(ValueError):
+        dsa.pivot_refine(Q, W, K, 4, 32, k, out=(good, score, torch.empty((1, 63, 32), dtype=torch.int32,
+                                                                             device=DEV)))
+    i, s = dsa.dense(Q, W, K, k, out=(good, score))
+    assert i.data_ptr() == good.data_ptr()

@@ -23,6 +23,18 @@ MUTANTS = {
     "relu_is_abs": ("double relu = dot > 0.0 ? dot : 0.0;", "double relu = fabs(dot);"),
     "weight_of_head0": ("total += (double)w[j] * relu;", "total += (double)w[0] * relu;"),
     "weight_dropped": ("total += (double)w[j] * relu;", "total += relu;"),
+    "mass_abs_of_dot": ("bound += fabs((double)w[j]) * adot;", "bound += fabs((double)w[j]) * fabs(dot);"),
+    "mass_inflated": ("bound += fabs((double)w[j]) * adot;", "bound += 10.0 * fabs((double)w[j]) * adot;"),
+    "mass_signed_weight": ("bound += fabs((double)w[j]) * adot;", "bound += (double)w[j] * adot;"),
+    "mass_unweighted": ("bound += fabs((double)w[j]) * adot;", "bound += adot;"),
+    "mass_signed_products": ("adot += fabs(p);", "adot += p;"),
+    "candidate_after_last": ("if (s < 0 || s > t_last || seen[s])",
+                             "if (s < 0 || s > t_last + 1 || (s <= t_last && seen[s]))"),
+    "candidate_tail_unchecked": ("} else if (s != -1) {", "} else if (s < -1) {"),
+    "candidate_tail_negative_ok": ("} else if (s != -1) {", "} else if (s >= 0) {"),
+    "candidate_list_short": ("int64_t want = c < t_last + 1 ? c : t_last + 1;",
+                             "int64_t want = c < t_last + 1 ? c - 1 : t_last;"),
+    "candidate_duplicates_ok": ("if (s < 0 || s > t_last || seen[s])", "if (s < 0 || s > t_last)"),
     "query_of_head0": ("double p = qd[(int64_t)j * d + e] * kd[e];", "double p = qd[e] * kd[e];"),
     "key_element0": ("kd[e] = bf16_to_double(K[s * d + e]);", "kd[e] = bf16_to_double(K[s * d]);"),
     "causal_strict": ("int64_t n = L - q_len + r + 1;", "int64_t n = L - q_len + r;"),
