@@ -51,7 +51,8 @@
  * Memory ownership. Every pointer is caller-owned device memory (16-byte
  * aligned for Q, K and ws). The library allocates and frees nothing, never
  * synchronises the stream, and keeps no state between calls except the last
- * error message of the calling thread. Work is enqueued on `stream`; results
+ * error message of the calling thread (and, for indexer_pivot_refine_noalloc
+ * only, its fixed per-device scratch array). Work is enqueued on `stream`; results
  * are valid once the stream reaches that point. `ws` is scratch space of at
  * least indexer_workspace_bytes(...) bytes whose content on entry is
  * irrelevant; calls sharing one ws must not overlap in time.
@@ -133,6 +134,31 @@ int indexer_pivot_refine(const void *Q, const float *W, const void *K,
                          int g, int c, int k,
                          int32_t *out_idx, float *out_score, int32_t *out_cand,
                          void *ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * PIVOT-Refine exactly as indexer_pivot_refine, for callers that cannot
+ * allocate device memory or pass a workspace (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid allocation). Its scratch is an
+ * array of DSAIDX_SCRATCH_BYTES bytes that the library holds on each GPU it
+ * runs on until the process ends (placed when the library's code is loaded on
+ * that device; the library calls no allocator). Sizes whose workspace (what
+ * indexer_pivot_refine would need with the same arguments, at most
+ * indexer_workspace_bytes(DSAIDX_REFINE, ...)) exceeds that return
+ * DSAIDX_EWORKSPACE before anything is enqueued; a decode step of 32 requests
+ * of 65536 keys (g = 2, c = 4096, k = 2048) needs about 9 MiB. `stream` must
+ * belong to the current device. Every call on one GPU uses that GPU's single
+ * copy of the scratch: calls that overlap in time on one GPU (other streams,
+ * other threads) race and must be serialised by the caller. No content of the
+ * scratch carries over from one call to the next. Outputs, ranking, padding,
+ * shapes and errors as for indexer_pivot_refine.
+ */
+#define DSAIDX_SCRATCH_BYTES ((size_t)64 << 20)
+
+int indexer_pivot_refine_noalloc(const void *Q, const float *W, const void *K,
+                                 int B, int64_t L, int64_t q_len, int H_I, int d_I,
+                                 int g, int c, int k,
+                                 int32_t *out_idx, float *out_score, int32_t *out_cand,
+                                 hipStream_t stream);
 
 /*
  * Options of the variable-length PIVOT entry points (NULL: all defaults).

@@ -32,7 +32,7 @@ EXPORTS = ("indexer_workspace_bytes", "indexer_dense", "indexer_pivot_reuse",
            "indexer_pivot_reuse_varlen", "indexer_pivot_refine_varlen", "indexer_chunks_fixed",
            "indexer_chunks_adaptive_workspace_bytes", "indexer_chunks_adaptive", "indexer_chunk_means",
            "indexer_chunk_refine_workspace_bytes", "indexer_chunk_refine", "indexer_sort_rows",
-           "indexer_last_error", "indexer_version")
+           "indexer_last_error", "indexer_version", "indexer_pivot_refine_noalloc")
 
 
 class IndexerError(RuntimeError):
@@ -61,6 +61,8 @@ def load(path: str = LIB_PATH):
     for f in (lib.indexer_pivot_reuse, lib.indexer_pivot_refine):
         f.argtypes = [P, P, P, i32, i64, i64, i32, i32, i32, i32, i32, P, P, P, P, sz, P]
         f.restype = i32
+    lib.indexer_pivot_refine_noalloc.argtypes = [P, P, P, i32, i64, i64, i32, i32, i32, i32, i32, P, P, P, P]
+    lib.indexer_pivot_refine_noalloc.restype = i32
     lib.indexer_varlen_workspace_bytes.argtypes = [i32, i32, P, P, i32, i32, i32, i32, i32, P]
     lib.indexer_varlen_workspace_bytes.restype = sz
     lib.indexer_dense_varlen.argtypes = [P, P, P, i32, P, P, i32, i32, i32, P, P, P, sz, P]
@@ -111,6 +113,12 @@ def indexer_pivot_refine(Q, W, K, B, L, q_len, H_I, d_I, g, c, k, out_idx, out_s
                          ws, ws_bytes, stream):
     return load().indexer_pivot_refine(Q, W, K, B, L, q_len, H_I, d_I, g, c, k, out_idx, out_score,
                                        out_cand, ws, ws_bytes, stream)
+
+
+def indexer_pivot_refine_noalloc(Q, W, K, B, L, q_len, H_I, d_I, g, c, k, out_idx, out_score, out_cand,
+                                 stream):
+    return load().indexer_pivot_refine_noalloc(Q, W, K, B, L, q_len, H_I, d_I, g, c, k, out_idx,
+                                               out_score, out_cand, stream)
 
 
 class PivotOpts(ctypes.Structure):

@@ -15,6 +15,7 @@
 
 #include <algorithm>
 #include <cstdio>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -926,6 +927,48 @@ int check_chunk_sizes(int B, int64_t L, int block)
     return DSAIDX_OK;
 }
 
+// --------------------------------------------------- library-held scratch
+// Scratch of indexer_pivot_refine_noalloc: a fixed device array, one copy per
+// GPU, held until the process ends. In host code the array's name is only a
+// stand-in for the symbol: its device address comes from hipGetSymbolAddress,
+// once per device with that device current, and only that address is used.
+static __device__ __align__(256) unsigned char scratch[DSAIDX_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices] = {};
+
+// The scratch array's device address on the device `stream` runs on (which
+// must be the current device, as for every launch of this library).
+int scratch_address(hipStream_t stream, void **out)
+{
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess)
+        return hip_fail(e, "hipGetDevice");
+    int sdev = -1;
+    e = hipStreamGetDevice(stream, &sdev);
+    if (e != hipSuccess)
+        return hip_fail(e, "hipStreamGetDevice");
+    if (sdev != dev)
+        return fail(DSAIDX_EINVAL, "the stream belongs to device %d, the current device is %d", sdev, dev);
+    if (dev < 0 || dev >= kMaxDevices)
+        return fail(DSAIDX_EUNSUPPORTED, "device %d is beyond the %d devices the scratch table holds", dev,
+                    kMaxDevices);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess)
+            return hip_fail(e, "hipGetSymbolAddress(scratch)");
+        if (!p)
+            return fail(DSAIDX_EHIP, "hipGetSymbolAddress(scratch) returned NULL");
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return DSAIDX_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -977,6 +1020,34 @@ int indexer_pivot_refine(const void *Q, const float *W, const void *K, int B, in
     if (s != DSAIDX_OK)
         return s;
     return run_pivot(DSAIDX_REFINE, b, Q, W, K, H_I, d_I, c, k, out_idx, out_score, out_cand, ws, ws_bytes, stream);
+}
+
+int indexer_pivot_refine_noalloc(const void *Q, const float *W, const void *K, int B, int64_t L, int64_t q_len,
+                                 int H_I, int d_I, int g, int c, int k, int32_t *out_idx, float *out_score,
+                                 int32_t *out_cand, hipStream_t stream)
+{
+    if (g < 1)
+        return fail(DSAIDX_EINVAL, "g=%d must be >= 1", g);
+    Batch b;
+    int s = uniform_batch(B, L, q_len, g, b);
+    if (s != DSAIDX_OK)
+        return s;
+    Plan pl;
+    s = make_plan(DSAIDX_REFINE, b, H_I, d_I, c, k, out_cand != nullptr, pl);
+    if (s != DSAIDX_OK)
+        return s;
+    if (pl.total > (size_t)DSAIDX_SCRATCH_BYTES)
+        return fail(DSAIDX_EWORKSPACE,
+                    "these sizes need %zu bytes of scratch, above the %zu the library holds per device",
+                    pl.total, (size_t)DSAIDX_SCRATCH_BYTES);
+    if (b.total_q == 0)
+        return DSAIDX_OK;
+    void *ws = nullptr;
+    s = scratch_address(stream, &ws);
+    if (s != DSAIDX_OK)
+        return s;
+    return run_pivot(DSAIDX_REFINE, b, Q, W, K, H_I, d_I, c, k, out_idx, out_score, out_cand, ws,
+                     (size_t)DSAIDX_SCRATCH_BYTES, stream);
 }
 
 size_t indexer_varlen_workspace_bytes(int mode, int B, const int64_t *L, const int64_t *q_len, int H_I, int d_I,
