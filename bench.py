@@ -13,8 +13,8 @@ coarse stage (fixed and score-adaptive partitions of 64-key blocks, chunk scan
 and Refine, on keys with local structure) with its recall against dense, and
 the CPU oracle timed on a bounded sample of the same workload.
 
-usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
-                       [--sweep | --chunk-sweep | --chunk-only PARTITION,G,NSEL]
+usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-pivot1m]
+                       [--sweep | --guard-sweep | --chunk-sweep | --chunk-only PARTITION,G,NSEL]
                        [--no-decode] [--no-chunks] [--no-dense16k] [--variants dense,reuse,refine]
        python bench.py --decode-only [--steps K] [--warmup W]
 """
@@ -351,6 +351,207 @@ def bench_chunks(dsa, synth, torch, w, Q, W, configs=CHUNK_CONFIGS, steps=3):
     return res
 
 
+# --------------------------------------------------------------------- step
+def bench_step(dsa, torch, Q, W, K, w, variants, steps, warmup):
+    """Warm-up passes, then `steps` timed passes of the variants (dense, Reuse,
+    Refine) over the same inputs, HIP events between the calls; work counted
+    outside the timed region."""
+    B, L, q_len, H, d = dsa._shapes(Q, W, K)
+    k, g, c = w.k, w.g, w.c
+    dev = Q.device
+
+    def alloc(cand_c=None):
+        G = (q_len + g - 1) // g
+        return (torch.empty((B, q_len, k), dtype=torch.int32, device=dev),
+                torch.empty((B, q_len, k), dtype=torch.float32, device=dev),
+                torch.empty((B, G, cand_c), dtype=torch.int32, device=dev) if cand_c else None)
+
+    outs = {v: alloc(c if v == "refine" else None) for v in variants}
+    wss = {v: dsa.Workspace() for v in variants}
+
+    def run(v):
+        if v == "dense":
+            dsa.dense(Q, W, K, k, ws=wss[v], out=outs[v][:2])
+        elif v == "reuse":
+            dsa.pivot_reuse(Q, W, K, g, k, ws=wss[v], out=outs[v])
+        else:
+            dsa.pivot_refine(Q, W, K, g, c, k, ws=wss[v], out=outs[v])
+
+    print("[bench] warmup", file=sys.stderr, flush=True)
+    for _ in range(warmup):
+        for v in variants:
+            run(v)
+    torch.cuda.synchronize()
+
+    print("[bench] timed steps", file=sys.stderr, flush=True)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(variants) + 1)]
+          for _ in range(steps)]
+    t0 = time.perf_counter()
+    torch.cuda.synchronize()
+    for s in range(steps):
+        ev[s][0].record()
+        for i, v in enumerate(variants):
+            run(v)
+            ev[s][i + 1].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per_variant = {v: 0.0 for v in variants}
+    samples = {v: [] for v in variants}
+    step_ms = 0.0
+    for s in range(steps):
+        for i, v in enumerate(variants):
+            t = ev[s][i].elapsed_time(ev[s][i + 1])
+            per_variant[v] += t / steps
+            samples[v].append(t)
+        step_ms += ev[s][0].elapsed_time(ev[s][-1]) / steps
+
+    # work accounting (outside the timed region)
+    pd = dense_pairs(L, q_len) * B
+    pp = proxy_pairs(L, q_len, g) * B if g > 0 else 0
+    pairs = {"dense": pd}
+    if "reuse" in variants:
+        pairs["reuse"] = pp
+    if "refine" in variants:
+        pairs["refine"] = pp + refine_pairs(outs["refine"][2], L, q_len, g)
+    total_pairs = sum(pairs[v] for v in variants)
+    flop_per_pair = 2 * H * d
+    detail = {}
+    for v in variants:
+        ms = per_variant[v]
+        detail[v] = {"ms": ms, "median_ms": sorted(samples[v])[len(samples[v]) // 2], "scored_pairs": pairs[v],
+                     "pairs_per_s": pairs[v] / (ms * 1e-3),
+                     "dense_equiv_pairs_per_s": pd / (ms * 1e-3),
+                     "queries_per_s": B * q_len / (ms * 1e-3),
+                     "mfma_frac": pairs[v] * flop_per_pair / (ms * 1e-3) / (PEAK_BF16_TFLOPS * 1e12)}
+        if v != "dense":
+            detail[v]["speedup_vs_dense"] = per_variant["dense"] / ms
+            detail[v]["recall_vs_dense"] = recall(outs[v][0], outs["dense"][0])
+    return {"outs": outs, "per_variant": per_variant, "detail": detail, "step_ms": step_ms,
+            "total_pairs": total_pairs, "wall": wall, "dense_pairs": pd}
+
+
+def bench_pivot1m(dsa, synth, torch, dev):
+    """The long-context workload (L = 1048576, g = 16, c = 8192, k = 2048):
+    one warm-up and one timed pass of dense, Reuse and Refine on the same
+    inputs (HIP events around each call), recall of Reuse and Refine against
+    dense over every row."""
+    w = synth.WORKLOADS["pivot1m"]
+    Q, W, K = synth.make(w, device=dev)
+    step = bench_step(dsa, torch, Q, W, K, w, list(w.variants), 1, 1)
+    det = step["detail"]
+    res = {"workload": w.name, "L": w.L, "g": w.g, "c": w.c, "k": w.k, "steps": 1, "warmup": 1,
+           "ms_per_step": step["step_ms"], "pairs_per_s": step["total_pairs"] / (step["step_ms"] * 1e-3),
+           "variants": {v: {x: det[v][x] for x in ("ms", "scored_pairs", "pairs_per_s", "queries_per_s",
+                                                   "mfma_frac", "speedup_vs_dense", "recall_vs_dense")
+                            if x in det[v]} for v in det}}
+    del step, Q, W, K
+    torch.cuda.empty_cache()
+    return res
+
+
+# ------------------------------------------------------------ guard sweep
+GUARD_L = (2048, 4096, 8192, 16384, 32768, 65536, 131072)
+
+
+def guard_sweep(dsa, synth, torch, steps=3, g=4, c=4096, k=2048):
+    """Dense against PIVOT-Refine without and with the guard (guard = c: a
+    group whose whole prefix fits in c keys is scored densely, which for
+    Refine leaves the results unchanged; guard = 2c: groups whose prefix holds
+    up to 2c keys are scored densely, their rows exact) and PIVOT-Reuse, at
+    short and long sequences, through the variable-length entry points. One
+    JSON line per L."""
+    ws = dsa.Workspace()
+
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(steps):
+            out = fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return out, e0.elapsed_time(e1) / steps
+
+    rows = []
+    for L in GUARD_L:
+        Q, W, K = synth.prefill(L, 64, 128, 0.95, 4, seed=0, device="cuda")
+        Qp, Wp, Kp = Q[0].contiguous(), W[0].contiguous(), K[0].contiguous()
+        del Q, W, K
+        kk = min(k, L)
+        (d_idx, _), d_ms = timed(lambda: dsa.dense_varlen(Qp, Wp, Kp, [L], [L], kk, scores=False, ws=ws))
+        (r_idx, _, _), r_ms = timed(lambda: dsa.pivot_refine_varlen(Qp, Wp, Kp, [L], [L], g, c, kk, guard=0,
+                                                                    scores=False, ws=ws))
+        (q_idx, _, _), q_ms = timed(lambda: dsa.pivot_refine_varlen(Qp, Wp, Kp, [L], [L], g, c, kk, guard=c,
+                                                                    scores=False, ws=ws))
+        (q2_idx, _, _), q2_ms = timed(lambda: dsa.pivot_refine_varlen(Qp, Wp, Kp, [L], [L], g, c, kk,
+                                                                      guard=2 * c, scores=False, ws=ws))
+        (u_idx, _, _), u_ms = timed(lambda: dsa.pivot_reuse_varlen(Qp, Wp, Kp, [L], [L], g, kk, scores=False,
+                                                                   ws=ws))
+        row = {"sweep": "guard", "L": L, "g": g, "c": c, "k": kk, "dense_ms": d_ms, "refine_ms": r_ms,
+               "refine_guarded_ms": q_ms, "refine_guarded_2c_ms": q2_ms, "reuse_ms": u_ms,
+               "guarded_groups": min(c // g, (L + g - 1) // g),
+               "guarded_groups_2c": min(2 * c // g, (L + g - 1) // g),
+               "guarded_refine_le_dense": q_ms <= d_ms, "guarded_2c_refine_le_dense": q2_ms <= d_ms,
+               "recall_refine_guarded_2c": recall(q2_idx, d_idx),
+               "refine_identical_with_guard": bool(torch.equal(r_idx, q_idx)),
+               "recall_refine": recall(r_idx, d_idx), "recall_reuse": recall(u_idx, d_idx)}
+        print(json.dumps(row), flush=True)
+        rows.append(row)
+        del d_idx, r_idx, q_idx, q2_idx, u_idx, Qp, Wp, Kp
+        torch.cuda.empty_cache()
+    return rows
+
+
+def kernel_ms(torch, fn, pattern):
+    """Mean device time (ms) of the kernels whose name contains `pattern`, and
+    their count, over one call of fn, from torch's profiler (which traces every
+    HIP kernel launched in the process, the library's included)."""
+    from torch.profiler import ProfilerActivity, profile
+    torch.cuda.synchronize()
+    with profile(activities=[ProfilerActivity.CUDA]) as prof:
+        fn()
+        torch.cuda.synchronize()
+    times = []
+    for e in prof.events():
+        if pattern not in e.name:
+            continue
+        us = getattr(e, "device_time", None)
+        if us is None:
+            us = getattr(e, "cuda_time", None)
+        if us:
+            times.append(float(us) / 1e3)
+    if not times:
+        return None, 0
+    return sum(times) / len(times), len(times)
+
+
+def refine_gather(dsa, torch, Q, W, K, g, c, k, cand):
+    """The prefill Refine re-score (scan_select_kernel in its Refine mode: each
+    group's candidate keys gathered by DMA once for its members) against the
+    HBM roofline: algorithmic bytes = every group's causal candidate keys
+    (2 d bytes each) plus its list, the members' queries and weights, and their
+    outputs; time = that kernel's own device time, from torch's profiler."""
+    B, q_len, H, d = Q.shape
+    L = K.shape[1]
+    G = cand.shape[1]
+    t_last = torch.clamp((torch.arange(G, device=cand.device) + 1) * g, max=q_len) - 1 + (L - q_len)
+    ncand = int(torch.clamp(t_last + 1, max=c).sum()) * B
+    gather = ncand * 2 * d
+    total = gather + ncand * 4 + B * q_len * (H * d * 2 + H * 4 + k * 8)
+    try:
+        ms, n = kernel_ms(torch, lambda: dsa.pivot_refine(Q, W, K, g, c, k, scores=False), ", 2>(dsaidx::ScanParams)")
+    except Exception as e:  # noqa: BLE001 - report, do not fail the bench line
+        return {"error": f"profiler: {e!r}"}
+    if ms is None:
+        return {"error": "no Refine scan kernel in the profile"}
+    return {"kernel": "scan_select_kernel<64,128,4,refine>", "launches": n, "kernel_ms": ms,
+            "candidate_keys": ncand, "gather_bytes": gather, "algorithmic_bytes": total,
+            "gather_GBps": gather / (ms * 1e-3) / 1e9, "achieved_GBps": total / (ms * 1e-3) / 1e9,
+            "hbm_frac": total / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS}
+
+
 # --------------------------------------------------------------------- main
 def main():
     ap = argparse.ArgumentParser()
@@ -373,6 +574,9 @@ def main():
     ap.add_argument("--no-dense16k", action="store_true", help="skip the L=16384 dense measurement")
     ap.add_argument("--chunk-sweep", action="store_true",
                     help="instead of the step: the key-chunk path over partitions, g and nsel")
+    ap.add_argument("--guard-sweep", action="store_true",
+                    help="instead of the step: dense vs Refine with and without the guard over L")
+    ap.add_argument("--no-pivot1m", action="store_true", help="skip the L=1048576 pass")
     ap.add_argument("--chunk-only", default=None, metavar="PARTITION,G,NSEL",
                     help="instead of the step: build one partition and run only that chunk call "
                          "(--steps times; for kernel traces)")
@@ -395,6 +599,9 @@ def main():
     torch.cuda.set_device(dev)
     if args.decode_only:
         print(json.dumps(bench_decode(dsa, synth, torch, iters=args.steps, warmup=args.warmup)), flush=True)
+        return
+    if args.guard_sweep:
+        guard_sweep(dsa, synth, torch)
         return
     w = synth.WORKLOADS[args.workload]
     print(f"[bench] generating {w.name} inputs", file=sys.stderr, flush=True)
@@ -429,72 +636,10 @@ def main():
         print(json.dumps(bench_chunks(dsa, synth, torch, w, Q, W, configs=CHUNK_SWEEP, steps=2)), flush=True)
         return
 
-    def alloc(cand_c=None):
-        G = (q_len + g - 1) // g
-        return (torch.empty((B, q_len, k), dtype=torch.int32, device=dev),
-                torch.empty((B, q_len, k), dtype=torch.float32, device=dev),
-                torch.empty((B, G, cand_c), dtype=torch.int32, device=dev) if cand_c else None)
-
-    outs = {"dense": alloc(), "reuse": alloc(), "refine": alloc(c)}
-    wss = {v: dsa.Workspace() for v in variants}
-
-    def run(v):
-        if v == "dense":
-            dsa.dense(Q, W, K, k, ws=wss[v], out=outs[v][:2])
-        elif v == "reuse":
-            dsa.pivot_reuse(Q, W, K, g, k, ws=wss[v], out=outs[v])
-        else:
-            dsa.pivot_refine(Q, W, K, g, c, k, ws=wss[v], out=outs[v])
-
-    print("[bench] warmup", file=sys.stderr, flush=True)
-    for _ in range(args.warmup):
-        for v in variants:
-            run(v)
-    torch.cuda.synchronize()
-
-    print("[bench] timed steps", file=sys.stderr, flush=True)
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(variants) + 1)]
-          for _ in range(args.steps)]
-    t0 = time.perf_counter()
-    torch.cuda.synchronize()
-    for s in range(args.steps):
-        ev[s][0].record()
-        for i, v in enumerate(variants):
-            run(v)
-            ev[s][i + 1].record()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    per_variant = {v: 0.0 for v in variants}
-    samples = {v: [] for v in variants}
-    step_ms = 0.0
-    for s in range(args.steps):
-        for i, v in enumerate(variants):
-            t = ev[s][i].elapsed_time(ev[s][i + 1])
-            per_variant[v] += t / args.steps
-            samples[v].append(t)
-        step_ms += ev[s][0].elapsed_time(ev[s][-1]) / args.steps
-
-    # work accounting (outside the timed region)
-    pd = dense_pairs(L, q_len) * B
-    pp = proxy_pairs(L, q_len, g) * B if g > 0 else 0
-    pairs = {"dense": pd}
-    if "reuse" in variants:
-        pairs["reuse"] = pp
-    if "refine" in variants:
-        pairs["refine"] = pp + refine_pairs(outs["refine"][2], L, q_len, g)
-    total_pairs = sum(pairs[v] for v in variants)
+    step = bench_step(dsa, torch, Q, W, K, w, variants, args.steps, args.warmup)
+    outs, per_variant, detail = step["outs"], step["per_variant"], step["detail"]
+    step_ms, total_pairs, wall, pd = step["step_ms"], step["total_pairs"], step["wall"], step["dense_pairs"]
     flop_per_pair = 2 * H * d
-    detail = {}
-    for v in variants:
-        ms = per_variant[v]
-        detail[v] = {"ms": ms, "median_ms": sorted(samples[v])[len(samples[v]) // 2], "scored_pairs": pairs[v],
-                     "pairs_per_s": pairs[v] / (ms * 1e-3),
-                     "dense_equiv_pairs_per_s": pd / (ms * 1e-3),
-                     "queries_per_s": B * q_len / (ms * 1e-3),
-                     "mfma_frac": pairs[v] * flop_per_pair / (ms * 1e-3) / (PEAK_BF16_TFLOPS * 1e12)}
-        if v != "dense":
-            detail[v]["speedup_vs_dense"] = per_variant["dense"] / ms
-            detail[v]["recall_vs_dense"] = recall(outs[v][0], outs["dense"][0])
 
     dense_ms = per_variant["dense"]
     achieved = pd * flop_per_pair / (dense_ms * 1e-3) / 1e12
@@ -508,6 +653,12 @@ def main():
                 "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS, "traffic": traffic,
                 "kernel": "scan_select_kernel<64,128,8,dense>",
                 "flop_per_launch": pd * flop_per_pair}
+
+    gather = None
+    if "refine" in variants:
+        print("[bench] Refine re-score kernel (profiler)", file=sys.stderr, flush=True)
+        gather = refine_gather(dsa, torch, Q, W, K, g, c, k, outs["refine"][2])
+        detail["refine"]["gather"] = gather
 
     if args.calibrate_copy:
         a = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
@@ -537,6 +688,13 @@ def main():
         cpu = cpu_baseline(Q, W, K, k, L, q_len, args.cpu_rows)
         cpu["gpu_over_cpu"] = (total_pairs / (step_ms * 1e-3)) / cpu["value"]
 
+    p1m = None
+    if not args.no_pivot1m and w.name == "pivot128k":
+        del outs, step, Q, W, K
+        torch.cuda.empty_cache()
+        print("[bench] L=1048576 pass", file=sys.stderr, flush=True)
+        p1m = bench_pivot1m(dsa, synth, torch, dev)
+
     value = total_pairs / (step_ms * 1e-3)
     line = {
         "metric": "indexer (query,key) pairs/s + top-k queries/s at L=128K; % MFMA / HBM peak",
@@ -551,6 +709,7 @@ def main():
         "decode": decode,
         "dense16k": d16,
         "chunks": chunks,
+        "pivot1m": p1m,
         "cpu_baseline": cpu,
         "wall_s_timed": wall,
         "kernel_hash": kernel_hash(),
