@@ -577,6 +577,8 @@ def main():
     ap.add_argument("--guard-sweep", action="store_true",
                     help="instead of the step: dense vs Refine with and without the guard over L")
     ap.add_argument("--no-pivot1m", action="store_true", help="skip the L=1048576 pass")
+    ap.add_argument("--no-gather", action="store_true",
+                    help="skip the profiler timing of the Refine re-score kernel (for counter runs)")
     ap.add_argument("--chunk-only", default=None, metavar="PARTITION,G,NSEL",
                     help="instead of the step: build one partition and run only that chunk call "
                          "(--steps times; for kernel traces)")
@@ -655,7 +657,7 @@ def main():
                 "flop_per_launch": pd * flop_per_pair}
 
     gather = None
-    if "refine" in variants:
+    if "refine" in variants and not args.no_gather:
         print("[bench] Refine re-score kernel (profiler)", file=sys.stderr, flush=True)
         gather = refine_gather(dsa, torch, Q, W, K, g, c, k, outs["refine"][2])
         detail["refine"]["gather"] = gather
