@@ -271,7 +271,7 @@ int indexer_chunks_fixed(int B, int64_t L, int block, int32_t *cend, hipStream_t
 
 /* Score-adaptive chunks (the reading taken of SCALE's rule; the abstract gives
  * no procedure): start from fixed blocks of `block` keys (block even,
- * n = ceil(L / block) blocks, at most 4096 per request). The split gain of a
+ * n = ceil(L / block) blocks, at most 262144 per request). The split gain of a
  * full block is the drop of the squared reconstruction error by the mean,
  * D(block) - D(first half) - D(second half); the merge loss of an aligned pair
  * of full blocks (2j, 2j+1) is D(pair) - D(2j) - D(2j+1). Splits are taken in

@@ -916,6 +916,46 @@ int run_chunk_refine(const Batch &b, const void *Qv, const float *W, const void 
     return DSAIDX_OK;
 }
 
+// Workspace of the adaptive partition: split gains and merge losses, and,
+// beyond kAdaptBlocksLds blocks per request, the space their sort runs in.
+struct AdaptLayout {
+    int64_t n, nfull, npair, g2, p2;
+    size_t off_loss, off_gk, off_gi, off_lk, off_li, total;
+};
+
+int64_t pow2_at_least(int64_t x)
+{
+    int64_t p = 1;
+    while (p < x)
+        p <<= 1;
+    return p;
+}
+
+AdaptLayout adapt_layout(int B, int64_t L, int64_t block)
+{
+    AdaptLayout a{};
+    a.n = ceil_div(L, block);
+    a.nfull = L / block;
+    a.npair = a.nfull / 2;
+    a.g2 = pow2_at_least(std::max<int64_t>(a.nfull, 1));
+    a.p2 = pow2_at_least(std::max<int64_t>(a.npair, 1));
+    size_t off = align_up((size_t)B * a.nfull * sizeof(double));
+    a.off_loss = off;
+    off += align_up((size_t)B * a.npair * sizeof(double));
+    if (a.n > kAdaptBlocksLds) {
+        a.off_gk = off;
+        off += align_up((size_t)B * a.g2 * sizeof(double));
+        a.off_gi = off;
+        off += align_up((size_t)B * a.g2 * sizeof(int32_t));
+        a.off_lk = off;
+        off += align_up((size_t)B * a.p2 * sizeof(double));
+        a.off_li = off;
+        off += align_up((size_t)B * a.p2 * sizeof(int32_t));
+    }
+    a.total = off;
+    return a;
+}
+
 int check_chunk_sizes(int B, int64_t L, int block)
 {
     if (B < 1 || B > 65535)
@@ -1122,8 +1162,7 @@ size_t indexer_chunks_adaptive_workspace_bytes(int B, int64_t L, int block)
 {
     if (check_chunk_sizes(B, L, block) != DSAIDX_OK)
         return 0;
-    const int64_t nfull = L / block;
-    return align_up((size_t)B * nfull * sizeof(double)) + align_up((size_t)B * (nfull / 2) * sizeof(double));
+    return adapt_layout(B, L, block).total;
 }
 
 int indexer_chunks_adaptive(const void *K, int B, int64_t L, int d_I, int block, int32_t *cend, void *ws,
@@ -1147,16 +1186,25 @@ int indexer_chunks_adaptive(const void *K, int B, int64_t L, int d_I, int block,
         return fail(DSAIDX_EINVAL, "ws must be a non-NULL 16-byte aligned pointer (%zu bytes needed)", need);
     if (ws_bytes < need)
         return fail(DSAIDX_EWORKSPACE, "workspace of %zu bytes is below the %zu needed", ws_bytes, need);
+    const AdaptLayout al = adapt_layout(B, L, block);
+    unsigned char *wsb = static_cast<unsigned char *>(ws);
     ChunkAdaptParams p{};
     p.K = static_cast<const uint16_t *>(K);
     p.L = L;
     p.block = block;
-    p.n = n;
-    p.nfull = L / block;
-    p.npair = p.nfull / 2;
-    p.gain = static_cast<double *>(ws);
-    p.loss = reinterpret_cast<double *>(static_cast<unsigned char *>(ws) +
-                                        align_up((size_t)B * p.nfull * sizeof(double)));
+    p.n = al.n;
+    p.nfull = al.nfull;
+    p.npair = al.npair;
+    p.g2 = al.g2;
+    p.p2 = al.p2;
+    p.gain = reinterpret_cast<double *>(wsb);
+    p.loss = reinterpret_cast<double *>(wsb + al.off_loss);
+    if (al.n > kAdaptBlocksLds) {
+        p.gk = reinterpret_cast<double *>(wsb + al.off_gk);
+        p.gi = reinterpret_cast<int32_t *>(wsb + al.off_gi);
+        p.lk = reinterpret_cast<double *>(wsb + al.off_lk);
+        p.li = reinterpret_cast<int32_t *>(wsb + al.off_li);
+    }
     p.cend = cend;
     hipError_t e = launch_chunk_adaptive(d_I, B, p, stream);
     return e == hipSuccess ? DSAIDX_OK : hip_fail(e, "adaptive chunk launch");

@@ -288,21 +288,26 @@ __global__ __launch_bounds__(D) void chunk_disp_kernel(ChunkAdaptParams p)
 // losses (lowest first), ties to the lower number; the greedy pairing of
 // splits and merges while the gain exceeds the loss (passing over a split
 // whose pair is merged and a merge that holds a split block or the split
-// candidate); then the chunk ends in key order.
+// candidate); then the chunk ends in key order. Up to kAdaptBlocksLds blocks
+// the sort runs in LDS, beyond that on the workspace (the same steps through
+// generic pointers); the split and merge flags are LDS bitmaps either way.
 constexpr int kAdaptThreads = 1024;
 
 struct RankLds {
-    double gk[kAdaptBlocksMax];
-    int32_t gi[kAdaptBlocksMax];
-    double lk[kAdaptBlocksMax / 2];
-    int32_t li[kAdaptBlocksMax / 2];
-    uint8_t split[kAdaptBlocksMax];
-    uint8_t merged[kAdaptBlocksMax / 2];
-    int32_t cnt[kAdaptBlocksMax + 1];
+    double gk[kAdaptBlocksLds];
+    int32_t gi[kAdaptBlocksLds];
+    double lk[kAdaptBlocksLds / 2];
+    int32_t li[kAdaptBlocksLds / 2];
+    uint32_t split[kAdaptBlocksMax / 32];
+    uint32_t merged[kAdaptBlocksMax / 64];
     int32_t wsum[kAdaptThreads / kWave];
 };
 
-// bitonic sort of n2 (a power of two) entries; `before(x, y)` is a strict total order
+__device__ __forceinline__ bool bit_of(const uint32_t *b, int i) { return (b[i >> 5] >> (i & 31)) & 1u; }
+
+// bitonic sort of n2 (a power of two) entries; `before(x, y)` is a strict
+// total order; the arrays are in LDS or in global memory written only by this
+// workgroup (a barrier separates the passes)
 template <typename Before>
 __device__ __forceinline__ void bitonic(double *k, int32_t *ix, int n2, Before before)
 {
@@ -334,71 +339,69 @@ __global__ __launch_bounds__(kAdaptThreads) void chunk_greedy_kernel(ChunkAdaptP
     const int bi = blockIdx.x;
     const int tid = threadIdx.x;
     const int nfull = (int)p.nfull, npair = (int)p.npair, n = (int)p.n;
-    int g2 = 1, p2 = 1;
-    while (g2 < nfull)
-        g2 <<= 1;
-    while (p2 < npair)
-        p2 <<= 1;
+    const int g2 = (int)p.g2, p2 = (int)p.p2;
+    const bool lds = n <= kAdaptBlocksLds;
+    double *gk = lds ? sm.gk : p.gk + (int64_t)bi * g2;
+    int32_t *gi = lds ? sm.gi : p.gi + (int64_t)bi * g2;
+    double *lk = lds ? sm.lk : p.lk + (int64_t)bi * p2;
+    int32_t *li = lds ? sm.li : p.li + (int64_t)bi * p2;
     const double *gain = p.gain + (int64_t)bi * p.nfull;
     const double *loss = p.loss + (int64_t)bi * p.npair;
     for (int i = tid; i < g2; i += kAdaptThreads) {
-        sm.gk[i] = i < nfull ? gain[i] : -__builtin_inf();
-        sm.gi[i] = i < nfull ? i : 0x7FFFFFFF;
+        gk[i] = i < nfull ? gain[i] : -__builtin_inf();
+        gi[i] = i < nfull ? i : 0x7FFFFFFF;
     }
     for (int i = tid; i < p2; i += kAdaptThreads) {
-        sm.lk[i] = i < npair ? loss[i] : __builtin_inf();
-        sm.li[i] = i < npair ? i : 0x7FFFFFFF;
+        lk[i] = i < npair ? loss[i] : __builtin_inf();
+        li[i] = i < npair ? i : 0x7FFFFFFF;
     }
-    for (int i = tid; i < n; i += kAdaptThreads)
-        sm.split[i] = 0;
-    for (int i = tid; i < npair; i += kAdaptThreads)
-        sm.merged[i] = 0;
+    for (int i = tid; i < (n + 31) / 32; i += kAdaptThreads)
+        sm.split[i] = 0u;
+    for (int i = tid; i < (npair + 31) / 32; i += kAdaptThreads)
+        sm.merged[i] = 0u;
     __syncthreads();
-    bitonic(sm.gk, sm.gi, g2, [](double ka, int32_t ia, double kb, int32_t ib) {
+    bitonic(gk, gi, g2, [](double ka, int32_t ia, double kb, int32_t ib) {
         return ka > kb || (ka == kb && ia < ib);
     });
-    bitonic(sm.lk, sm.li, p2, [](double ka, int32_t ia, double kb, int32_t ib) {
+    bitonic(lk, li, p2, [](double ka, int32_t ia, double kb, int32_t ib) {
         return ka < kb || (ka == kb && ia < ib);
     });
     if (tid == 0) {
         int ia = 0, ib = 0;
         for (;;) {
-            while (ia < nfull && sm.gi[ia] / 2 < npair && sm.merged[sm.gi[ia] / 2])
+            while (ia < nfull && gi[ia] / 2 < npair && bit_of(sm.merged, gi[ia] / 2))
                 ++ia;
             while (ib < npair) {
-                const int jj = sm.li[ib];
-                const bool conflict =
-                    sm.split[2 * jj] || sm.split[2 * jj + 1] || (ia < nfull && sm.gi[ia] / 2 == jj);
+                const int jj = li[ib];
+                const bool conflict = bit_of(sm.split, 2 * jj) || bit_of(sm.split, 2 * jj + 1) ||
+                                      (ia < nfull && gi[ia] / 2 == jj);
                 if (!conflict)
                     break;
                 ++ib;
             }
-            if (ia >= nfull || ib >= npair || !(sm.gk[ia] > sm.lk[ib]))
+            if (ia >= nfull || ib >= npair || !(gk[ia] > lk[ib]))
                 break;
-            sm.split[sm.gi[ia]] = 1;
-            sm.merged[sm.li[ib]] = 1;
+            const int sb = gi[ia], mj = li[ib];
+            sm.split[sb >> 5] |= 1u << (sb & 31);
+            sm.merged[mj >> 5] |= 1u << (mj & 31);
             ++ia;
             ++ib;
         }
     }
     __syncthreads();
-    // chunks contributed by each block (a merged pair counts on its first block)
-    for (int b = tid; b < n; b += kAdaptThreads) {
-        const bool in_merged = b / 2 < npair && sm.merged[b / 2];
-        sm.cnt[b] = in_merged ? (b % 2 == 0 ? 1 : 0) : (sm.split[b] ? 2 : 1);
-    }
-    __syncthreads();
-    // exclusive prefix sum of cnt over n <= kAdaptBlocksMax entries: each
-    // thread sums a contiguous run of PER entries
-    constexpr int PER = kAdaptBlocksMax / kAdaptThreads;
-    int run[PER];
+    // chunks contributed by each block (a merged pair counts on its first
+    // block); thread t takes the blocks [t R, (t + 1) R): their count, an
+    // exclusive scan over the threads, then their chunk ends
+    auto chunks_of = [&](int b) {
+        const bool in_merged = b / 2 < npair && bit_of(sm.merged, b / 2);
+        return in_merged ? (b % 2 == 0 ? 1 : 0) : (bit_of(sm.split, b) ? 2 : 1);
+    };
+    const int R = (n + kAdaptThreads - 1) / kAdaptThreads;
+    const int b0 = tid * R;
+    const int b1 = (b0 + R < n) ? b0 + R : n;
     int tot = 0;
-#pragma unroll
-    for (int u = 0; u < PER; ++u) {
-        const int b = tid * PER + u;
-        run[u] = b < n ? sm.cnt[b] : 0;
-        tot += run[u];
-    }
+    for (int b = b0; b < b1; ++b)
+        tot += chunks_of(b);
     int x = tot;
 #pragma unroll
     for (int d = 1; d < kWave; d <<= 1) {
@@ -415,22 +418,21 @@ __global__ __launch_bounds__(kAdaptThreads) void chunk_greedy_kernel(ChunkAdaptP
     int pos = before + x - tot;
     int32_t *ce = p.cend + (int64_t)bi * n;
     const int64_t blk = p.block, h = p.block / 2;
-#pragma unroll
-    for (int u = 0; u < PER; ++u) {
-        const int b = tid * PER + u;
-        if (b < n && run[u] > 0) {
-            const int64_t a = (int64_t)b * blk;
-            const bool in_merged = b / 2 < npair && sm.merged[b / 2];
-            if (in_merged) {
-                ce[pos] = (int32_t)(a + 2 * blk);
-            } else if (sm.split[b]) {
-                ce[pos] = (int32_t)(a + h);
-                ce[pos + 1] = (int32_t)(a + blk);
-            } else {
-                ce[pos] = (int32_t)(a + blk < p.L ? a + blk : p.L);
-            }
-            pos += run[u];
+    for (int b = b0; b < b1; ++b) {
+        const int cnt = chunks_of(b);
+        if (cnt == 0)
+            continue;
+        const int64_t a = (int64_t)b * blk;
+        const bool in_merged = b / 2 < npair && bit_of(sm.merged, b / 2);
+        if (in_merged) {
+            ce[pos] = (int32_t)(a + 2 * blk);
+        } else if (bit_of(sm.split, b)) {
+            ce[pos] = (int32_t)(a + h);
+            ce[pos + 1] = (int32_t)(a + blk);
+        } else {
+            ce[pos] = (int32_t)(a + blk < p.L ? a + blk : p.L);
         }
+        pos += cnt;
     }
 }
 

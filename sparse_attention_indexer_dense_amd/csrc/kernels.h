@@ -163,15 +163,23 @@ struct ChunkExpandParams {
     int32_t *cand_n;        // [B][G]
 };
 
-// Adaptive chunking: at most this many blocks per request (its sort runs in LDS).
-constexpr int kAdaptBlocksMax = 4096;
+// Adaptive chunking: at most this many blocks per request (its per-block
+// flags are LDS bitmaps); up to kAdaptBlocksLds blocks the gains and losses
+// are sorted in LDS, beyond that in the workspace.
+constexpr int kAdaptBlocksMax = 1 << 18;
+constexpr int kAdaptBlocksLds = 4096;
 
 struct ChunkAdaptParams {
     const uint16_t *K;      // [B][L][D]
     int64_t L, block;
     int64_t n, nfull, npair;  // blocks, full blocks, aligned pairs of full blocks
+    int64_t g2, p2;         // nfull and npair rounded up to powers of two
     double *gain;           // [B][nfull] split gains
     double *loss;           // [B][npair] merge losses
+    double *gk;             // n > kAdaptBlocksLds: sort space [B][g2] gains, [B][g2] their blocks,
+    int32_t *gi;            //   [B][p2] losses, [B][p2] their pairs (unused otherwise)
+    double *lk;
+    int32_t *li;
     int32_t *cend;          // [B][n]
 };
 

@@ -196,8 +196,8 @@ def test_chunk_entry_points_reject_bad_arguments():
     big = 1 << 40
     # adaptive: odd block, too many blocks, unsupported d
     assert dsa.indexer_chunks_adaptive(fake(), 1, 1000, 128, 7, fake(), fake(), big, None) == EINVAL
-    rc = dsa.indexer_chunks_adaptive(fake(), 1, 4097 * 64, 128, 64, fake(), fake(), big, None)
-    assert rc == EUNSUPPORTED and "4096" in dsa.indexer_last_error()
+    rc = dsa.indexer_chunks_adaptive(fake(), 1, (262144 + 1) * 64, 128, 64, fake(), fake(), big, None)
+    assert rc == EUNSUPPORTED and "262144" in dsa.indexer_last_error()
     assert dsa.indexer_chunks_adaptive(fake(), 1, 1000, 64, 8, fake(), fake(), big, None) == EUNSUPPORTED
     assert dsa.indexer_chunks_adaptive(fake(), 1, 1000, 128, 8, fake(), fake(), 8, None) == EWORKSPACE
     # summaries

@@ -72,7 +72,7 @@ def test_chunk_means_refresh_leaves_earlier_rows():
 
 
 @pytest.mark.parametrize("d", [32, 128])
-@pytest.mark.parametrize("L,block", [(4096, 64), (4000, 64), (1024, 8), (130, 16)])
+@pytest.mark.parametrize("L,block", [(4096, 64), (4000, 64), (1024, 8), (130, 16), (300000, 64), (65537, 8)])
 def test_adaptive_chunks_bitexact(d, L, block):
     B = 2
     K = uneven_keys(B, L, d, block, seed=3 * L + d)
