@@ -504,33 +504,36 @@ def guard_sweep(dsa, synth, torch, steps=3, g=4, c=4096, k=2048):
     return rows
 
 
-def kernel_ms(torch, fn, pattern):
-    """Mean device time (ms) of the kernels whose name contains `pattern`, and
-    their count, over one call of fn, from torch's profiler (which traces every
-    HIP kernel launched in the process, the library's included)."""
+def kernel_ms(torch, fn, patterns):
+    """Mean device time (ms) of the kernels whose name contains one of
+    `patterns`, their count and the first such name, over one call of fn, from
+    torch's profiler (which traces every HIP kernel launched in the process,
+    the library's included)."""
     from torch.profiler import ProfilerActivity, profile
     torch.cuda.synchronize()
     with profile(activities=[ProfilerActivity.CUDA]) as prof:
         fn()
         torch.cuda.synchronize()
-    times = []
+    times, name = [], None
     for e in prof.events():
-        if pattern not in e.name:
+        if not any(pt in e.name for pt in patterns):
             continue
         us = getattr(e, "device_time", None)
         if us is None:
             us = getattr(e, "cuda_time", None)
         if us:
             times.append(float(us) / 1e3)
+            name = name or e.name
     if not times:
-        return None, 0
-    return sum(times) / len(times), len(times)
+        return None, 0, None
+    return sum(times) / len(times), len(times), name
 
 
 def refine_gather(dsa, torch, Q, W, K, g, c, k, cand):
-    """The prefill Refine re-score (scan_select_kernel in its Refine mode: each
-    group's candidate keys gathered by DMA once for its members) against the
-    HBM roofline: algorithmic bytes = every group's causal candidate keys
+    """The prefill Refine re-score (refine_lds_kernel for groups of up to four
+    members and up to 4096 candidates, else scan_select_kernel in its Refine
+    mode: each group's candidate keys gathered once for its members) against
+    the HBM roofline: algorithmic bytes = every group's causal candidate keys
     (2 d bytes each) plus its list, the members' queries and weights, and their
     outputs; time = that kernel's own device time, from torch's profiler."""
     B, q_len, H, d = Q.shape
@@ -541,12 +544,13 @@ def refine_gather(dsa, torch, Q, W, K, g, c, k, cand):
     gather = ncand * 2 * d
     total = gather + ncand * 4 + B * q_len * (H * d * 2 + H * 4 + k * 8)
     try:
-        ms, n = kernel_ms(torch, lambda: dsa.pivot_refine(Q, W, K, g, c, k, scores=False), ", 2>(dsaidx::ScanParams)")
+        ms, n, name = kernel_ms(torch, lambda: dsa.pivot_refine(Q, W, K, g, c, k, scores=False),
+                                ("refine_lds_kernel", ", 2>(dsaidx::ScanParams)"))
     except Exception as e:  # noqa: BLE001 - report, do not fail the bench line
         return {"error": f"profiler: {e!r}"}
     if ms is None:
         return {"error": "no Refine scan kernel in the profile"}
-    return {"kernel": "scan_select_kernel<64,128,4,refine>", "launches": n, "kernel_ms": ms,
+    return {"kernel": name, "launches": n, "kernel_ms": ms,
             "candidate_keys": ncand, "gather_bytes": gather, "algorithmic_bytes": total,
             "gather_GBps": gather / (ms * 1e-3) / 1e9, "achieved_GBps": total / (ms * 1e-3) / 1e9,
             "hbm_frac": total / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS}

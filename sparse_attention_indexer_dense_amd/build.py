@@ -16,7 +16,7 @@ CSRC = os.path.join(PKG, "csrc")
 OUT = os.path.join(PKG, "libdsaidx.so")
 BUILD = os.path.join(PKG, "_build")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
-SOURCES = ["scan.hip", "split.hip", "batch.hip", "chunks.hip", "sort.hip", "abi.cpp"]
+SOURCES = ["scan.hip", "split.hip", "refine.hip", "batch.hip", "chunks.hip", "sort.hip", "abi.cpp"]
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
     # packed fp32 VALU forms are kept out of the generated code

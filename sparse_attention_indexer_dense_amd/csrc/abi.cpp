@@ -248,6 +248,7 @@ struct Plan {
     int mode;
     bool dense_pass, pivot_pass;      // PIVOT: some groups guarded / unguarded
     bool split_dense, split_scan, split_refine;
+    bool refine_lds;                  // Refine re-score with the members' scores in LDS (refine.hip)
     int nw_scan, nw_refine;
     int cap_dense, cap_scan, cap_refine;
     int sel, sel2;
@@ -331,10 +332,13 @@ int make_plan(int mode, const Batch &b, int H, int D, int64_t c, int64_t k, bool
                                             : scan_bytes(H, D, pl.nw_scan, pl.cap_scan));
         if (mode == DSAIDX_REFINE) {
             pl.split_refine = b.max_refine_rows <= kSplitRowsMax;
+            pl.refine_lds = !pl.split_refine && g <= 4 && c <= kRefineLdsCandMax;
             pl.nw_refine = g <= 4 ? 4 : 8;
             pl.cap_refine = (int)ceil_div(c + 128, 64) * 64;
-            work = std::max(work, pl.split_refine ? (size_t)b.B * b.max_refine_rows * score_row(c) * sizeof(float)
-                                                  : scan_bytes(H, D, pl.nw_refine, pl.cap_refine));
+            if (pl.split_refine)
+                work = std::max(work, (size_t)b.B * b.max_refine_rows * score_row(c) * sizeof(float));
+            else if (!pl.refine_lds)
+                work = std::max(work, scan_bytes(H, D, pl.nw_refine, pl.cap_refine));
         }
     }
     pl.off_work = off;
@@ -642,6 +646,30 @@ int run_pivot(int mode, const Batch &b, const void *Qv, const float *W, const vo
     if (pl.split_refine) {
         return run_split(kRefine, ps, Q, W, K, cand, b.max_refine_rows, score_row(c), H, D, (int)k, 0, out_idx,
                          out_score, 0, nullptr, nullptr, reinterpret_cast<float *>(wsb + pl.off_work), stream);
+    }
+    if (pl.refine_lds) {
+        RefineLdsParams rp{};
+        rp.Q = Q;
+        rp.W = W;
+        rp.K = K;
+        rp.cand = cand;
+        rp.req = ps.req;
+        rp.B = b.B;
+        rp.L = b.L;
+        rp.q_len = b.q_len;
+        rp.g = b.g;
+        rp.c = c;
+        rp.m0 = b.m0;
+        rp.k = (int)k;
+        rp.out_idx = out_idx;
+        rp.out_score = out_score;
+        rp.nwork = (int64_t)b.B * b.max_pivot_groups;
+        // one workgroup per CU (the kernel's LDS), each looping over groups
+        const int grid = (int)std::min<int64_t>(rp.nwork, std::max(1, num_cus()));
+        e = launch_refine_lds(H, D, rp, grid, stream);
+        if (e != hipSuccess)
+            return hip_fail(e, "refine launch");
+        return DSAIDX_OK;
     }
     ScanParams p = scan_base(ps, kRefine, Q, W, K);
     p.cand = cand;

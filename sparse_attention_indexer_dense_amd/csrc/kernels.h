@@ -97,6 +97,24 @@ struct ScanParams {
     const int32_t *cand_n;   // kRefine: keys in each group's list (nullptr: min(c, t_last + 1))
 };
 
+// PIVOT-Refine with the members' scores in LDS (refine.hip): groups of at
+// most four members and at most kRefineLdsCandMax candidates.
+constexpr int kRefineLdsCandMax = 4096;
+
+struct RefineLdsParams {
+    const uint16_t *Q;     // queries [B][q_len][H][D]
+    const float *W;
+    const uint16_t *K;     // keys [B][L][D]
+    const int32_t *cand;   // candidate lists [B][G][c] (or packed per request)
+    const ReqDesc *req;    // requests of a variable-length batch (nullptr: uniform)
+    int B;
+    int64_t L, q_len, g, c, m0;
+    int k;
+    int32_t *out_idx;      // [rows][k]
+    float *out_score;      // [rows][k] or nullptr
+    int64_t nwork;         // groups of the launch: B x groups of the largest request
+};
+
 struct PoolParams {
     const uint16_t *Q;
     const float *W;
@@ -202,6 +220,8 @@ hipError_t launch_fill_guarded(const ReqDesc *req, int B, int64_t L, int64_t q_l
 hipError_t launch_scan_select(int H, int D, int NW, int mode, const ScanParams &prm, int grid,
                               hipStream_t stream);
 hipError_t launch_pool(int H, int D, const PoolParams &prm, hipStream_t stream);
+// one workgroup per (request, group) slot: nblocks = B * (groups of the largest request)
+hipError_t launch_refine_lds(int H, int D, const RefineLdsParams &prm, int grid, hipStream_t stream);
 // mr: score rows per wave (2: Refine member rows paired over their group's
 // candidate list; needs an even g)
 hipError_t launch_split_score(int H, int D, const SplitScoreParams &prm, int mr, dim3 grid, hipStream_t stream);
