@@ -14,9 +14,9 @@
 // from. The score tile and its epilogue are those of scan.hip's Refine mode
 // (same fragment order, same additions), so the scores are the same bits.
 // Every score goes to the member's row in LDS (4096 floats), and after the
-// last stage one wave per member selects the exact top-k of its causal
+// last stage the member's two waves select the exact top-k of its causal
 // candidates from that row (a radix cut over the row's key range, ties to
-// the lower index) and writes it in ascending index order. No candidate
+// the lower index) and write it in ascending index order. No candidate
 // buffer goes to global memory: the kernel writes the outputs only.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -33,57 +33,80 @@ constexpr int kRefStage = 128;                 // keys per stage: two 32-key til
 constexpr int kRefRing = 2;                    // stages gathered ahead (registers)
 static_assert(kRefineLdsCandMax % kRefStage == 0, "whole stages");
 
-constexpr int kRefSelQ = kRefineLdsCandMax / kWave;  // row entries per lane
+constexpr int kRefSelQ = kRefineLdsCandMax / kWave / kRefHalves;  // row entries per lane per wave
+constexpr int kRefXch = 8;  // words of LDS per member for its two waves' exchanges
 
 // Exact top-`sel` of the n scores r[0..n) (LDS) of one row, ties to the lower
-// index, by one wave, written to oidx/osc in ascending index order (list[x] is
-// the key index of entry x) and padded with -1 / -inf up to sel.
+// index, by the row's two waves (hv = 0, 1), written to oidx/osc in ascending
+// index order (list[x] is the key index of entry x) and padded with -1 / -inf
+// up to sel. Every wave of the workgroup calls it (its barriers are the
+// workgroup's); a wave of an absent member passes active = false.
 //
-// Lane l holds entries l, l + 64, ... as order-preserving keys in registers.
-// The cut is a radix select over the keys' own range [kmin, kmax] rather than
-// over fixed bit fields: level 1 splits the range into at most 2048 bins of
-// 2^s keys, each later level splits the boundary bin of the one before into
-// 2048 (the last into single keys), and a level ends the search as soon as
-// its boundary bin is wholly in. Scores of one row share few exponents, so
-// fixed top-bit bins would pile most keys into a handful of bins, and the
-// LDS atomics of a bin serialise. Counting reads registers only; the emit
-// pass takes 16 entries per lane at a time: their list indices, then every
-// selected entry's output slot (ballots, no branches), then the writes.
-__device__ __forceinline__ void member_select(const float *r, const int32_t *list, int n, int sel,
-                                              uint32_t *h, int32_t *oidx, float *osc)
+// Wave hv holds entries x = (hv * 32 + q) * 64 + lane, q < 32, as
+// order-preserving keys in registers. The cut is a radix select over the
+// row's own key range [kmin, kmax] rather than over fixed bit fields: level 1
+// splits the range into at most 2048 bins of 2^s keys, each later level
+// splits the boundary bin of the one before into 2048 (the last into single
+// keys), and a level ends the search as soon as its boundary bin is wholly
+// in. Scores of one row share few exponents, so fixed top-bit bins would pile
+// most keys into a handful of bins, and the LDS atomics of a bin serialise.
+// Both waves count into the member's histogram h and both read it back; xch
+// carries the range and wave 0's counts. The emit pass takes 16 entries per
+// lane at a time: their list indices, then every selected entry's output slot
+// (ballots, no branches), then the writes; wave 1 starts after wave 0's share.
+__device__ __forceinline__ void member_select(const float *r, const int32_t *list, int n, int sel, uint32_t *h,
+                                              uint32_t *xch, int hv, bool active, int32_t *oidx, float *osc)
 {
     const int lane = lane_id();
-    const int nq = (n + kWave - 1) / kWave;
+    const int e0 = hv * kRefSelQ;  // this wave's first entry block
     uint32_t key[kRefSelQ];
 #pragma unroll
     for (int q = 0; q < kRefSelQ; ++q)
-        key[q] = score_key(r[q * kWave + lane]);  // (past n: unused)
-    auto valid = [&](int q) { return q * kWave + lane < n; };
+        key[q] = score_key(r[(e0 + q) * kWave + lane]);  // (past n: unused)
+    auto valid = [&](int q) { return active && (e0 + q) * kWave + lane < n; };
+
+    // the key range of the row
+    uint32_t lo = 0xFFFFFFFFu, hi = 0u;
+#pragma unroll
+    for (int q = 0; q < kRefSelQ; ++q)
+        if (valid(q)) {
+            lo = min(lo, key[q]);
+            hi = max(hi, key[q]);
+        }
+    lo = wave_min(lo);
+    hi = wave_max(hi);
+    if (active && lane == 0) {
+        xch[2 * hv] = lo;
+        xch[2 * hv + 1] = hi;
+    }
+    __syncthreads();
+    lo = min(xch[0], xch[2]);
+    hi = max(xch[1], xch[3]);
 
     Cut c{-1, 0u, 0};  // every key when n <= sel
-    if (n > sel) {
-        uint32_t lo = 0xFFFFFFFFu, hi = 0u;
+    bool done = !(active && n > sel);
+    uint64_t width = (uint64_t)(hi - lo) + 1;  // keys in [lo, lo + width)
+    int sh = 0;
+    while ((width - 1) >> sh >= (uint64_t)kBins1)
+        ++sh;
+    int need = sel;
+    // at most three levels: sh <= 21 at level 1, <= 10 at level 2, 0 at 3
+    for (int level = 0; level < 3; ++level) {
+        if (!done)
 #pragma unroll
-        for (int q = 0; q < kRefSelQ; ++q)
-            if (valid(q)) {
-                lo = min(lo, key[q]);
-                hi = max(hi, key[q]);
-            }
-        lo = uniform((int)wave_min(lo));
-        hi = uniform((int)wave_max(hi));
-        uint64_t width = (uint64_t)(hi - lo) + 1;  // keys in [lo, lo + width)
-        int sh = 0;
-        while ((width - 1) >> sh >= (uint64_t)kBins1)
-            ++sh;
-        int need = sel;
-        for (;;) {
-            clear_hist<kBins1>(h);
+            for (int b = 0; b < kBins1 / kRefHalves / kWave; ++b)
+                h[(hv * (kBins1 / kRefHalves)) + b * kWave + lane] = 0u;
+        __syncthreads();
+        if (!done) {
 #pragma unroll
             for (int q = 0; q < kRefSelQ; ++q) {
                 const uint32_t d = key[q] - lo;  // wraps below lo: out of range
                 if (valid(q) && key[q] >= lo && (uint64_t)d < width)
                     atomicAdd(&h[d >> sh], 1u);
             }
+        }
+        __syncthreads();
+        if (!done) {
             int b, above;
             find_bin<kBins1>(h, need, b, above);
             need -= above;
@@ -92,35 +115,55 @@ __device__ __forceinline__ void member_select(const float *r, const int32_t *lis
                 c.kgt = (int64_t)base;
                 c.keq = base;
                 c.req = need;
-                break;
-            }
-            if (need == uniform((int)h[b])) {
+                done = true;
+            } else if (need == uniform((int)h[b])) {
                 c.kgt = (int64_t)base - 1;
-                break;
+                done = true;
+            } else {
+                lo = base;
+                width = (uint64_t)1 << sh;
+                sh = sh > 11 ? sh - 11 : 0;
             }
-            lo = base;
-            width = (uint64_t)1 << sh;
-            sh = sh > 11 ? sh - 11 : 0;
         }
+        __syncthreads();
     }
 
-    // blocks of 16 entries per lane: their list indices, then the output
-    // slot of each (-1: not selected), then the writes. Without a partial
-    // take of equal keys (req = 0) an entry is in iff its key is above kgt,
-    // one 32-bit compare (kgt = -1: every entry).
-    constexpr int EQ = 16;
+    // Without a partial take of equal keys (req = 0) an entry is in iff its
+    // key is above kgt, one 32-bit compare (kgt = -1: every entry).
     const bool partial = c.req > 0;
     const bool every = c.kgt < 0;
     const uint32_t thr = (uint32_t)c.kgt;
+    // wave 0's share: its selected entries and its entries equal to keq
+    if (active && hv == 0) {
+        int ngt = 0, neq = 0;
+#pragma unroll
+        for (int q = 0; q < kRefSelQ; ++q) {
+            ngt += __popcll(ballot(valid(q) && (every || key[q] > thr)));
+            if (partial)
+                neq += __popcll(ballot(valid(q) && key[q] == c.keq));
+        }
+        if (lane == 0) {
+            xch[4] = (uint32_t)ngt;
+            xch[5] = (uint32_t)neq;
+        }
+    }
+    __syncthreads();
+    if (!active)
+        return;
     int emitted = 0, eqseen = 0;
+    if (hv == 1) {
+        eqseen = (int)xch[5];
+        emitted = (int)xch[4] + min(eqseen, c.req);
+    }
+    constexpr int EQ = 16;
 #pragma unroll
     for (int q0 = 0; q0 < kRefSelQ; q0 += EQ) {
-        if (q0 < nq) {
+        if ((e0 + q0) * kWave < n) {
             int32_t idx[EQ];
             int slot[EQ];
 #pragma unroll
             for (int e = 0; e < EQ; ++e)
-                idx[e] = list[(q0 + e) * kWave + lane];  // (past n: an unused entry)
+                idx[e] = list[(e0 + q0 + e) * kWave + lane];  // (past n: an unused entry)
             if (!partial) {
 #pragma unroll
                 for (int e = 0; e < EQ; ++e) {
@@ -154,11 +197,12 @@ __device__ __forceinline__ void member_select(const float *r, const int32_t *lis
                 }
         }
     }
-    for (int x = emitted + lane; x < sel; x += kWave) {
-        oidx[x] = -1;
-        if (osc)
-            osc[x] = -__builtin_inff();
-    }
+    if (hv == 1)
+        for (int x = emitted + lane; x < sel; x += kWave) {
+            oidx[x] = -1;
+            if (osc)
+                osc[x] = -__builtin_inff();
+        }
 }
 
 // Group j of the launch (request j % B, its (j / B)-th longest group).
@@ -174,8 +218,9 @@ __device__ __forceinline__ void refine_group(const RefineLdsParams &p, int64_t j
     constexpr int RPL = 1024 / ROWB;              // key rows per 1 KiB gather
 
     // two stage buffers; after the last stage the same bytes hold one level
-    // histogram per member (so at least kRefMembers * kBins1 words)
-    constexpr int KBUF = (2 * STAGE_BYTES > kRefMembers * kBins1 * 4) ? 2 * STAGE_BYTES : kRefMembers * kBins1 * 4;
+    // histogram and the exchange words per member
+    constexpr int SELB = kRefMembers * (kBins1 + kRefXch) * 4;
+    constexpr int KBUF = (2 * STAGE_BYTES > SELB) ? 2 * STAGE_BYTES : SELB;
     __shared__ __align__(1024) unsigned char kbuf[KBUF];
     __shared__ __align__(16) int32_t lst[kRefineLdsCandMax];
     __shared__ __align__(16) float rows[kRefMembers][kRefineLdsCandMax];
@@ -373,12 +418,14 @@ __device__ __forceinline__ void refine_group(const RefineLdsParams &p, int64_t j
     auto compute = [&](const unsigned char *kb, int t) {
         if (!live)
             return;
+        wave_priority(1);
         mfma_tile(kb, 2 * hv, accA);
         if (t > 0) {
             const float s1 = epilogue(accB);
             interleave();
             store_pair(t - 1, s0, s1);
         }
+        wave_priority(0);
         mfma_tile(kb, 2 * hv + 1, accB);
         s0 = epilogue(accA);
         interleave();
@@ -408,19 +455,19 @@ __device__ __forceinline__ void refine_group(const RefineLdsParams &p, int64_t j
         store_pair(nst2 - 1, s0, epilogue(accB));
     __syncthreads();
 
-    // selection: one wave per member over its causal candidates, a prefix
-    // of the ascending list (at most the last nmem - 1 entries lie after the
-    // member's position); the stage buffers become the waves' histograms
-    if (!live || hv != 0)
-        return;
+    // selection: both waves of each member over its causal candidates, a
+    // prefix of the ascending list (at most the last nmem - 1 entries lie
+    // after the member's position); the stage buffers become the members'
+    // histograms and exchange words
     const int pos = (int)(off + r0 + mem);
-    int ncaus = ncand;
+    int ncaus = live ? ncand : 0;
     while (ncaus > 0 && lst[ncaus - 1] > pos)
         --ncaus;
     uint32_t *h = reinterpret_cast<uint32_t *>(kbuf) + mem * kBins1;
+    uint32_t *xch = reinterpret_cast<uint32_t *>(kbuf) + kRefMembers * kBins1 + mem * kRefXch;
     int32_t *oidx = p.out_idx + row * p.k;
     float *osc = p.out_score ? p.out_score + row * p.k : nullptr;
-    member_select(myrow, lst, ncaus, p.k, h, oidx, osc);
+    member_select(myrow, lst, ncaus, p.k, h, xch, hv, live, oidx, osc);
 }
 
 // Persistent workgroups: each takes groups j = blockIdx.x, + gridDim.x, ...;
