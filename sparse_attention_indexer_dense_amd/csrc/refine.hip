@@ -477,7 +477,11 @@ template <int H, int D>
 __global__ __launch_bounds__(kRefWaves * kWave) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void refine_lds_kernel(RefineLdsParams p)
 {
-    for (int64_t j = blockIdx.x; j < p.nwork; j += gridDim.x) {
+    // workgroups are dealt to the 8 XCDs round-robin; let the ones of one XCD
+    // take consecutive groups (neighbouring groups share most candidates)
+    const int G8 = gridDim.x / 8;
+    const int64_t b = (gridDim.x % 8 == 0) ? (int64_t)(blockIdx.x % 8) * G8 + blockIdx.x / 8 : blockIdx.x;
+    for (int64_t j = b; j < p.nwork; j += gridDim.x) {
         refine_group<H, D>(p, j);
         __syncthreads();
     }
