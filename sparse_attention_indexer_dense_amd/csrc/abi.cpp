@@ -927,6 +927,33 @@ int run_chunk_refine(const Batch &b, const void *Qv, const float *W, const void 
     if (pl.split_refine)
         return run_split(kRefine, pr, Q, W, K, cand, b.q_len, score_row(pl.cw), H, D, (int)k, 0, out_idx, out_score, 0,
                          nullptr, nullptr, work, stream);
+    if (b.g >= 2 && b.g <= 4 && pl.cw <= kRefineLdsCandMax) {
+        // groups of two to four rows sharing a list: the members' scores and
+        // selections on chip (a single row per list stays on the one-wave
+        // scan workgroups below)
+        RefineLdsParams rp{};
+        rp.Q = Q;
+        rp.W = W;
+        rp.K = K;
+        rp.cand = cand;
+        rp.cand_n = cn;
+        rp.req = nullptr;
+        rp.B = b.B;
+        rp.L = b.L;
+        rp.q_len = b.q_len;
+        rp.g = b.g;
+        rp.c = pl.cw;
+        rp.m0 = 0;
+        rp.k = (int)k;
+        rp.out_idx = out_idx;
+        rp.out_score = out_score;
+        rp.nwork = (int64_t)b.B * pl.G;
+        const int grid = (int)std::min<int64_t>(rp.nwork, std::max(1, num_cus()));
+        e = launch_refine_lds(H, D, rp, grid, stream);
+        if (e != hipSuccess)
+            return hip_fail(e, "refine launch");
+        return DSAIDX_OK;
+    }
     ScanParams p = scan_base(pr, kRefine, Q, W, K);
     p.cand = cand;
     p.member_chunks = ceil_div(b.g, pl.nw_refine);

@@ -99,7 +99,7 @@ struct ScanParams {
 
 // PIVOT-Refine with the members' scores in LDS (refine.hip): groups of at
 // most four members and at most kRefineLdsCandMax candidates.
-constexpr int kRefineLdsCandMax = 4096;
+constexpr int kRefineLdsCandMax = 4608;
 
 struct RefineLdsParams {
     const uint16_t *Q;     // queries [B][q_len][H][D]
@@ -113,6 +113,7 @@ struct RefineLdsParams {
     int32_t *out_idx;      // [rows][k]
     float *out_score;      // [rows][k] or nullptr
     int64_t nwork;         // groups of the launch: B x groups of the largest request
+    const int32_t *cand_n; // keys in each group's list (nullptr: min(c, t_last + 1))
 };
 
 struct PoolParams {

@@ -1,7 +1,7 @@
 // refine.hip - PIVOT-Refine (PIVOT paper, abstract and Method: every member of
 // a group re-scores the group's candidates that are causal for it, with its
 // own query and weights, and keeps its own top-k) for groups of at most four
-// members and at most 4096 candidates, with the members' scores kept on chip.
+// members and at most 4608 candidates, with the members' scores kept on chip.
 //
 // One workgroup per CU (the LDS below), looping over groups, eight waves:
 // wave (member m, half h) scores tiles 2h and 2h+1 of every 128-key stage for
@@ -13,10 +13,10 @@
 // rows, as in scan.hip) that all eight waves read their MFMA B fragments
 // from. The score tile and its epilogue are those of scan.hip's Refine mode
 // (same fragment order, same additions), so the scores are the same bits.
-// Every score goes to the member's row in LDS (4096 floats), and after the
-// last stage the member's two waves select the exact top-k of its causal
-// candidates from that row (a radix cut over the row's key range, ties to
-// the lower index) and write it in ascending index order. No candidate
+// Every score goes to the member's row in LDS (4096 or 4608 floats), and
+// after the last stage the member's two waves select the exact top-k of its
+// causal candidates from that row (a radix cut over the row's key range,
+// ties to the lower index) and write it in ascending index order. No candidate
 // buffer goes to global memory: the kernel writes the outputs only.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -31,10 +31,14 @@ constexpr int kRefHalves = 2;                  // waves per member
 constexpr int kRefWaves = kRefMembers * kRefHalves;
 constexpr int kRefStage = 128;                 // keys per stage: two 32-key tiles per wave
 constexpr int kRefRing = 2;                    // stages gathered ahead (registers)
-static_assert(kRefineLdsCandMax % kRefStage == 0, "whole stages");
-
-constexpr int kRefSelQ = kRefineLdsCandMax / kWave / kRefHalves;  // row entries per lane per wave
 constexpr int kRefXch = 8;  // words of LDS per member for its two waves' exchanges
+
+// List capacities the kernel is built for (candidates per group): one for
+// the common c <= 4096, one for the key-chunk path's lists of (nsel + 1)
+// 64-key chunks; the LDS is 64 KiB + 20 bytes per entry of capacity.
+constexpr int kRefCapSmall = 4096;
+static_assert(kRefineLdsCandMax == 4608 && kRefineLdsCandMax % kRefStage == 0 &&
+                  kRefCapSmall % kRefStage == 0, "whole stages");
 
 // Exact top-`sel` of the n scores r[0..n) (LDS) of one row, ties to the lower
 // index, by the row's two waves (hv = 0, 1), written to oidx/osc in ascending
@@ -42,7 +46,7 @@ constexpr int kRefXch = 8;  // words of LDS per member for its two waves' exchan
 // up to sel. Every wave of the workgroup calls it (its barriers are the
 // workgroup's); a wave of an absent member passes active = false.
 //
-// Wave hv holds entries x = (hv * 32 + q) * 64 + lane, q < 32, as
+// Wave hv holds entries x = (hv * NQ + q) * 64 + lane, q < NQ, as
 // order-preserving keys in registers. The cut is a radix select over the
 // row's own key range [kmin, kmax] rather than over fixed bit fields: level 1
 // splits the range into at most 2048 bins of 2^s keys, each later level
@@ -54,21 +58,22 @@ constexpr int kRefXch = 8;  // words of LDS per member for its two waves' exchan
 // carries the range and wave 0's counts. The emit pass takes 16 entries per
 // lane at a time: their list indices, then every selected entry's output slot
 // (ballots, no branches), then the writes; wave 1 starts after wave 0's share.
+template <int NQ>  // row entries per lane per wave
 __device__ __forceinline__ void member_select(const float *r, const int32_t *list, int n, int sel, uint32_t *h,
                                               uint32_t *xch, int hv, bool active, int32_t *oidx, float *osc)
 {
     const int lane = lane_id();
-    const int e0 = hv * kRefSelQ;  // this wave's first entry block
-    uint32_t key[kRefSelQ];
+    const int e0 = hv * NQ;  // this wave's first entry block
+    uint32_t key[NQ];
 #pragma unroll
-    for (int q = 0; q < kRefSelQ; ++q)
+    for (int q = 0; q < NQ; ++q)
         key[q] = score_key(r[(e0 + q) * kWave + lane]);  // (past n: unused)
     auto valid = [&](int q) { return active && (e0 + q) * kWave + lane < n; };
 
     // the key range of the row
     uint32_t lo = 0xFFFFFFFFu, hi = 0u;
 #pragma unroll
-    for (int q = 0; q < kRefSelQ; ++q)
+    for (int q = 0; q < NQ; ++q)
         if (valid(q)) {
             lo = min(lo, key[q]);
             hi = max(hi, key[q]);
@@ -99,7 +104,7 @@ __device__ __forceinline__ void member_select(const float *r, const int32_t *lis
         __syncthreads();
         if (!done) {
 #pragma unroll
-            for (int q = 0; q < kRefSelQ; ++q) {
+            for (int q = 0; q < NQ; ++q) {
                 const uint32_t d = key[q] - lo;  // wraps below lo: out of range
                 if (valid(q) && key[q] >= lo && (uint64_t)d < width)
                     atomicAdd(&h[d >> sh], 1u);
@@ -137,7 +142,7 @@ __device__ __forceinline__ void member_select(const float *r, const int32_t *lis
     if (active && hv == 0) {
         int ngt = 0, neq = 0;
 #pragma unroll
-        for (int q = 0; q < kRefSelQ; ++q) {
+        for (int q = 0; q < NQ; ++q) {
             ngt += __popcll(ballot(valid(q) && (every || key[q] > thr)));
             if (partial)
                 neq += __popcll(ballot(valid(q) && key[q] == c.keq));
@@ -157,17 +162,20 @@ __device__ __forceinline__ void member_select(const float *r, const int32_t *lis
     }
     constexpr int EQ = 16;
 #pragma unroll
-    for (int q0 = 0; q0 < kRefSelQ; q0 += EQ) {
+    for (int q0 = 0; q0 < NQ; q0 += EQ) {
         if ((e0 + q0) * kWave < n) {
             int32_t idx[EQ];
             int slot[EQ];
 #pragma unroll
-            for (int e = 0; e < EQ; ++e)
-                idx[e] = list[(e0 + q0 + e) * kWave + lane];  // (past n: an unused entry)
+            for (int e = 0; e < EQ; ++e)  // (past n: an unused entry)
+                idx[e] = (q0 + e < NQ) ? list[(e0 + q0 + e) * kWave + lane] : -1;
             if (!partial) {
 #pragma unroll
                 for (int e = 0; e < EQ; ++e) {
                     const int q = q0 + e;
+                    slot[e] = -1;
+                    if (q >= NQ)
+                        continue;
                     const bool in = valid(q) && (every || key[q] > thr);
                     const uint64_t min_ = ballot(in);
                     slot[e] = in ? emitted + prefix_count(min_) : -1;
@@ -177,6 +185,9 @@ __device__ __forceinline__ void member_select(const float *r, const int32_t *lis
 #pragma unroll
                 for (int e = 0; e < EQ; ++e) {
                     const int q = q0 + e;
+                    slot[e] = -1;
+                    if (q >= NQ)
+                        continue;
                     const bool v = valid(q);
                     const bool eq = v && key[q] == c.keq;
                     const uint64_t meq = ballot(eq);
@@ -190,10 +201,10 @@ __device__ __forceinline__ void member_select(const float *r, const int32_t *lis
             }
 #pragma unroll
             for (int e = 0; e < EQ; ++e)
-                if (slot[e] >= 0 && slot[e] < sel) {
+                if (q0 + e < NQ && slot[e] >= 0 && slot[e] < sel) {
                     oidx[slot[e]] = idx[e];
                     if (osc)
-                        osc[slot[e]] = key_score(key[q0 + e]);
+                        osc[slot[e]] = key_score(key[q0 + e < NQ ? q0 + e : 0]);
                 }
         }
     }
@@ -205,8 +216,9 @@ __device__ __forceinline__ void member_select(const float *r, const int32_t *lis
         }
 }
 
-// Group j of the launch (request j % B, its (j / B)-th longest group).
-template <int H, int D>
+// Group j of the launch (request j % B, its (j / B)-th longest group), with
+// lists of at most CAP candidates.
+template <int H, int D, int CAP>
 __device__ __forceinline__ void refine_group(const RefineLdsParams &p, int64_t j)
 {
     using S = Shape<H, D>;
@@ -222,8 +234,8 @@ __device__ __forceinline__ void refine_group(const RefineLdsParams &p, int64_t j
     constexpr int SELB = kRefMembers * (kBins1 + kRefXch) * 4;
     constexpr int KBUF = (2 * STAGE_BYTES > SELB) ? 2 * STAGE_BYTES : SELB;
     __shared__ __align__(1024) unsigned char kbuf[KBUF];
-    __shared__ __align__(16) int32_t lst[kRefineLdsCandMax];
-    __shared__ __align__(16) float rows[kRefMembers][kRefineLdsCandMax];
+    __shared__ __align__(16) int32_t lst[CAP];
+    __shared__ __align__(16) float rows[kRefMembers][CAP];
 
     const int bi = (int)(j % p.B);
     const Req rq = request_of(p.req, bi, p.L, p.q_len, p.g, p.m0);
@@ -247,13 +259,15 @@ __device__ __forceinline__ void refine_group(const RefineLdsParams &p, int64_t j
     const int64_t r1 = (r0 + p.g < rq.q_len) ? r0 + p.g : rq.q_len;
     const int nmem = (int)(r1 - r0);
     const int64_t t_last = off + r1 - 1;
-    const int ncand = (int)((p.c < t_last + 1) ? p.c : t_last + 1);
+    // the group's list: its first min(c, t_last + 1) entries, or cand_n[g]
+    // of them (key-chunk lists)
+    const int ncand = p.cand_n ? p.cand_n[rq.g_off + m] : (int)((p.c < t_last + 1) ? p.c : t_last + 1);
     const int32_t *clist = p.cand + (rq.g_off + m) * p.c;
     const unsigned char *Kb = reinterpret_cast<const unsigned char *>(p.K + rq.key_off * D);
     // the candidate list (eight entries per thread at most) and the member's
     // query and weights are loaded together, then the list goes to LDS
     constexpr int NT = kRefWaves * kWave;
-    constexpr int LPT = kRefineLdsCandMax / NT;
+    constexpr int LPT = CAP / NT;
     int32_t lv[LPT];
 #pragma unroll
     for (int i = 0; i < LPT; ++i) {
@@ -467,13 +481,13 @@ __device__ __forceinline__ void refine_group(const RefineLdsParams &p, int64_t j
     uint32_t *xch = reinterpret_cast<uint32_t *>(kbuf) + kRefMembers * kBins1 + mem * kRefXch;
     int32_t *oidx = p.out_idx + row * p.k;
     float *osc = p.out_score ? p.out_score + row * p.k : nullptr;
-    member_select(myrow, lst, ncaus, p.k, h, xch, hv, live, oidx, osc);
+    member_select<CAP / kWave / kRefHalves>(myrow, lst, ncaus, p.k, h, xch, hv, live, oidx, osc);
 }
 
 // Persistent workgroups: each takes groups j = blockIdx.x, + gridDim.x, ...;
 // the barrier between two groups keeps the next group's list and stage
 // writes behind the last selection's reads.
-template <int H, int D>
+template <int H, int D, int CAP>
 __global__ __launch_bounds__(kRefWaves * kWave) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void refine_lds_kernel(RefineLdsParams p)
 {
@@ -482,20 +496,30 @@ void refine_lds_kernel(RefineLdsParams p)
     const int G8 = gridDim.x / 8;
     const int64_t b = (gridDim.x % 8 == 0) ? (int64_t)(blockIdx.x % 8) * G8 + blockIdx.x / 8 : blockIdx.x;
     for (int64_t j = b; j < p.nwork; j += gridDim.x) {
-        refine_group<H, D>(p, j);
+        refine_group<H, D, CAP>(p, j);
         __syncthreads();
     }
+}
+
+template <int H, int D>
+static void launch_refine_lds_t(const RefineLdsParams &prm, int grid, hipStream_t stream)
+{
+    const dim3 block(kRefWaves * kWave);
+    if (prm.c <= kRefCapSmall)
+        hipLaunchKernelGGL((refine_lds_kernel<H, D, kRefCapSmall>), dim3((unsigned)grid), block, 0, stream, prm);
+    else
+        hipLaunchKernelGGL((refine_lds_kernel<H, D, kRefineLdsCandMax>), dim3((unsigned)grid), block, 0, stream,
+                           prm);
 }
 
 hipError_t launch_refine_lds(int H, int D, const RefineLdsParams &prm, int grid, hipStream_t stream)
 {
     if (prm.g > kRefMembers || prm.c > kRefineLdsCandMax || prm.nwork < 1 || grid < 1)
         return hipErrorInvalidValue;
-    const dim3 block(kRefWaves * kWave);
     if (H == 64 && D == 128)
-        hipLaunchKernelGGL((refine_lds_kernel<64, 128>), dim3((unsigned)grid), block, 0, stream, prm);
+        launch_refine_lds_t<64, 128>(prm, grid, stream);
     else if (H == 4 && D == 32)
-        hipLaunchKernelGGL((refine_lds_kernel<4, 32>), dim3((unsigned)grid), block, 0, stream, prm);
+        launch_refine_lds_t<4, 32>(prm, grid, stream);
     else
         return hipErrorInvalidValue;
     return hipGetLastError();

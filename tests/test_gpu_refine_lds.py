@@ -1,10 +1,11 @@
 """PIVOT-Refine on the on-chip re-score kernel (groups of at most four members
-and at most 4096 candidates, each member's scores and top-k kept in LDS) at
+and at most 4608 candidates, each member's scores and top-k kept in LDS) at
 its limits, against the oracle re-scoring the GPU's own candidates (PIVOT,
 Method: member i keeps its own top-k among the candidates causal for it).
 
-Covered: the largest list it takes (c = 4096) beside the first one it does not
-(c = 4097, the scan kernel's Refine); k above 2048 (output slots past the
+Covered: both list capacities it is built for (c = 4096 and c = 4097 .. 4608)
+at their edges, beside the first list it does not take (c = 4609, the scan
+kernel's Refine); k above 2048 (output slots past the
 first half of a row) and above a short group's list (padding); exact-integer
 inputs whose rows hold long runs of equal scores (the partial take of equal
 keys at the cut); all-zero queries (every score equal: the first k candidates
@@ -28,7 +29,7 @@ def sample_groups(G, n, seed):
     return [(0, int(m)) for m in sorted(set(range(n)) | set(range(G - n, G)) | set(mid.tolist()))]
 
 
-@pytest.mark.parametrize("c", [4096, 4097])
+@pytest.mark.parametrize("c", [4096, 4097, 4608, 4609])
 def test_refine_list_limit(c):
     L, g, k = 6000, 4, 2048
     Q, W, K = synth.prefill(L, 64, 128, 0.95, 4, seed=71, device=DEV)
