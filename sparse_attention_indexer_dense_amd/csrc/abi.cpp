@@ -737,6 +737,7 @@ size_t workspace_for(int mode, const Batch &b, int H, int D, int64_t c, int64_t 
 // one region shared by the coarse scan and Refine.
 struct ChunkPlan {
     bool split_scan = false, split_refine = false;
+    bool refine_lds = false;  // Refine on refine.hip (groups of 2-4 rows, short lists)
     int nw_refine = 4;
     int cap_scan = 0, cap_refine = 0;
     int64_t G = 0, cw = 0;
@@ -793,10 +794,13 @@ int make_chunk_plan(const Batch &b, int H, int D, int64_t nc, int64_t nsel, int6
     // one row per group: every row has a list of its own, so each one-wave
     // workgroup streams its own list (several per CU)
     pl.split_refine = b.q_len <= kSplitRowsMax;
+    pl.refine_lds = !pl.split_refine && b.g >= 2 && b.g <= 4 && pl.cw <= kRefineLdsCandMax;
     pl.nw_refine = b.g == 1 ? 1 : (b.g <= 4 ? 4 : 8);
     pl.cap_refine = (int)ceil_div(pl.cw + 128, 64) * 64;
-    work = std::max(work, pl.split_refine ? (size_t)b.B * b.q_len * score_row(pl.cw) * sizeof(float)
-                                          : scan_bytes(H, D, pl.nw_refine, pl.cap_refine));
+    if (pl.split_refine)
+        work = std::max(work, (size_t)b.B * b.q_len * score_row(pl.cw) * sizeof(float));
+    else if (!pl.refine_lds)
+        work = std::max(work, scan_bytes(H, D, pl.nw_refine, pl.cap_refine));
     pl.off_work = off;
     off += align_up(work);
     pl.total = off;
@@ -927,7 +931,7 @@ int run_chunk_refine(const Batch &b, const void *Qv, const float *W, const void 
     if (pl.split_refine)
         return run_split(kRefine, pr, Q, W, K, cand, b.q_len, score_row(pl.cw), H, D, (int)k, 0, out_idx, out_score, 0,
                          nullptr, nullptr, work, stream);
-    if (b.g >= 2 && b.g <= 4 && pl.cw <= kRefineLdsCandMax) {
+    if (pl.refine_lds) {
         // groups of two to four rows sharing a list: the members' scores and
         // selections on chip (a single row per list stays on the one-wave
         // scan workgroups below)

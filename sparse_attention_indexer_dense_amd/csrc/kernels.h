@@ -221,7 +221,8 @@ hipError_t launch_fill_guarded(const ReqDesc *req, int B, int64_t L, int64_t q_l
 hipError_t launch_scan_select(int H, int D, int NW, int mode, const ScanParams &prm, int grid,
                               hipStream_t stream);
 hipError_t launch_pool(int H, int D, const PoolParams &prm, hipStream_t stream);
-// one workgroup per (request, group) slot: nblocks = B * (groups of the largest request)
+// grid workgroups (at most one per CU fits its LDS), each looping over the
+// prm.nwork groups of the launch
 hipError_t launch_refine_lds(int H, int D, const RefineLdsParams &prm, int grid, hipStream_t stream);
 // mr: score rows per wave (2: Refine member rows paired over their group's
 // candidate list; needs an even g)
