@@ -10,7 +10,8 @@ first half of a row) and above a short group's list (padding); exact-integer
 inputs whose rows hold long runs of equal scores (the partial take of equal
 keys at the cut); all-zero queries (every score equal: the first k candidates
 in index order); three-member groups with a short last group and a stage
-count that is odd before padding, on the small shape."""
+count that is odd before padding, on the small shape; and a mix of g, c, k,
+lengths and batch sizes on sampled groups."""
 import numpy as np
 import pytest
 import torch
@@ -83,4 +84,32 @@ def test_refine_three_members_small_shape():
     L, g, c, k = 5001, 3, 300, 100
     Q, W, K = synth.prefill(L, 4, 32, 0.9, 2, seed=75, device=DEV)
     rc, rr, _, _, _ = check_pivot(Q, W, K, g, c, k, "refine", groups=sample_groups((L + g - 1) // g, 8, 5))
+    assert_ok(rc, rr)
+
+
+# (seed, B, L, shape, g, c, k): list lengths below, at and between the two
+# capacities, every g the kernel takes, k from small to c, one and two requests
+MIX = [
+    (81, 1, 777, (4, 32), 1, 130, 17),
+    (82, 2, 1300, (4, 32), 2, 257, 256),
+    (83, 1, 2049, (4, 32), 3, 2048, 1000),
+    (84, 2, 5000, (4, 32), 4, 4500, 4500),
+    (85, 1, 4700, (4, 32), 2, 4608, 123),
+    (86, 1, 3000, (64, 128), 3, 1000, 999),
+]
+
+
+@pytest.mark.parametrize("case", MIX, ids=[f"mix{i}" for i in range(len(MIX))])
+def test_refine_parameter_mix(case):
+    seed, B, L, (H, d), g, c, k = case
+    Qs, Ws, Ks = [], [], []
+    for b in range(B):
+        Q, W, K = synth.prefill(L, H, d, 0.9, 2, seed + 13 * b, DEV)
+        Qs.append(Q)
+        Ws.append(W)
+        Ks.append(K)
+    Q, W, K = torch.cat(Qs), torch.cat(Ws), torch.cat(Ks)
+    G = -(-L // g)
+    groups = [(b, m) for b in range(B) for _, m in sample_groups(G, 4, seed)]
+    rc, rr, _, _, _ = check_pivot(Q, W, K, g, c, k, "refine", groups=groups)
     assert_ok(rc, rr)
