@@ -124,12 +124,21 @@ __global__ __launch_bounds__(kSplitWaves * kWave) void split_score_kernel(SplitS
     const int half = lane >> 5;
     const int col = lane & 31;
     const SplitRow sr = split_row(p, H, D, bi, r);
+    // Tiles of a row without a list are dealt to the row's waves in turn
+    // (wave wr of nwr takes tiles wr, wr + nwr, ...), so that the row's waves
+    // read neighbouring key rows at any moment; with a list, each wave takes
+    // a contiguous span (its part of the list is staged in LDS).
+    const int nwr = (int)gridDim.x * kSplitWaves;
+    const int wr = (int)blockIdx.x * kSplitWaves + wave;
+    const int ntr = (sr.npos + 31) / 32;  // tiles of the row
     const int span = (int)(p.chunk / kSplitWaves);
-    const int w0 = (int)(blockIdx.x * p.chunk) + wave * span;
-    if (w0 >= sr.npos)
+    const int w0 = LIST ? (int)(blockIdx.x * p.chunk) + wave * span : 0;
+    const int w1 = LIST ? ((w0 + span < sr.npos) ? w0 + span : sr.npos) : sr.npos;
+    const int ntile = LIST ? (w1 - w0 + 31) / 32 : (wr < ntr ? (ntr - wr + nwr - 1) / nwr : 0);
+    if (LIST ? w0 >= sr.npos : ntile == 0)
         return;
-    const int w1 = (w0 + span < sr.npos) ? w0 + span : sr.npos;
-    const int ntile = (w1 - w0 + 31) / 32;
+    // position of lane col in the wave's tile t
+    auto tile_pos = [&](int t) { return (LIST ? w0 + t * 32 : (t * nwr + wr) * 32) + col; };
     const uint16_t *Kb = sr.Kb;
     float *out = p.scores + ((int64_t)bi * p.nrows + r) * p.rowlen;  // row r + m at out + m * rowlen
     int32_t *wl = lst[wave];
@@ -182,13 +191,13 @@ __global__ __launch_bounds__(kSplitWaves * kWave) void split_score_kernel(SplitS
         }
     }
 
-    // B fragments of tile t: key row w0 + 32t + col (through the list for
-    // Refine); a lane without a key (past the span or the list's valid
-    // entries, or beyond the ring's last tile) reads row 0, whose score is
-    // never stored
+    // B fragments of tile t: key row tile_pos(t) (through the list for
+    // Refine); a lane without a key (past the row, the span or the list's
+    // valid entries, or beyond the ring's last tile) reads row 0, whose score
+    // is never stored
     bf16x8 kq[P][KS];
     auto load_tile = [&](int t, bf16x8 (&kf)[KS]) {
-        const int pos = w0 + t * 32 + col;
+        const int pos = tile_pos(t);
         const bool ok = t < ntile && pos < w1;
         int key = pos;
         if (LIST)
@@ -234,7 +243,7 @@ __global__ __launch_bounds__(kSplitWaves * kWave) void split_score_kernel(SplitS
             for (int mb = 1; mb < MB; ++mb)
                 srow[m] += part[mb];
         }
-        const int pos = w0 + t * 32 + col;
+        const int pos = tile_pos(t);
         if constexpr (MR == 1) {
             const float total = half_wave_sum(srow[0]) + 0.0f;
             if (lane < 32 && pos < w1)
