@@ -367,9 +367,10 @@ int check_ptrs(const void *Q, const float *W, const void *K, const int32_t *out_
 }
 
 // Positions per workgroup of split_score_kernel: one round of workgroups (one
-// per CU, four waves each) covers all rows, each wave a contiguous span of at
-// least 128 positions (to amortise loading its query row); a span that reads
-// a candidate list is capped by the list's LDS buffer.
+// per CU, four waves each) covers all rows, each wave at least 128 positions
+// (to amortise loading its query row): a contiguous span when it reads a
+// candidate list (capped by the list's LDS buffer), else the same number of
+// 32-key tiles dealt over the row's waves in turn.
 int64_t split_chunk(int64_t rows_total, int64_t npos, bool list)
 {
     const int64_t waves = (int64_t)std::max(1, num_cus()) * kSplitWaves;

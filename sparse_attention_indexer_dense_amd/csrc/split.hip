@@ -4,10 +4,10 @@
 // drafts of one step) scores only g new rows per request against a long
 // cache, so there are too few rows to fill the GPU with one workgroup per row.
 // The key axis is split instead:
-//   split_score_kernel  - a workgroup owns (batch item, row, span of key
-//                         positions), one round of workgroups for all rows;
-//                         each wave streams its own contiguous part of the
-//                         span in 32-key tiles, loaded straight into
+//   split_score_kernel  - workgroups per (batch item, row), one round of
+//                         workgroups for all rows; the row's waves take its
+//                         32-key tiles in turn (a Refine wave: a contiguous
+//                         span of its group's candidate list), loaded straight into
 //                         registers as MFMA B fragments (several tiles in
 //                         flight while one is scored), runs the MFMA score
 //                         tile and the ReLU/weight/head-sum epilogue, and
