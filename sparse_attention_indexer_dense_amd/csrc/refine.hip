@@ -260,7 +260,9 @@ __device__ __forceinline__ void refine_group(const RefineLdsParams &p, int64_t j
     const int nmem = (int)(r1 - r0);
     const int64_t t_last = off + r1 - 1;
     // the group's list: its first min(c, t_last + 1) entries, or cand_n[g]
-    // of them (key-chunk lists)
+    // of them (key-chunk lists); at least one either way (c >= k >= 1, and a
+    // key-chunk list holds a selected chunk or the keys after the last one),
+    // which the clamped gather index below relies on
     const int ncand = p.cand_n ? p.cand_n[rq.g_off + m] : (int)((p.c < t_last + 1) ? p.c : t_last + 1);
     const int32_t *clist = p.cand + (rq.g_off + m) * p.c;
     const unsigned char *Kb = reinterpret_cast<const unsigned char *>(p.K + rq.key_off * D);
