@@ -261,8 +261,9 @@ int indexer_pivot_refine_varlen(const void *Q, const float *W, const void *K,
  *                   in index order divided (IEEE fp32) by the chunk's size,
  *                   rounded to bf16 nearest-even (a stated reading: the paper
  *                   gives no precision).
- * Uniform batches only (B requests of L keys, the last q_len positions
- * queried), with L >= 1 and q_len >= 1.
+ * Uniform batches (B requests of L keys, the last q_len positions queried,
+ * L >= 1 and q_len >= 1), and variable-length ones (the *_varlen calls
+ * below).
  * ------------------------------------------------------------------------ */
 
 /* Fixed blocks: cend[b] = min((b + 1) * block, L) for b < nc = ceil(L / block),
@@ -309,8 +310,8 @@ int indexer_chunk_means(const void *K, int B, int64_t L, int d_I, const int32_t 
  *  3. every member re-scores the candidates at or before its own position and
  *     keeps its top-k (out_idx, out_score as for the other entry points).
  * max_chunk: the largest chunk size in cend (block for fixed blocks, 2*block
- * for adaptive ones); a larger chunk makes the list exceed cw and is
- * truncated. Requires cw >= k. opts->guard must be 0.
+ * for adaptive ones; a larger value only widens the rows); a larger chunk
+ * makes the list exceed cw and is truncated. Requires cw >= k. opts->guard must be 0.
  *   Kbar     [B][nc][d_I]     summaries (indexer_chunk_means)
  *   out_chunks [B][G][nsel]   int32, may be NULL: selected chunks, ascending, -1 after
  *   out_cand [B][G][cw]       int32, may be NULL: the candidate lists
@@ -323,6 +324,39 @@ int indexer_chunk_refine(const void *Q, const float *W, const void *K, const voi
                          const dsaidx_pivot_opts *opts, int32_t *out_idx, float *out_score,
                          int32_t *out_chunks, int32_t *out_cand,
                          void *ws, size_t ws_bytes, hipStream_t stream);
+
+/* Variable-length batches on the key-chunk path (the calls above for B
+ * requests of their own lengths). Request r has L[r] >= 1 keys, q_len[r]
+ * queried positions (0 <= q_len[r] <= L[r], the last q_len[r] of its keys) and
+ * nc[r] chunks (1 <= nc[r] <= L[r]); L, q_len and nc are host arrays of B
+ * entries. Device arrays are the requests' rows one after the other:
+ *   K [sum L][d_I], Q [sum q_len][H_I][d_I], W [sum q_len][H_I],
+ *   cend [sum nc] (each request's chunk ends counted from its own first key,
+ *   as in the uniform form), Kbar [sum nc][d_I],
+ *   out_idx, out_score [sum q_len][k], out_chunks [sum G_r][nsel],
+ *   out_cand [sum G_r][cw] with G_r = ceil(q_len[r] / g), cw = (nsel + 1) * max_chunk.
+ * Every size is checked before anything is enqueued (a request with
+ * q_len[r] = 0 only advances the offsets); then each request runs as a
+ * uniform batch of one, in order, on `stream`, with the launches of that
+ * form, reusing ws: suited to batches of few long requests. Results equal
+ * those of the uniform calls on each request alone. fixed: nc[r] =
+ * ceil(L[r] / block) chunk ends per request; adaptive: as indexer_chunks_adaptive
+ * per request (ws: the largest request's scratch). */
+int indexer_chunks_fixed_varlen(int B, const int64_t *L, int block, int32_t *cend, hipStream_t stream);
+size_t indexer_chunks_adaptive_varlen_workspace_bytes(int B, const int64_t *L, int block);
+int indexer_chunks_adaptive_varlen(const void *K, int B, const int64_t *L, int d_I, int block, int32_t *cend,
+                                   void *ws, size_t ws_bytes, hipStream_t stream);
+int indexer_chunk_means_varlen(const void *K, int B, const int64_t *L, int d_I, const int32_t *cend,
+                               const int64_t *nc, void *Kbar, hipStream_t stream);
+size_t indexer_chunk_refine_varlen_workspace_bytes(int B, const int64_t *L, const int64_t *q_len, int H_I,
+                                                   int d_I, int g, const int64_t *nc, int nsel, int max_chunk,
+                                                   int k);
+int indexer_chunk_refine_varlen(const void *Q, const float *W, const void *K, const void *Kbar,
+                                const int32_t *cend, const int64_t *nc, int B, const int64_t *L,
+                                const int64_t *q_len, int H_I, int d_I, int g, int nsel, int max_chunk, int k,
+                                const dsaidx_pivot_opts *opts, int32_t *out_idx, float *out_score,
+                                int32_t *out_chunks, int32_t *out_cand,
+                                void *ws, size_t ws_bytes, hipStream_t stream);
 
 /* Rows of a selection in ranking order. The entry points above write each
  * output row in ascending index order (the order in which a sparse attention

@@ -32,7 +32,10 @@ EXPORTS = ("indexer_workspace_bytes", "indexer_dense", "indexer_pivot_reuse",
            "indexer_pivot_reuse_varlen", "indexer_pivot_refine_varlen", "indexer_chunks_fixed",
            "indexer_chunks_adaptive_workspace_bytes", "indexer_chunks_adaptive", "indexer_chunk_means",
            "indexer_chunk_refine_workspace_bytes", "indexer_chunk_refine", "indexer_sort_rows",
-           "indexer_last_error", "indexer_version", "indexer_pivot_refine_noalloc")
+           "indexer_last_error", "indexer_version", "indexer_pivot_refine_noalloc",
+           "indexer_chunks_fixed_varlen", "indexer_chunks_adaptive_varlen_workspace_bytes",
+           "indexer_chunks_adaptive_varlen", "indexer_chunk_means_varlen",
+           "indexer_chunk_refine_varlen_workspace_bytes", "indexer_chunk_refine_varlen")
 
 
 class IndexerError(RuntimeError):
@@ -83,6 +86,19 @@ def load(path: str = LIB_PATH):
     lib.indexer_chunk_refine.argtypes = [P, P, P, P, P, i64, i32, i64, i64, i32, i32, i32, i32, i32, i32, P,
                                          P, P, P, P, P, sz, P]
     lib.indexer_chunk_refine.restype = i32
+    lib.indexer_chunks_fixed_varlen.argtypes = [i32, P, i32, P, P]
+    lib.indexer_chunks_fixed_varlen.restype = i32
+    lib.indexer_chunks_adaptive_varlen_workspace_bytes.argtypes = [i32, P, i32]
+    lib.indexer_chunks_adaptive_varlen_workspace_bytes.restype = sz
+    lib.indexer_chunks_adaptive_varlen.argtypes = [P, i32, P, i32, i32, P, P, sz, P]
+    lib.indexer_chunks_adaptive_varlen.restype = i32
+    lib.indexer_chunk_means_varlen.argtypes = [P, i32, P, i32, P, P, P, P]
+    lib.indexer_chunk_means_varlen.restype = i32
+    lib.indexer_chunk_refine_varlen_workspace_bytes.argtypes = [i32, P, P, i32, i32, i32, P, i32, i32, i32]
+    lib.indexer_chunk_refine_varlen_workspace_bytes.restype = sz
+    lib.indexer_chunk_refine_varlen.argtypes = [P, P, P, P, P, P, i32, P, P, i32, i32, i32, i32, i32, i32, P,
+                                                P, P, P, P, P, sz, P]
+    lib.indexer_chunk_refine_varlen.restype = i32
     lib.indexer_sort_rows.argtypes = [P, P, i64, i32, P]
     lib.indexer_sort_rows.restype = i32
     lib.indexer_last_error.argtypes = []
@@ -175,6 +191,34 @@ def indexer_chunk_refine(Q, W, K, Kbar, cend, nc, B, L, q_len, H_I, d_I, g, nsel
     return load().indexer_chunk_refine(Q, W, K, Kbar, cend, nc, B, L, q_len, H_I, d_I, g, nsel, max_chunk,
                                        k, opts, out_idx, out_score, out_chunks, out_cand, ws, ws_bytes,
                                        stream)
+
+
+def indexer_chunks_fixed_varlen(B, L, block, cend, stream):
+    return load().indexer_chunks_fixed_varlen(B, L, block, cend, stream)
+
+
+def indexer_chunks_adaptive_varlen_workspace_bytes(B, L, block):
+    return load().indexer_chunks_adaptive_varlen_workspace_bytes(B, L, block)
+
+
+def indexer_chunks_adaptive_varlen(K, B, L, d_I, block, cend, ws, ws_bytes, stream):
+    return load().indexer_chunks_adaptive_varlen(K, B, L, d_I, block, cend, ws, ws_bytes, stream)
+
+
+def indexer_chunk_means_varlen(K, B, L, d_I, cend, nc, Kbar, stream):
+    return load().indexer_chunk_means_varlen(K, B, L, d_I, cend, nc, Kbar, stream)
+
+
+def indexer_chunk_refine_varlen_workspace_bytes(B, L, q_len, H_I, d_I, g, nc, nsel, max_chunk, k):
+    return load().indexer_chunk_refine_varlen_workspace_bytes(B, L, q_len, H_I, d_I, g, nc, nsel, max_chunk,
+                                                              k)
+
+
+def indexer_chunk_refine_varlen(Q, W, K, Kbar, cend, nc, B, L, q_len, H_I, d_I, g, nsel, max_chunk, k, opts,
+                                out_idx, out_score, out_chunks, out_cand, ws, ws_bytes, stream):
+    return load().indexer_chunk_refine_varlen(Q, W, K, Kbar, cend, nc, B, L, q_len, H_I, d_I, g, nsel,
+                                              max_chunk, k, opts, out_idx, out_score, out_chunks, out_cand,
+                                              ws, ws_bytes, stream)
 
 
 def indexer_sort_rows(idx, score, rows, k, stream):
@@ -456,6 +500,90 @@ def chunk_refine(Q, W, K, Kbar, cend, g, nsel, max_chunk, k, proxy="mean", windo
                                 g, nsel, max_chunk, k, opts, _ptr(out_idx), _ptr(out_score),
                                 _ptr(out_chunks), _ptr(out_cand), _ptr(wsb), wsb.numel(),
                                 _stream(dev)))
+    return out_idx, out_score, out_chunks, out_cand
+
+
+def _i64(xs):
+    xs = [int(x) for x in xs]
+    return len(xs), (ctypes.c_int64 * len(xs))(*xs), xs
+
+
+def chunks_fixed_varlen(L, block, device="cuda"):
+    """Chunk ends of fixed blocks for requests of L[r] keys, one after the
+    other: (cend int32 [sum nc], nc list), nc[r] = ceil(L[r] / block)."""
+    import torch
+    dev = torch.device(device)
+    B, La, Ls = _i64(L)
+    nc = [-(-x // block) for x in Ls]
+    cend = torch.empty((sum(nc),), dtype=torch.int32, device=dev)
+    _check(indexer_chunks_fixed_varlen(B, La, block, _ptr(cend), _stream(dev)))
+    return cend, nc
+
+
+def chunks_adaptive_varlen(K, L, block, ws=None):
+    """Score-adaptive chunk ends of packed keys K [sum L, d] per request:
+    (cend int32 [sum nc], nc list), nc[r] = ceil(L[r] / block)."""
+    import torch
+    if K.dtype != torch.bfloat16 or K.dim() != 2 or not K.is_cuda or not K.is_contiguous():
+        raise ValueError("K must be a contiguous bf16 GPU tensor [sum L, d]")
+    B, La, Ls = _i64(L)
+    if K.shape[0] != sum(Ls):
+        raise ValueError("K rows do not match the request lengths")
+    dev = K.device
+    need = indexer_chunks_adaptive_varlen_workspace_bytes(B, La, block)
+    wsb = (ws or _default_ws).get(need, dev)
+    nc = [-(-x // block) for x in Ls]
+    cend = torch.empty((sum(nc),), dtype=torch.int32, device=dev)
+    _check(indexer_chunks_adaptive_varlen(_ptr(K), B, La, K.shape[1], block, _ptr(cend), _ptr(wsb), wsb.numel(),
+                                          _stream(dev)))
+    return cend, nc
+
+
+def chunk_means_varlen(K, L, cend, nc, out=None):
+    """Mean-key summaries bf16 [sum nc, d] of the chunks of packed keys K [sum L, d]."""
+    import torch
+    B, La, Ls = _i64(L)
+    _, nca, ncs = _i64(nc)
+    if len(ncs) != B or K.shape[0] != sum(Ls):
+        raise ValueError("L, nc and K rows do not match")
+    if cend.dtype != torch.int32 or tuple(cend.shape) != (sum(ncs),) or not cend.is_contiguous():
+        raise ValueError("cend must be contiguous int32 [sum nc]")
+    d = K.shape[1]
+    Kbar = out if out is not None else torch.empty((sum(ncs), d), dtype=torch.bfloat16, device=K.device)
+    _check(indexer_chunk_means_varlen(_ptr(K), B, La, d, _ptr(cend), nca, _ptr(Kbar), _stream(K.device)))
+    return Kbar
+
+
+def chunk_refine_varlen(Q, W, K, Kbar, cend, L, q_len, nc, g, nsel, max_chunk, k, proxy="mean", window=0,
+                        scores=True, chunks=False, cand=False, ws=None):
+    """The key-chunk path over packed requests: (idx [sum q_len, k], score or
+    None, selected chunks [sum G, nsel] or None, candidate lists [sum G, cw]
+    or None), G_r = ceil(q_len[r] / g), cw = (nsel + 1) * max_chunk."""
+    import torch
+    B, La, qa, H, d = _varlen_shapes(Q, W, K, L, q_len)
+    _, nca, ncs = _i64(nc)
+    if len(ncs) != B:
+        raise ValueError("nc must list one chunk count per request")
+    if tuple(Kbar.shape) != (sum(ncs), d) or Kbar.dtype != torch.bfloat16 or not Kbar.is_contiguous():
+        raise ValueError("Kbar must be contiguous bf16 [sum nc, d]")
+    if cend.dtype != torch.int32 or tuple(cend.shape) != (sum(ncs),) or not cend.is_contiguous():
+        raise ValueError("cend must be contiguous int32 [sum nc]")
+    if proxy not in PROXY:
+        raise ValueError(f"proxy must be one of {sorted(PROXY)}")
+    dev = Q.device
+    need = indexer_chunk_refine_varlen_workspace_bytes(B, La, qa, H, d, g, nca, nsel, max_chunk, k)
+    wsb = (ws or _default_ws).get(need, dev)
+    nq = Q.shape[0]
+    ng = sum((int(x) + g - 1) // g for x in q_len)
+    cw = (nsel + 1) * max_chunk
+    out_idx = torch.empty((nq, k), dtype=torch.int32, device=dev)
+    out_score = torch.empty((nq, k), dtype=torch.float32, device=dev) if scores else None
+    out_chunks = torch.empty((ng, nsel), dtype=torch.int32, device=dev) if chunks else None
+    out_cand = torch.empty((ng, cw), dtype=torch.int32, device=dev) if cand else None
+    opts = ctypes.byref(PivotOpts(0, PROXY[proxy], int(window)))
+    _check(indexer_chunk_refine_varlen(_ptr(Q), _ptr(W), _ptr(K), _ptr(Kbar), _ptr(cend), nca, B, La, qa, H, d,
+                                       g, nsel, max_chunk, k, opts, _ptr(out_idx), _ptr(out_score),
+                                       _ptr(out_chunks), _ptr(out_cand), _ptr(wsb), wsb.numel(), _stream(dev)))
     return out_idx, out_score, out_chunks, out_cand
 
 

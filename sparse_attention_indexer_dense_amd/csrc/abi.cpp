@@ -760,8 +760,8 @@ int make_chunk_plan(const Batch &b, int H, int D, int64_t nc, int64_t nsel, int6
         return fail(DSAIDX_EINVAL, "nc=%lld must be in [1, L=%lld]", (long long)nc, (long long)b.L);
     if (nsel < 1 || nsel > kMaxSel)
         return fail(DSAIDX_EINVAL, "nsel=%lld must be in [1, 2^20]", (long long)nsel);
-    if (max_chunk < 1 || max_chunk > b.L)
-        return fail(DSAIDX_EINVAL, "max_chunk=%lld must be in [1, L=%lld]", (long long)max_chunk, (long long)b.L);
+    if (max_chunk < 1)
+        return fail(DSAIDX_EINVAL, "max_chunk=%lld must be >= 1", (long long)max_chunk);
     pl = ChunkPlan{};
     pl.cw = (nsel + 1) * max_chunk;
     if (pl.cw > kMaxCandWidth)
@@ -1071,6 +1071,30 @@ int scratch_address(hipStream_t stream, void **out)
 
 }  // namespace
 
+// ------------------------------------ key chunks, variable-length batches
+// Request r of a variable-length chunk call: L[r] keys, q_len[r] queried
+// positions, nc[r] chunks (nc may be NULL where the call has none), checked
+// before anything is enqueued; each request then runs as a uniform batch of
+// one on the caller's stream.
+int check_chunk_varlen(int B, const int64_t *L, const int64_t *q_len, const int64_t *nc)
+{
+    if (B < 1 || B > 65535)
+        return fail(DSAIDX_EINVAL, "B=%d must be in [1, 65535]", B);
+    if (!L)
+        return fail(DSAIDX_EINVAL, "L must not be NULL");
+    for (int r = 0; r < B; ++r) {
+        if (L[r] < 1 || L[r] >= (int64_t)INT32_MAX)
+            return fail(DSAIDX_EINVAL, "request %d: L=%lld must be in [1, 2^31-1)", r, (long long)L[r]);
+        if (q_len && (q_len[r] < 0 || q_len[r] > L[r]))
+            return fail(DSAIDX_EINVAL, "request %d: q_len=%lld must be in [0, L=%lld]", r, (long long)q_len[r],
+                        (long long)L[r]);
+        if (nc && (nc[r] < 1 || nc[r] > L[r]))
+            return fail(DSAIDX_EINVAL, "request %d: nc=%lld must be in [1, L=%lld]", r, (long long)nc[r],
+                        (long long)L[r]);
+    }
+    return DSAIDX_OK;
+}
+
 extern "C" {
 
 size_t indexer_workspace_bytes(int mode, int B, int64_t L, int64_t q_len, int H_I, int d_I, int g, int c, int k)
@@ -1313,6 +1337,187 @@ int indexer_chunk_refine(const void *Q, const float *W, const void *K, const voi
         return s;
     return run_chunk_refine(b, Q, W, K, Kbar, cend, nc, H_I, d_I, nsel, max_chunk, k, out_idx, out_score,
                             out_chunks, out_cand, ws, ws_bytes, stream);
+}
+
+int indexer_chunks_fixed_varlen(int B, const int64_t *L, int block, int32_t *cend, hipStream_t stream)
+{
+    int s = check_chunk_varlen(B, L, nullptr, nullptr);
+    if (s != DSAIDX_OK)
+        return s;
+    if (block < 1)
+        return fail(DSAIDX_EINVAL, "block=%d must be >= 1", block);
+    if (!cend || !aligned(cend, 4))
+        return fail(DSAIDX_EINVAL, "cend must be a non-NULL 4-byte aligned pointer");
+    int64_t off = 0;
+    for (int r = 0; r < B; ++r) {
+        const int64_t n = ceil_div(L[r], block);
+        hipError_t e = launch_chunk_fixed(1, L[r], block, n, cend + off, stream);
+        if (e != hipSuccess)
+            return hip_fail(e, "chunk launch");
+        off += n;
+    }
+    return DSAIDX_OK;
+}
+
+size_t indexer_chunks_adaptive_varlen_workspace_bytes(int B, const int64_t *L, int block)
+{
+    if (check_chunk_varlen(B, L, nullptr, nullptr) != DSAIDX_OK)
+        return 0;
+    size_t need = 0;
+    for (int r = 0; r < B; ++r) {
+        const size_t n = indexer_chunks_adaptive_workspace_bytes(1, L[r], block);
+        if (n == 0)
+            return 0;
+        need = std::max(need, n);
+    }
+    return need;
+}
+
+int indexer_chunks_adaptive_varlen(const void *K, int B, const int64_t *L, int d_I, int block, int32_t *cend,
+                                   void *ws, size_t ws_bytes, hipStream_t stream)
+{
+    int s = check_chunk_varlen(B, L, nullptr, nullptr);
+    if (s != DSAIDX_OK)
+        return s;
+    if (block < 2 || block % 2)
+        return fail(DSAIDX_EINVAL, "block=%d must be even", block);
+    if (d_I != 128 && d_I != 32)
+        return fail(DSAIDX_EUNSUPPORTED, "d_I=%d has no kernel; supported: 32, 128", d_I);
+    for (int r = 0; r < B; ++r)
+        if (ceil_div(L[r], block) > kAdaptBlocksMax)
+            return fail(DSAIDX_EUNSUPPORTED, "request %d: %lld blocks exceed the %d the adaptive partition supports",
+                        r, (long long)ceil_div(L[r], block), kAdaptBlocksMax);
+    if (!K || !cend || !aligned(K, 16) || !aligned(cend, 4))
+        return fail(DSAIDX_EINVAL, "K (16-byte aligned) and cend (4-byte aligned) must not be NULL");
+    const size_t need = indexer_chunks_adaptive_varlen_workspace_bytes(B, L, block);
+    if (need > 0 && (!ws || !aligned(ws, 16)))
+        return fail(DSAIDX_EINVAL, "ws must be a non-NULL 16-byte aligned pointer (%zu bytes needed)", need);
+    if (ws_bytes < need)
+        return fail(DSAIDX_EWORKSPACE, "workspace of %zu bytes is below the %zu needed", ws_bytes, need);
+    const uint16_t *Kh = static_cast<const uint16_t *>(K);
+    int64_t koff = 0, coff = 0;
+    for (int r = 0; r < B; ++r) {
+        // (the request's own call reuses ws: its launches follow the previous
+        // request's on the same stream)
+        s = indexer_chunks_adaptive(Kh + koff * d_I, 1, L[r], d_I, block, cend + coff, ws, ws_bytes, stream);
+        if (s != DSAIDX_OK)
+            return s;
+        koff += L[r];
+        coff += ceil_div(L[r], block);
+    }
+    return DSAIDX_OK;
+}
+
+int indexer_chunk_means_varlen(const void *K, int B, const int64_t *L, int d_I, const int32_t *cend,
+                               const int64_t *nc, void *Kbar, hipStream_t stream)
+{
+    if (!nc)
+        return fail(DSAIDX_EINVAL, "nc must not be NULL");
+    int s = check_chunk_varlen(B, L, nullptr, nc);
+    if (s != DSAIDX_OK)
+        return s;
+    if (d_I != 128 && d_I != 32)
+        return fail(DSAIDX_EUNSUPPORTED, "d_I=%d has no kernel; supported: 32, 128", d_I);
+    if (!K || !cend || !Kbar || !aligned(K, 16) || !aligned(Kbar, 16) || !aligned(cend, 4))
+        return fail(DSAIDX_EINVAL, "K, Kbar (16-byte aligned) and cend (4-byte aligned) must not be NULL");
+    const uint16_t *Kh = static_cast<const uint16_t *>(K);
+    uint16_t *Kb = static_cast<uint16_t *>(Kbar);
+    int64_t koff = 0, coff = 0;
+    for (int r = 0; r < B; ++r) {
+        s = indexer_chunk_means(Kh + koff * d_I, 1, L[r], d_I, cend + coff, nc[r], 0, Kb + coff * d_I, stream);
+        if (s != DSAIDX_OK)
+            return s;
+        koff += L[r];
+        coff += nc[r];
+    }
+    return DSAIDX_OK;
+}
+
+size_t indexer_chunk_refine_varlen_workspace_bytes(int B, const int64_t *L, const int64_t *q_len, int H_I, int d_I,
+                                                   int g, const int64_t *nc, int nsel, int max_chunk, int k)
+{
+    if (!q_len || !nc) {
+        fail(DSAIDX_EINVAL, "q_len and nc must not be NULL");
+        return 0;
+    }
+    if (check_chunk_varlen(B, L, q_len, nc) != DSAIDX_OK)
+        return 0;
+    size_t need = 256;  // (no request with rows: nothing is used, but 0 means an error)
+    for (int r = 0; r < B; ++r) {
+        if (q_len[r] == 0)
+            continue;
+        const size_t n =
+            indexer_chunk_refine_workspace_bytes(1, L[r], q_len[r], H_I, d_I, g, nc[r], nsel, max_chunk, k);
+        if (n == 0)
+            return 0;
+        need = std::max(need, n);
+    }
+    return need;
+}
+
+int indexer_chunk_refine_varlen(const void *Q, const float *W, const void *K, const void *Kbar,
+                                const int32_t *cend, const int64_t *nc, int B, const int64_t *L,
+                                const int64_t *q_len, int H_I, int d_I, int g, int nsel, int max_chunk, int k,
+                                const dsaidx_pivot_opts *opts, int32_t *out_idx, float *out_score,
+                                int32_t *out_chunks, int32_t *out_cand, void *ws, size_t ws_bytes,
+                                hipStream_t stream)
+{
+    if (!q_len || !nc)
+        return fail(DSAIDX_EINVAL, "q_len and nc must not be NULL");
+    int s = check_chunk_varlen(B, L, q_len, nc);
+    if (s != DSAIDX_OK)
+        return s;
+    // every request's plan and the pointers, before anything is enqueued
+    size_t need = 0;
+    bool any = false;
+    for (int r = 0; r < B; ++r) {
+        if (q_len[r] == 0)
+            continue;
+        Batch b;
+        s = chunk_batch(1, L[r], q_len[r], g, opts, b);
+        if (s != DSAIDX_OK)
+            return s;
+        ChunkPlan pl;
+        s = make_chunk_plan(b, H_I, d_I, nc[r], nsel, max_chunk, k, out_chunks != nullptr, out_cand != nullptr, pl);
+        if (s != DSAIDX_OK)
+            return s;
+        need = std::max(need, pl.total);
+        any = true;
+    }
+    if (!any)
+        return DSAIDX_OK;
+    s = check_ptrs(Q, W, K, out_idx, out_score, out_cand, ws, need);
+    if (s != DSAIDX_OK)
+        return s;
+    if (!Kbar || !cend)
+        return fail(DSAIDX_EINVAL, "Kbar and cend must not be NULL");
+    if (!aligned(Kbar, 16) || !aligned(cend, 4) || (out_chunks && !aligned(out_chunks, 4)))
+        return fail(DSAIDX_EINVAL, "Kbar must be 16-byte aligned, cend and out_chunks 4-byte aligned");
+    if (ws_bytes < need)
+        return fail(DSAIDX_EWORKSPACE, "workspace of %zu bytes is below the %zu needed", ws_bytes, need);
+    const uint16_t *Qh = static_cast<const uint16_t *>(Q);
+    const uint16_t *Kh = static_cast<const uint16_t *>(K);
+    const uint16_t *Kb = static_cast<const uint16_t *>(Kbar);
+    const int64_t cw = (int64_t)(nsel + 1) * max_chunk;
+    int64_t koff = 0, qoff = 0, coff = 0, goff = 0;
+    for (int r = 0; r < B; ++r) {
+        if (q_len[r] > 0) {
+            Batch b;
+            chunk_batch(1, L[r], q_len[r], g, opts, b);
+            s = run_chunk_refine(b, Qh + qoff * H_I * d_I, W + qoff * H_I, Kh + koff * d_I, Kb + coff * d_I,
+                                 cend + coff, nc[r], H_I, d_I, nsel, max_chunk, k, out_idx + qoff * k,
+                                 out_score ? out_score + qoff * k : nullptr,
+                                 out_chunks ? out_chunks + goff * nsel : nullptr,
+                                 out_cand ? out_cand + goff * cw : nullptr, ws, ws_bytes, stream);
+            if (s != DSAIDX_OK)
+                return s;
+        }
+        koff += L[r];
+        qoff += q_len[r];
+        coff += nc[r];
+        goff += ceil_div(q_len[r], g);
+    }
+    return DSAIDX_OK;
 }
 
 int indexer_sort_rows(int32_t *idx, float *score, int64_t rows, int k, hipStream_t stream)

@@ -225,3 +225,47 @@ def test_sort_rows_rejects_bad_arguments():
     assert dsa.indexer_sort_rows(fake(), None, 10, 64, None) == EINVAL
     assert dsa.indexer_sort_rows(fake(), fake(), -1, 64, None) == EINVAL
     assert dsa.indexer_sort_rows(fake(), fake(), 0, 64, None) == OK  # nothing to do
+
+
+def arr(*xs):
+    return (ctypes.c_int64 * len(xs))(*xs)
+
+
+def test_chunk_varlen_entry_points_reject_bad_arguments():
+    big = 1 << 40
+    L, q, nc = arr(3000, 64, 500), arr(3000, 10, 0), arr(47, 1, 8)
+    # sizes: every request is checked before anything is enqueued
+    assert dsa.indexer_chunks_fixed_varlen(3, arr(3000, 0, 500), 64, fake(), None) == EINVAL
+    assert "request 1" in dsa.indexer_last_error()
+    assert dsa.indexer_chunks_fixed_varlen(3, L, 0, fake(), None) == EINVAL
+    assert dsa.indexer_chunks_fixed_varlen(3, L, 64, None, None) == EINVAL
+    assert dsa.indexer_chunks_fixed_varlen(0, L, 64, fake(), None) == EINVAL
+    assert dsa.indexer_chunks_adaptive_varlen_workspace_bytes(3, L, 64) > 0
+    assert dsa.indexer_chunks_adaptive_varlen(fake(), 3, L, 128, 7, fake(), fake(), big, None) == EINVAL
+    assert dsa.indexer_chunks_adaptive_varlen(fake(), 3, L, 128, 64, fake(), fake(), 8, None) == EWORKSPACE
+    assert dsa.indexer_chunk_means_varlen(fake(), 3, L, 128, fake(), None, fake(), None) == EINVAL
+    assert dsa.indexer_chunk_means_varlen(fake(), 3, L, 128, fake(), arr(47, 65, 8), fake(), None) == EINVAL
+    assert "request 1" in dsa.indexer_last_error()
+
+    def ws(q_len=q, nc_=nc, nsel=8, max_chunk=64, k=128):
+        return dsa.indexer_chunk_refine_varlen_workspace_bytes(3, L, q_len, 64, 128, 4, nc_, nsel, max_chunk, k)
+    assert ws() > 0
+    assert ws(q_len=arr(0, 0, 0)) > 0                # nothing to run is still a valid call
+    assert ws(q_len=arr(3000, 65, 0)) == 0           # q_len > L
+    assert ws(nc_=arr(47, 1, 0)) == 0                # nc < 1
+    assert ws(nsel=1, max_chunk=32, k=128) == 0      # (nsel + 1) * max_chunk < k
+    assert ws(q_len=None) == 0 and ws(nc_=None) == 0
+    # a request shorter than the largest chunk is valid (its rows are only wider)
+    assert dsa.indexer_chunk_refine_varlen_workspace_bytes(2, arr(3000, 40), arr(8, 8), 64, 128, 4,
+                                                         arr(47, 1), 8, 64, 128) > 0
+
+    def refine(q_len=q, nc_=nc, Kbar=fake(), ws_bytes=big, opts=None):
+        return dsa.indexer_chunk_refine_varlen(fake(), fake(), fake(), Kbar, fake(), nc_, 3, L, q_len, 64, 128,
+                                               4, 8, 64, 128, opts, fake(), None, None, None, fake(), ws_bytes,
+                                               None)
+    assert refine(q_len=arr(3000, 65, 0)) == EINVAL and "request 1" in dsa.indexer_last_error()
+    assert refine(nc_=None) == EINVAL
+    assert refine(Kbar=None) == EINVAL
+    assert refine(ws_bytes=64) == EWORKSPACE
+    assert refine(opts=ctypes.byref(dsa.PivotOpts(64, 0, 0))) == EINVAL and "guard" in dsa.indexer_last_error()
+    assert refine(q_len=arr(0, 0, 0)) == OK          # no request has rows: nothing to do
