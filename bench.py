@@ -581,8 +581,14 @@ def refine_gather(dsa, torch, Q, W, K, g, c, k, cand):
     B, q_len, H, d = Q.shape
     L = K.shape[1]
     G = cand.shape[1]
-    t_last = torch.clamp((torch.arange(G, device=cand.device) + 1) * g, max=q_len) - 1 + (L - q_len)
-    ncand = int(torch.clamp(t_last + 1, max=c).sum()) * B
+    ar = torch.arange(G, device=cand.device)
+    t_last = torch.clamp((ar + 1) * g, max=q_len) - 1 + (L - q_len)
+    per_group = torch.clamp(t_last + 1, max=c)
+    ncand = int(per_group.sum()) * B
+    # every member scores its group's whole list (causality is applied when
+    # it selects): members x list length pairs, 2 H d flop each
+    members = torch.clamp(q_len - ar * g, max=g)
+    pairs = int((per_group * members).sum()) * B
     gather = ncand * 2 * d
     total = gather + ncand * 4 + B * q_len * (H * d * 2 + H * 4 + k * 8)
     try:
@@ -596,10 +602,12 @@ def refine_gather(dsa, torch, Q, W, K, g, c, k, cand):
         # torch's profiler under another tracer (rocprofv3) reports sub-microsecond
         # durations; no kernel moves these bytes at 4x the HBM peak
         return {"error": f"implausible profiler time {ms:.6f} ms (another tracer attached?)"}
+    tflops = pairs * 2.0 * H * d / (ms * 1e-3) / 1e12
     return {"kernel": name, "launches": n, "kernel_ms": ms,
             "candidate_keys": ncand, "gather_bytes": gather, "algorithmic_bytes": total,
             "gather_GBps": gather / (ms * 1e-3) / 1e9, "achieved_GBps": total / (ms * 1e-3) / 1e9,
-            "hbm_frac": total / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS}
+            "hbm_frac": total / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
+            "scored_pairs": pairs, "achieved_TFLOPs": tflops, "mfma_frac": tflops / PEAK_BF16_TFLOPS}
 
 
 # --------------------------------------------------------------------- main
