@@ -311,13 +311,19 @@ int indexer_chunk_means(const void *K, int B, int64_t L, int d_I, const int32_t 
  *     keeps its top-k (out_idx, out_score as for the other entry points).
  * max_chunk: the largest chunk size in cend (block for fixed blocks, 2*block
  * for adaptive ones; a larger value only widens the rows); a larger chunk
- * makes the list exceed cw and is truncated. Requires cw >= k. opts->guard must be 0.
+ * makes the list exceed cw and is truncated. Requires cw >= k.
+ * opts->guard (>= 0; PIVOT, results, the guardrail: short groups fall back to
+ * the dense indexer): a group whose whole causal prefix holds at most `guard`
+ * keys (t_last + 1 <= guard) is scored as dense rows instead, its out_chunks
+ * and out_cand rows are -1.
  *   Kbar     [B][nc][d_I]     summaries (indexer_chunk_means)
  *   out_chunks [B][G][nsel]   int32, may be NULL: selected chunks, ascending, -1 after
  *   out_cand [B][G][cw]       int32, may be NULL: the candidate lists
- * ws: indexer_chunk_refine_workspace_bytes(...) bytes. */
+ * ws: indexer_chunk_refine_workspace_bytes(...) bytes, with the call's opts
+ * (NULL: the defaults; a guard adds the dense pass of the guarded rows). */
 size_t indexer_chunk_refine_workspace_bytes(int B, int64_t L, int64_t q_len, int H_I, int d_I, int g,
-                                            int64_t nc, int nsel, int max_chunk, int k);
+                                            int64_t nc, int nsel, int max_chunk, int k,
+                                            const dsaidx_pivot_opts *opts);
 int indexer_chunk_refine(const void *Q, const float *W, const void *K, const void *Kbar,
                          const int32_t *cend, int64_t nc, int B, int64_t L, int64_t q_len,
                          int H_I, int d_I, int g, int nsel, int max_chunk, int k,
@@ -350,7 +356,7 @@ int indexer_chunk_means_varlen(const void *K, int B, const int64_t *L, int d_I, 
                                const int64_t *nc, void *Kbar, hipStream_t stream);
 size_t indexer_chunk_refine_varlen_workspace_bytes(int B, const int64_t *L, const int64_t *q_len, int H_I,
                                                    int d_I, int g, const int64_t *nc, int nsel, int max_chunk,
-                                                   int k);
+                                                   int k, const dsaidx_pivot_opts *opts);
 int indexer_chunk_refine_varlen(const void *Q, const float *W, const void *K, const void *Kbar,
                                 const int32_t *cend, const int64_t *nc, int B, const int64_t *L,
                                 const int64_t *q_len, int H_I, int d_I, int g, int nsel, int max_chunk, int k,

@@ -81,7 +81,7 @@ def load(path: str = LIB_PATH):
     lib.indexer_chunks_adaptive.restype = i32
     lib.indexer_chunk_means.argtypes = [P, i32, i64, i32, P, i64, i64, P, P]
     lib.indexer_chunk_means.restype = i32
-    lib.indexer_chunk_refine_workspace_bytes.argtypes = [i32, i64, i64, i32, i32, i32, i64, i32, i32, i32]
+    lib.indexer_chunk_refine_workspace_bytes.argtypes = [i32, i64, i64, i32, i32, i32, i64, i32, i32, i32, P]
     lib.indexer_chunk_refine_workspace_bytes.restype = sz
     lib.indexer_chunk_refine.argtypes = [P, P, P, P, P, i64, i32, i64, i64, i32, i32, i32, i32, i32, i32, P,
                                          P, P, P, P, P, sz, P]
@@ -94,7 +94,7 @@ def load(path: str = LIB_PATH):
     lib.indexer_chunks_adaptive_varlen.restype = i32
     lib.indexer_chunk_means_varlen.argtypes = [P, i32, P, i32, P, P, P, P]
     lib.indexer_chunk_means_varlen.restype = i32
-    lib.indexer_chunk_refine_varlen_workspace_bytes.argtypes = [i32, P, P, i32, i32, i32, P, i32, i32, i32]
+    lib.indexer_chunk_refine_varlen_workspace_bytes.argtypes = [i32, P, P, i32, i32, i32, P, i32, i32, i32, P]
     lib.indexer_chunk_refine_varlen_workspace_bytes.restype = sz
     lib.indexer_chunk_refine_varlen.argtypes = [P, P, P, P, P, P, i32, P, P, i32, i32, i32, i32, i32, i32, P,
                                                 P, P, P, P, P, sz, P]
@@ -182,8 +182,8 @@ def indexer_chunk_means(K, B, L, d_I, cend, nc, first, Kbar, stream):
     return load().indexer_chunk_means(K, B, L, d_I, cend, nc, first, Kbar, stream)
 
 
-def indexer_chunk_refine_workspace_bytes(B, L, q_len, H_I, d_I, g, nc, nsel, max_chunk, k):
-    return load().indexer_chunk_refine_workspace_bytes(B, L, q_len, H_I, d_I, g, nc, nsel, max_chunk, k)
+def indexer_chunk_refine_workspace_bytes(B, L, q_len, H_I, d_I, g, nc, nsel, max_chunk, k, opts=None):
+    return load().indexer_chunk_refine_workspace_bytes(B, L, q_len, H_I, d_I, g, nc, nsel, max_chunk, k, opts)
 
 
 def indexer_chunk_refine(Q, W, K, Kbar, cend, nc, B, L, q_len, H_I, d_I, g, nsel, max_chunk, k, opts,
@@ -209,9 +209,9 @@ def indexer_chunk_means_varlen(K, B, L, d_I, cend, nc, Kbar, stream):
     return load().indexer_chunk_means_varlen(K, B, L, d_I, cend, nc, Kbar, stream)
 
 
-def indexer_chunk_refine_varlen_workspace_bytes(B, L, q_len, H_I, d_I, g, nc, nsel, max_chunk, k):
+def indexer_chunk_refine_varlen_workspace_bytes(B, L, q_len, H_I, d_I, g, nc, nsel, max_chunk, k, opts=None):
     return load().indexer_chunk_refine_varlen_workspace_bytes(B, L, q_len, H_I, d_I, g, nc, nsel, max_chunk,
-                                                              k)
+                                                              k, opts)
 
 
 def indexer_chunk_refine_varlen(Q, W, K, Kbar, cend, nc, B, L, q_len, H_I, d_I, g, nsel, max_chunk, k, opts,
@@ -473,7 +473,7 @@ def chunk_means(K, cend, first=0, out=None):
 
 
 def chunk_refine(Q, W, K, Kbar, cend, g, nsel, max_chunk, k, proxy="mean", window=0, scores=True,
-                 chunks=False, cand=False, ws=None):
+                 chunks=False, cand=False, ws=None, guard=0):
     """Chunk-level candidates and token-level Refine: (idx [B, q_len, k], score or
     None, selected chunks [B, G, nsel] or None, candidate lists [B, G, cw] or
     None), cw = (nsel + 1) * max_chunk."""
@@ -487,7 +487,8 @@ def chunk_refine(Q, W, K, Kbar, cend, g, nsel, max_chunk, k, proxy="mean", windo
     if proxy not in PROXY:
         raise ValueError(f"proxy must be one of {sorted(PROXY)}")
     dev = Q.device
-    need = indexer_chunk_refine_workspace_bytes(B, L, q_len, H, d, g, nc, nsel, max_chunk, k)
+    opts = ctypes.byref(PivotOpts(int(guard), PROXY[proxy], int(window)))
+    need = indexer_chunk_refine_workspace_bytes(B, L, q_len, H, d, g, nc, nsel, max_chunk, k, opts)
     wsb = (ws or _default_ws).get(need, dev)
     G = (q_len + g - 1) // g
     cw = (nsel + 1) * max_chunk
@@ -495,7 +496,6 @@ def chunk_refine(Q, W, K, Kbar, cend, g, nsel, max_chunk, k, proxy="mean", windo
     out_score = torch.empty((B, q_len, k), dtype=torch.float32, device=dev) if scores else None
     out_chunks = torch.empty((B, G, nsel), dtype=torch.int32, device=dev) if chunks else None
     out_cand = torch.empty((B, G, cw), dtype=torch.int32, device=dev) if cand else None
-    opts = ctypes.byref(PivotOpts(0, PROXY[proxy], int(window)))
     _check(indexer_chunk_refine(_ptr(Q), _ptr(W), _ptr(K), _ptr(Kbar), _ptr(cend), nc, B, L, q_len, H, d,
                                 g, nsel, max_chunk, k, opts, _ptr(out_idx), _ptr(out_score),
                                 _ptr(out_chunks), _ptr(out_cand), _ptr(wsb), wsb.numel(),
@@ -555,7 +555,7 @@ def chunk_means_varlen(K, L, cend, nc, out=None):
 
 
 def chunk_refine_varlen(Q, W, K, Kbar, cend, L, q_len, nc, g, nsel, max_chunk, k, proxy="mean", window=0,
-                        scores=True, chunks=False, cand=False, ws=None):
+                        scores=True, chunks=False, cand=False, ws=None, guard=0):
     """The key-chunk path over packed requests: (idx [sum q_len, k], score or
     None, selected chunks [sum G, nsel] or None, candidate lists [sum G, cw]
     or None), G_r = ceil(q_len[r] / g), cw = (nsel + 1) * max_chunk."""
@@ -571,7 +571,8 @@ def chunk_refine_varlen(Q, W, K, Kbar, cend, L, q_len, nc, g, nsel, max_chunk, k
     if proxy not in PROXY:
         raise ValueError(f"proxy must be one of {sorted(PROXY)}")
     dev = Q.device
-    need = indexer_chunk_refine_varlen_workspace_bytes(B, La, qa, H, d, g, nca, nsel, max_chunk, k)
+    opts = ctypes.byref(PivotOpts(int(guard), PROXY[proxy], int(window)))
+    need = indexer_chunk_refine_varlen_workspace_bytes(B, La, qa, H, d, g, nca, nsel, max_chunk, k, opts)
     wsb = (ws or _default_ws).get(need, dev)
     nq = Q.shape[0]
     ng = sum((int(x) + g - 1) // g for x in q_len)
@@ -580,7 +581,6 @@ def chunk_refine_varlen(Q, W, K, Kbar, cend, L, q_len, nc, g, nsel, max_chunk, k
     out_score = torch.empty((nq, k), dtype=torch.float32, device=dev) if scores else None
     out_chunks = torch.empty((ng, nsel), dtype=torch.int32, device=dev) if chunks else None
     out_cand = torch.empty((ng, cw), dtype=torch.int32, device=dev) if cand else None
-    opts = ctypes.byref(PivotOpts(0, PROXY[proxy], int(window)))
     _check(indexer_chunk_refine_varlen(_ptr(Q), _ptr(W), _ptr(K), _ptr(Kbar), _ptr(cend), nca, B, La, qa, H, d,
                                        g, nsel, max_chunk, k, opts, _ptr(out_idx), _ptr(out_score),
                                        _ptr(out_chunks), _ptr(out_cand), _ptr(wsb), wsb.numel(), _stream(dev)))

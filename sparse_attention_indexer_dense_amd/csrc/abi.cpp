@@ -738,6 +738,8 @@ size_t workspace_for(int mode, const Batch &b, int H, int D, int64_t c, int64_t 
 // one region shared by the coarse scan and Refine.
 struct ChunkPlan {
     bool split_scan = false, split_refine = false;
+    bool dense_pass = false, split_dense = false;  // guarded groups' rows
+    int cap_dense = 0;
     bool refine_lds = false;  // Refine on refine.hip (groups of 2-4 rows, short lists)
     int nw_refine = 4;
     int cap_scan = 0, cap_refine = 0;
@@ -788,18 +790,28 @@ int make_chunk_plan(const Batch &b, int H, int D, int64_t nc, int64_t nsel, int6
         pl.off_cand = off;
         off += align_up((size_t)groups * pl.cw * sizeof(int32_t));
     }
-    pl.split_scan = pl.G <= kSplitRowsMax;
+    // groups past the guard (all of them without one) take the chunk path
+    pl.split_scan = b.max_pivot_groups <= kSplitRowsMax;
     pl.cap_scan = scan_cap(nsel, nc);
-    size_t work = pl.split_scan ? (size_t)b.B * pl.G * score_row(nc) * sizeof(float)
+    size_t work = pl.split_scan ? (size_t)b.B * b.max_pivot_groups * score_row(nc) * sizeof(float)
                                 : scan_bytes(H, D, 8, pl.cap_scan);
+    // guarded groups: their rows in a dense pass (the same region)
+    pl.dense_pass = b.max_dense_rows > 0;
+    if (pl.dense_pass) {
+        pl.split_dense = b.max_dense_rows <= kSplitRowsMax;
+        // (a guarded row's prefix ends at the last guarded row)
+        pl.cap_dense = scan_cap(k, b.L - b.q_len + b.max_dense_rows);
+        work = std::max(work, pl.split_dense ? (size_t)b.B * b.max_dense_rows * score_row(b.L) * sizeof(float)
+                                             : scan_bytes(H, D, 8, pl.cap_dense));
+    }
     // one row per group: every row has a list of its own, so each one-wave
     // workgroup streams its own list (several per CU)
-    pl.split_refine = b.q_len <= kSplitRowsMax;
+    pl.split_refine = b.max_refine_rows <= kSplitRowsMax;
     pl.refine_lds = !pl.split_refine && b.g >= 2 && b.g <= 4 && pl.cw <= kRefineLdsCandMax;
     pl.nw_refine = b.g == 1 ? 1 : (b.g <= 4 ? 4 : 8);
     pl.cap_refine = (int)ceil_div(pl.cw + 128, 64) * 64;
     if (pl.split_refine)
-        work = std::max(work, (size_t)b.B * b.q_len * score_row(pl.cw) * sizeof(float));
+        work = std::max(work, (size_t)b.B * b.max_refine_rows * score_row(pl.cw) * sizeof(float));
     else if (!pl.refine_lds)
         work = std::max(work, scan_bytes(H, D, pl.nw_refine, pl.cap_refine));
     pl.off_work = off;
@@ -823,10 +835,12 @@ int chunk_batch(int B, int64_t L, int64_t q_len, int g, const dsaidx_pivot_opts 
             return fail(DSAIDX_EINVAL, "unknown proxy strategy %d", opts->proxy);
         if (opts->window < 0)
             return fail(DSAIDX_EINVAL, "window=%d must be >= 0", opts->window);
-        if (opts->guard != 0)
-            return fail(DSAIDX_EINVAL, "the chunk path has no guard (opts->guard must be 0)");
+        if (opts->guard < 0)
+            return fail(DSAIDX_EINVAL, "guard=%lld must be >= 0", (long long)opts->guard);
         b.proxy = opts->proxy;
         b.window = opts->window;
+        if (opts->guard > 0)
+            finish_batch(b, nullptr, nullptr, opts->guard);  // guarded groups: m0, dense rows
     }
     return DSAIDX_OK;
 }
@@ -860,6 +874,31 @@ int run_chunk_refine(const Batch &b, const void *Qv, const float *W, const void 
     int32_t *chunks = out_chunks ? out_chunks : reinterpret_cast<int32_t *>(wsb + pl.off_chunks);
     int32_t *cand = out_cand ? out_cand : reinterpret_cast<int32_t *>(wsb + pl.off_cand);
     float *work = reinterpret_cast<float *>(wsb + pl.off_work);
+    hipError_t e;
+
+    // 0. guarded groups (the first m0 of each request): dense rows, chunk and
+    // candidate rows -1
+    if (pl.dense_pass) {
+        Plan dp{};
+        dp.split_dense = pl.split_dense;
+        dp.nw_scan = 8;
+        dp.cap_dense = pl.cap_dense;
+        dp.off_work = pl.off_work;
+        Pass pd{&b, nullptr, 0, 1};
+        s = run_dense(dp, pd, Q, W, K, H, D, k, out_idx, out_score, wsb, stream);
+        if (s != DSAIDX_OK)
+            return s;
+        e = launch_fill_guarded(nullptr, b.B, b.L, b.q_len, b.g, b.m0, b.m0, nsel, chunks, stream);
+        if (e != hipSuccess)
+            return hip_fail(e, "chunk fill launch");
+        if (out_cand) {
+            e = launch_fill_guarded(nullptr, b.B, b.L, b.q_len, b.g, b.m0, b.m0, pl.cw, out_cand, stream);
+            if (e != hipSuccess)
+                return hip_fail(e, "candidate fill launch");
+        }
+    }
+    if (b.max_pivot_groups == 0)
+        return DSAIDX_OK;  // every group guarded
 
     // 1. proxies
     PoolParams pp{};
@@ -869,13 +908,13 @@ int run_chunk_refine(const Batch &b, const void *Qv, const float *W, const void 
     pp.L = b.L;
     pp.q_len = b.q_len;
     pp.g = b.g;
-    pp.m0 = 0;
+    pp.m0 = b.m0;
     pp.gmax = pl.G;
     pp.proxy = b.proxy;
     pp.window = b.window;
     pp.Qp = Qp;
     pp.Wp = Wp;
-    hipError_t e = launch_pool(H, D, pp, stream);
+    e = launch_pool(H, D, pp, stream);
     if (e != hipSuccess)
         return hip_fail(e, "pool launch");
 
@@ -889,13 +928,13 @@ int run_chunk_refine(const Batch &b, const void *Qv, const float *W, const void 
     ps.glim = glim;
     ps.krows = nc;
     if (pl.split_scan) {
-        s = run_split(kProxy, ps, Qp, Wp, Kbar, nullptr, pl.G, score_row(nc), H, D, (int)nsel, 0, chunks, nullptr, 0,
-                      nullptr, nullptr, work, stream);
+        s = run_split(kProxy, ps, Qp, Wp, Kbar, nullptr, b.max_pivot_groups, score_row(nc), H, D, (int)nsel, 0, chunks,
+                      nullptr, 0, nullptr, nullptr, work, stream);
         if (s != DSAIDX_OK)
             return s;
     } else {
         ScanParams p = scan_base(ps, kProxy, Qp, Wp, Kbar);
-        p.nblk_per_batch = ceil_div(pl.G, 8);
+        p.nblk_per_batch = ceil_div(b.max_pivot_groups, 8);
         p.nblocks = p.nblk_per_batch * b.B;
         p.sel = (int)nsel;
         p.sel2 = 0;
@@ -925,13 +964,19 @@ int run_chunk_refine(const Batch &b, const void *Qv, const float *W, const void 
     e = launch_chunk_expand(xp, (int64_t)b.B * pl.G, stream);
     if (e != hipSuccess)
         return hip_fail(e, "expansion launch");
+    if (out_cand && b.m0 > 0) {
+        // (a guarded group's list, from its -1 chunk row, is its tail only)
+        e = launch_fill_guarded(nullptr, b.B, b.L, b.q_len, b.g, b.m0, b.m0, pl.cw, out_cand, stream);
+        if (e != hipSuccess)
+            return hip_fail(e, "candidate fill launch");
+    }
 
     // 5. Refine on the lists
     Pass pr{&b, nullptr, pl.cw, 0};
     pr.cand_n = cn;
     if (pl.split_refine)
-        return run_split(kRefine, pr, Q, W, K, cand, b.q_len, score_row(pl.cw), H, D, (int)k, 0, out_idx, out_score, 0,
-                         nullptr, nullptr, work, stream);
+        return run_split(kRefine, pr, Q, W, K, cand, b.max_refine_rows, score_row(pl.cw), H, D, (int)k, 0, out_idx,
+                         out_score, 0, nullptr, nullptr, work, stream);
     if (pl.refine_lds) {
         // groups of two to four rows sharing a list: the members' scores and
         // selections on chip (a single row per list stays on the one-wave
@@ -948,11 +993,11 @@ int run_chunk_refine(const Batch &b, const void *Qv, const float *W, const void 
         rp.q_len = b.q_len;
         rp.g = b.g;
         rp.c = pl.cw;
-        rp.m0 = 0;
+        rp.m0 = b.m0;
         rp.k = (int)k;
         rp.out_idx = out_idx;
         rp.out_score = out_score;
-        rp.nwork = (int64_t)b.B * pl.G;
+        rp.nwork = (int64_t)b.B * b.max_pivot_groups;
         const int grid = (int)std::min<int64_t>(rp.nwork, std::max(1, num_cus()));
         e = launch_refine_lds(H, D, rp, grid, stream);
         if (e != hipSuccess)
@@ -962,7 +1007,7 @@ int run_chunk_refine(const Batch &b, const void *Qv, const float *W, const void 
     ScanParams p = scan_base(pr, kRefine, Q, W, K);
     p.cand = cand;
     p.member_chunks = ceil_div(b.g, pl.nw_refine);
-    p.nblk_per_batch = pl.G * p.member_chunks;
+    p.nblk_per_batch = b.max_pivot_groups * p.member_chunks;
     p.nblocks = p.nblk_per_batch * b.B;
     p.sel = (int)k;
     p.sel2 = 0;
@@ -1315,10 +1360,10 @@ int indexer_chunk_means(const void *K, int B, int64_t L, int d_I, const int32_t 
 }
 
 size_t indexer_chunk_refine_workspace_bytes(int B, int64_t L, int64_t q_len, int H_I, int d_I, int g, int64_t nc,
-                                            int nsel, int max_chunk, int k)
+                                            int nsel, int max_chunk, int k, const dsaidx_pivot_opts *opts)
 {
     Batch b;
-    if (chunk_batch(B, L, q_len, g, nullptr, b) != DSAIDX_OK)
+    if (chunk_batch(B, L, q_len, g, opts, b) != DSAIDX_OK)
         return 0;
     ChunkPlan pl;
     if (make_chunk_plan(b, H_I, d_I, nc, nsel, max_chunk, k, false, false, pl) != DSAIDX_OK)
@@ -1434,7 +1479,8 @@ int indexer_chunk_means_varlen(const void *K, int B, const int64_t *L, int d_I, 
 }
 
 size_t indexer_chunk_refine_varlen_workspace_bytes(int B, const int64_t *L, const int64_t *q_len, int H_I, int d_I,
-                                                   int g, const int64_t *nc, int nsel, int max_chunk, int k)
+                                                   int g, const int64_t *nc, int nsel, int max_chunk, int k,
+                                                   const dsaidx_pivot_opts *opts)
 {
     if (!q_len || !nc) {
         fail(DSAIDX_EINVAL, "q_len and nc must not be NULL");
@@ -1447,7 +1493,7 @@ size_t indexer_chunk_refine_varlen_workspace_bytes(int B, const int64_t *L, cons
         if (q_len[r] == 0)
             continue;
         const size_t n =
-            indexer_chunk_refine_workspace_bytes(1, L[r], q_len[r], H_I, d_I, g, nc[r], nsel, max_chunk, k);
+            indexer_chunk_refine_workspace_bytes(1, L[r], q_len[r], H_I, d_I, g, nc[r], nsel, max_chunk, k, opts);
         if (n == 0)
             return 0;
         need = std::max(need, n);

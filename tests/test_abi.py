@@ -175,7 +175,7 @@ def test_empty_batches_do_nothing():
 
 
 def chunk_ws(B=1, L=8192, q_len=8192, H=64, d=128, g=1, nc=128, nsel=16, max_chunk=64, k=256):
-    return dsa.indexer_chunk_refine_workspace_bytes(B, L, q_len, H, d, g, nc, nsel, max_chunk, k)
+    return dsa.indexer_chunk_refine_workspace_bytes(B, L, q_len, H, d, g, nc, nsel, max_chunk, k, None)
 
 
 def test_chunk_workspace_sizes():
@@ -209,7 +209,7 @@ def test_chunk_entry_points_reject_bad_arguments():
         return dsa.indexer_chunk_refine(fake(), fake(), fake(), Kbar, fake(), nc, 1, 8192, 8192, 64, 128, 1,
                                         nsel, max_chunk, k, opts, fake(), None, None, None, fake(), ws_bytes,
                                         None)
-    assert refine(opts=ctypes.byref(dsa.PivotOpts(64, 0, 0))) == EINVAL
+    assert refine(opts=ctypes.byref(dsa.PivotOpts(-1, 0, 0))) == EINVAL
     assert "guard" in dsa.indexer_last_error()
     assert refine(opts=ctypes.byref(dsa.PivotOpts(0, 5, 0))) == EINVAL
     assert refine(nsel=2, max_chunk=32) == EINVAL and ">= k" in dsa.indexer_last_error()
@@ -248,7 +248,8 @@ def test_chunk_varlen_entry_points_reject_bad_arguments():
     assert "request 1" in dsa.indexer_last_error()
 
     def ws(q_len=q, nc_=nc, nsel=8, max_chunk=64, k=128):
-        return dsa.indexer_chunk_refine_varlen_workspace_bytes(3, L, q_len, 64, 128, 4, nc_, nsel, max_chunk, k)
+        return dsa.indexer_chunk_refine_varlen_workspace_bytes(3, L, q_len, 64, 128, 4, nc_, nsel, max_chunk, k,
+                                                               None)
     assert ws() > 0
     assert ws(q_len=arr(0, 0, 0)) > 0                # nothing to run is still a valid call
     assert ws(q_len=arr(3000, 65, 0)) == 0           # q_len > L
@@ -257,7 +258,7 @@ def test_chunk_varlen_entry_points_reject_bad_arguments():
     assert ws(q_len=None) == 0 and ws(nc_=None) == 0
     # a request shorter than the largest chunk is valid (its rows are only wider)
     assert dsa.indexer_chunk_refine_varlen_workspace_bytes(2, arr(3000, 40), arr(8, 8), 64, 128, 4,
-                                                         arr(47, 1), 8, 64, 128) > 0
+                                                         arr(47, 1), 8, 64, 128, None) > 0
 
     def refine(q_len=q, nc_=nc, Kbar=fake(), ws_bytes=big, opts=None):
         return dsa.indexer_chunk_refine_varlen(fake(), fake(), fake(), Kbar, fake(), nc_, 3, L, q_len, 64, 128,
@@ -267,5 +268,5 @@ def test_chunk_varlen_entry_points_reject_bad_arguments():
     assert refine(nc_=None) == EINVAL
     assert refine(Kbar=None) == EINVAL
     assert refine(ws_bytes=64) == EWORKSPACE
-    assert refine(opts=ctypes.byref(dsa.PivotOpts(64, 0, 0))) == EINVAL and "guard" in dsa.indexer_last_error()
+    assert refine(opts=ctypes.byref(dsa.PivotOpts(-1, 0, 0))) == EINVAL and "guard" in dsa.indexer_last_error()
     assert refine(q_len=arr(0, 0, 0)) == OK          # no request has rows: nothing to do
