@@ -95,7 +95,7 @@ typedef enum {
  * (the matching entry point would return DSAIDX_EINVAL or
  * DSAIDX_EUNSUPPORTED).
  */
-size_t indexer_workspace_bytes(int mode, int B, int64_t L, int64_t q_len,
+size_t indexer_workspace_bytes(dsaidx_mode mode, int B, int64_t L, int64_t q_len,
                                int H_I, int d_I, int g, int c, int k);
 
 /*
@@ -222,7 +222,7 @@ typedef struct {
  *   ownership, errors) is as for the uniform entry points. The call uploads
  *   B small request descriptors into ws through kernel launches on `stream`.
  */
-size_t indexer_varlen_workspace_bytes(int mode, int B, const int64_t *L, const int64_t *q_len,
+size_t indexer_varlen_workspace_bytes(dsaidx_mode mode, int B, const int64_t *L, const int64_t *q_len,
                                       int H_I, int d_I, int g, int c, int k,
                                       const dsaidx_pivot_opts *opts);
 

@@ -1142,7 +1142,8 @@ int check_chunk_varlen(int B, const int64_t *L, const int64_t *q_len, const int6
 
 extern "C" {
 
-size_t indexer_workspace_bytes(int mode, int B, int64_t L, int64_t q_len, int H_I, int d_I, int g, int c, int k)
+size_t indexer_workspace_bytes(dsaidx_mode mode, int B, int64_t L, int64_t q_len, int H_I, int d_I, int g, int c,
+                               int k)
 {
     if (mode != DSAIDX_DENSE && mode != DSAIDX_REUSE && mode != DSAIDX_REFINE) {
         fail(DSAIDX_EINVAL, "unknown mode %d", mode);
@@ -1219,7 +1220,7 @@ int indexer_pivot_refine_noalloc(const void *Q, const float *W, const void *K, i
                      (size_t)DSAIDX_SCRATCH_BYTES, stream);
 }
 
-size_t indexer_varlen_workspace_bytes(int mode, int B, const int64_t *L, const int64_t *q_len, int H_I, int d_I,
+size_t indexer_varlen_workspace_bytes(dsaidx_mode mode, int B, const int64_t *L, const int64_t *q_len, int H_I, int d_I,
                                       int g, int c, int k, const dsaidx_pivot_opts *opts)
 {
     if (mode != DSAIDX_DENSE && mode != DSAIDX_REUSE && mode != DSAIDX_REFINE) {

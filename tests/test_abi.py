@@ -50,7 +50,9 @@ def test_workspace_sizes():
     assert ws(dsa.DENSE, B=0) == 0
     assert ws(dsa.DENSE, H=8, d=64) == 0
     assert ws(dsa.REFINE, c=100, k=200) == 0
-    assert ws(99) == 0
+    for bad in (3, -1, 99):  # not a dsaidx_mode
+        assert ws(bad) == 0
+        assert "unknown mode" in dsa.indexer_last_error()
 
 
 P = ctypes.c_void_p
@@ -116,6 +118,9 @@ def test_varlen_workspace_sizes():
     assert varlen_ws(dsa.DENSE, [100, 5000], [100, 2]) > 0
     assert varlen_ws(dsa.REFINE, [100, 5000], [100, 2]) > 0
     assert varlen_ws(dsa.REUSE, [100, 5000], [100, 2], guard=50) > 0
+    for bad in (3, -1):
+        assert varlen_ws(bad, [100, 5000], [100, 2]) == 0
+        assert "unknown mode" in dsa.indexer_last_error()
     # the guard removes the PIVOT stages when every group is guarded
     assert varlen_ws(dsa.REFINE, [4096], [4096], guard=4096) < varlen_ws(dsa.REFINE, [4096], [4096])
     assert varlen_ws(dsa.DENSE, [100, 50], [100, 60]) == 0   # q_len > L
