@@ -372,13 +372,28 @@ def bench_chunks(dsa, synth, torch, w, Q, W, configs=CHUNK_CONFIGS, steps=3):
         (idx, _, _, cand), ms = timed(lambda: dsa.chunk_refine(Q, W, K, Kbar, cend, g, nsel, mc, k,
                                                                scores=False, cand=True, ws=ws))
         coarse, refine = chunk_pairs(torch, cend, cand, L, q_len, g, nsel)
+        # the Refine launch alone: each group's candidate keys gathered once
+        # (every row's own list at g = 1), against HBM and MFMA rooflines
+        rk_ms, _, rk_name = kernel_ms(torch, lambda: dsa.chunk_refine(Q, W, K, Kbar, cend, g, nsel, mc, k,
+                                                                      scores=False, cand=True, ws=ws),
+                                      ("refine_lds_kernel", "scan_select_kernel<64, 128, 1, 2>",
+                                       "scan_select_kernel<64, 128, 4, 2>", "scan_select_kernel<64, 128, 8, 2>"))
+        gathered = int((cand >= 0).sum())
         print(f"[bench] chunks {part} g={g} nsel={nsel}: {ms:.2f} ms", file=sys.stderr, flush=True)
-        res["runs"].append({"partition": part, "g": g, "nsel": nsel, "max_chunk": mc, "ms": ms,
-                            "speedup_vs_dense": d_ms / ms, "recall_vs_dense": recall(idx, d_idx),
-                            "coarse_pairs": coarse, "refine_pairs": refine,
-                            "mean_candidates": refine / q_len,
-                            "mfma_frac": (coarse + refine) * flop_per_pair / (ms * 1e-3) /
-                            (PEAK_BF16_TFLOPS * 1e12)})
+        run = {"partition": part, "g": g, "nsel": nsel, "max_chunk": mc, "ms": ms,
+               "speedup_vs_dense": d_ms / ms, "recall_vs_dense": recall(idx, d_idx),
+               "coarse_pairs": coarse, "refine_pairs": refine,
+               "mean_candidates": refine / q_len,
+               "mfma_frac": (coarse + refine) * flop_per_pair / (ms * 1e-3) /
+               (PEAK_BF16_TFLOPS * 1e12)}
+        if rk_ms:
+            gb = gathered * 2 * d
+            run["refine_kernel"] = {"kernel": rk_name, "kernel_ms": rk_ms, "gathered_keys": gathered,
+                                    "gather_bytes": gb, "gather_GBps": gb / (rk_ms * 1e-3) / 1e9,
+                                    "gather_hbm_frac": gb / (rk_ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
+                                    "mfma_frac": refine * flop_per_pair / (rk_ms * 1e-3) /
+                                    (PEAK_BF16_TFLOPS * 1e12)}
+        res["runs"].append(run)
         del idx, cand
     return res
 
