@@ -47,6 +47,20 @@ def kernel_hash():
     return h.hexdigest()[:16]
 
 
+def dense_traffic(workload, path=TRAFFIC_FILE):
+    """HBM bytes of one dense launch from the committed counter record
+    (FETCH_SIZE and WRITE_SIZE, each scaled by a 1 GiB copy), or None when the
+    record is missing, belongs to another workload or was taken on other
+    kernel sources."""
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        tr = json.load(f)
+    if tr.get("kernel_hash") == kernel_hash() and tr.get("workload") == workload:
+        return tr.get("hbm_bytes_per_launch")
+    return None
+
+
 def dense_pairs(L, q_len):
     off = L - q_len
     return sum_range(off + 1, L)  # row r scores pos(r) + 1 keys
@@ -721,12 +735,7 @@ def main():
 
     dense_ms = per_variant["dense"]
     achieved = pd * flop_per_pair / (dense_ms * 1e-3) / 1e12
-    traffic = None
-    if os.path.exists(TRAFFIC_FILE):
-        with open(TRAFFIC_FILE) as f:
-            tr = json.load(f)
-        if tr.get("kernel_hash") == kernel_hash() and tr.get("workload") == w.name:
-            traffic = tr.get("hbm_bytes_per_launch")
+    traffic = dense_traffic(w.name)
     roofline = {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
                 "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS, "traffic": traffic,
                 "kernel": "scan_select_kernel<64,128,8,dense>",
