@@ -722,6 +722,8 @@ def main():
             dsa.chunk_refine(Q, W, Kl, Kbar, cend, int(cg), int(cn), mc, k, scores=False, ws=ws)
             torch.cuda.synchronize()
             print(f"[bench] chunk call {i} done", file=sys.stderr, flush=True)
+        if args.calibrate_copy:
+            copy_1gib(torch, dev)
         return
     if args.chunk_sweep:
         del K
