@@ -14,6 +14,10 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kWave = 64;
 
+// Word 3 of a raw buffer resource on this GPU family (no format conversion,
+// plain byte addressing with a stride of 0).
+constexpr int kBufferRsrcWord3 = 0x00020000;
+
 // Register/LDS geometry of one query row (H heads of D dims) on the
 // v_mfma_f32_32x32x16_bf16 tile: heads are MFMA rows, keys MFMA columns.
 template <int H, int D>

@@ -339,6 +339,17 @@ __device__ __forceinline__ void plan_block(const ScanParams &p, int64_t j, int w
 }
 
 // ------------------------------------------------------------------ kernel
+// Global->LDS DMA through a buffer resource (MUBUF buffer_load ... lds): lane
+// l writes 16 bytes at LDS address lds + 16*l from byte voffset of the range
+// [base, base + bytes); base and bytes must be wave-uniform.
+__device__ __forceinline__ void buffer_load_lds16(const unsigned char *base, int bytes, unsigned char *lds,
+                                                  int voffset)
+{
+    const __amdgpu_buffer_rsrc_t rs =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<unsigned char *>(base), (short)0, bytes, kBufferRsrcWord3);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void *)lds, 16, voffset, 0, 0, 0);
+}
+
 // Keys of one stage live in LDS as rows of 2*D bytes whose 16-byte chunks are
 // XOR-swizzled by the row index (chunk c of row n sits at slot c ^ (n % CHUNKS)),
 // so that the 32 rows one MFMA B-fragment read touches spread over all banks.
@@ -361,8 +372,14 @@ struct StageDma {
 // loff (this lane's row-in-slot and swizzled chunk, the same for every j
 // because NW*RPI is a multiple of CHUNKS) is fixed for the whole kernel. No
 // index arithmetic, bounds checks or branches per DMA. The last, partial
-// stage of a row block fetches row 0 for slots past the prefix (the causal
-// mask never admits them).
+// stage of a row block fetches the stage's first row for slots past the
+// prefix (the causal mask never admits them).
+//
+// These DMAs are buffer loads (MUBUF) through a resource based at the stage's
+// first key row and spanning the stage: with the global (FLAT-encoded) form
+// in flight, the compiler treats LDS completions as unordered and makes every
+// B-fragment read of the stage wait for all of a tile's reads (lgkmcnt(0))
+// before its first MFMA; with buffer loads it waits for each fragment only.
 template <int D, int NW, int STAGE>
 __device__ __forceinline__ void stage_issue_prefix(unsigned char *kbuf, const BlockKeys &bk, int t, uint32_t loff,
                                                    int wave, int lane)
@@ -370,29 +387,25 @@ __device__ __forceinline__ void stage_issue_prefix(unsigned char *kbuf, const Bl
     using SD = StageDma<D, NW, STAGE>;
     static_assert((NW * SD::RPI) % SD::CHUNKS == 0, "slot offsets must not change the swizzle");
     const int row0 = t * STAGE;
-    const unsigned char *kb = reinterpret_cast<const unsigned char *>(bk.Kb);
+    const unsigned char *sb = reinterpret_cast<const unsigned char *>(bk.Kb) + (int64_t)row0 * SD::ROWB;
     if (row0 + STAGE <= bk.nkeys) {
 #pragma unroll
         for (int j = 0; j < SD::PER_WAVE; ++j) {
             const int i = wave + NW * j;
-            if (SD::PER_STAGE % NW == 0 || i < SD::PER_STAGE) {
-                const unsigned char *sb = kb + ((int64_t)row0 * SD::ROWB + j * NW * SD::RPI * SD::ROWB);
-                __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void *)(sb + loff),
-                                                 (__attribute__((address_space(3))) void *)(kbuf + i * 1024), 16,
-                                                 0, 0);
-            }
+            if (SD::PER_STAGE % NW == 0 || i < SD::PER_STAGE)
+                buffer_load_lds16(sb, STAGE * SD::ROWB, kbuf + i * 1024, (int)(loff + j * NW * SD::RPI * SD::ROWB));
         }
     } else {
+        // the last, partial stage: slots past the prefix fetch the stage's
+        // first row again (the causal mask never admits them)
 #pragma unroll
         for (int j = 0; j < SD::PER_WAVE; ++j) {
             const int i = wave + NW * j;
             if (SD::PER_STAGE % NW == 0 || i < SD::PER_STAGE) {
                 const int n = i * SD::RPI + lane / SD::CHUNKS;
-                const int row = (row0 + n < bk.nkeys) ? row0 + n : 0;
+                const int rn = (row0 + n < bk.nkeys) ? n : 0;
                 const int c = (lane % SD::CHUNKS) ^ (n & (SD::CHUNKS - 1));
-                __builtin_amdgcn_global_load_lds(
-                    (const __attribute__((address_space(1))) void *)(kb + (int64_t)row * SD::ROWB + c * 16),
-                    (__attribute__((address_space(3))) void *)(kbuf + i * 1024), 16, 0, 0);
+                buffer_load_lds16(sb, STAGE * SD::ROWB, kbuf + i * 1024, rn * SD::ROWB + c * 16);
             }
         }
     }
